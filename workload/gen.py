@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the routed int4 MoE layer workloads.
+
+Only input generation lives here (random draws and their storage format); none of
+the method's arithmetic does. The generator itself is C (``moe_gen.c``, which states
+its exact definition); this file names the workloads and lays the drawn values out in
+the layouts the library and the oracle both take:
+
+* ``x``            [T][d]       bf16 bits (uint16), N(0, 1)
+* ``w_router``     [d][E]       fp32, N(0, sigma_r^2)
+* ``logit_bias``   [E]          fp32 or None (Zipf-like 1.5 * ln(1/rank) for the skewed workload)
+* per projection   codes [n_mat][out][in/2] uint8 (two 4-bit codes per byte, the even
+                   input index in the low nibble), scales and biases [n_mat][out][in/64]
+                   bf16 bits; scale = |N(0, 0.02^2)|, bias = -8 * scale
+* gate, up: out = I, in = d;  down: out = d, in = I;  the shared expert has n_mat = 1.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gen.so")
+
+# tensor ids of the streams of one layer
+T_ROUTER = 1
+T_GATE_CODES, T_GATE_SB = 2, 3
+T_UP_CODES, T_UP_SB = 4, 5
+T_DOWN_CODES, T_DOWN_SB = 6, 7
+T_SH_GATE_CODES, T_SH_GATE_SB = 8, 9
+T_SH_UP_CODES, T_SH_UP_SB = 10, 11
+T_SH_DOWN_CODES, T_SH_DOWN_SB = 12, 13
+T_PERM = 14
+T_X = 100  # + chunk index
+
+QUANT_SIGMA = 0.02
+GROUP = 64
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the generator with gcc (OpenMP, -O2, IEEE semantics)."""
+    import subprocess
+
+    src = os.path.join(_HERE, "moe_gen.c")
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           src, "-o", LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        u64, i64, i32, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p
+        L.gen_stream_key.restype = u64
+        L.gen_stream_key.argtypes = [u64, u64, u64]
+        L.gen_word.restype = u64
+        L.gen_word.argtypes = [u64, u64]
+        L.gen_bytes.argtypes = [u64, u64, i64, vp]
+        L.gen_normal_bf16.argtypes = [u64, u64, i64, dbl, vp]
+        L.gen_normal_f32.argtypes = [u64, u64, i64, dbl, vp]
+        L.gen_scale_bias_bf16.argtypes = [u64, u64, i64, dbl, vp, vp]
+        L.gen_zipf_bias.argtypes = [i32, dbl, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def key(seed: int, layer: int, tensor: int) -> int:
+    return lib().gen_stream_key(seed, layer, tensor)
+
+
+def rand_bytes(k: int, n: int, start: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
+    out = np.empty(n, np.uint8) if out is None else out
+    assert out.dtype == np.uint8 and out.size == n
+    lib().gen_bytes(k, start, n, _ptr(out))
+    return out
+
+
+def normal_bf16(k: int, n: int, sigma: float, start: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
+    out = np.empty(n, np.uint16) if out is None else out
+    assert out.dtype == np.uint16 and out.size == n
+    lib().gen_normal_bf16(k, start, n, sigma, _ptr(out))
+    return out
+
+
+def normal_f32(k: int, n: int, sigma: float, start: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
+    out = np.empty(n, np.float32) if out is None else out
+    assert out.dtype == np.float32 and out.size == n
+    lib().gen_normal_f32(k, start, n, sigma, _ptr(out))
+    return out
+
+
+def scale_bias(k: int, n: int, sigma: float = QUANT_SIGMA, start: int = 0, out_s=None, out_b=None):
+    s = np.empty(n, np.uint16) if out_s is None else out_s
+    b = np.empty(n, np.uint16) if out_b is None else out_b
+    lib().gen_scale_bias_bf16(k, start, n, sigma, _ptr(s), _ptr(b))
+    return s, b
+
+
+def zipf_bias(n_experts: int, alpha: float = 1.5, rank: Optional[np.ndarray] = None) -> np.ndarray:
+    out = np.empty(n_experts, np.float32)
+    if rank is not None:
+        rank = np.ascontiguousarray(rank, dtype=np.int32)
+        assert rank.size == n_experts
+    lib().gen_zipf_bias(n_experts, alpha, None if rank is None else _ptr(rank), _ptr(out))
+    return out
+
+
+def permutation(k: int, n: int) -> np.ndarray:
+    """Fisher-Yates shuffle of 0..n-1 driven by the stream's words (j = word % (i + 1))."""
+    p = np.arange(n, dtype=np.int32)
+    for i in range(n - 1, 0, -1):
+        j = lib().gen_word(k, n - 1 - i) % (i + 1)
+        p[i], p[j] = p[j], p[i]
+    return p
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int            # tokens per pass of the workload
+    d: int            # hidden size
+    E: int            # routed experts
+    k: int            # experts per token
+    I: int            # routed expert intermediate size
+    Is: int           # shared expert intermediate size (0 = no shared expert)
+    router_sigma: float
+    layers: int       # distinct layers the workload cycles through
+    chunk: int        # tokens per call (T is processed in T // chunk sequential calls)
+    zipf: bool = False
+    seed: int = 0
+
+    @property
+    def calls(self) -> int:
+        return self.T // self.chunk
+
+    @property
+    def expert_bytes(self) -> int:
+        """Packed bytes of one routed expert (codes + bf16 scales + bf16 biases, 3 matrices)."""
+        return 3 * self.d * self.I // 2 + 3 * 2 * 2 * self.d * self.I // GROUP
+
+    @property
+    def shared_bytes(self) -> int:
+        return 3 * self.d * self.Is // 2 + 3 * 2 * 2 * self.d * self.Is // GROUP
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # T=8, d=256, 16 experts top-4 + shared (I_s = I = 128), router N(0, 0.05^2)
+    "tiny": Workload("tiny", 8, 256, 16, 4, 128, 128, 0.05, 1, 8),
+    # batch-1 decode over 40 distinct layers, 256 experts top-8 + shared, I = 512
+    "decode": Workload("decode", 1, 2048, 256, 8, 512, 512, 0.02, 40, 1),
+    # 512-token prefill through one layer of the decode shapes
+    "prefill": Workload("prefill", 512, 2048, 256, 8, 512, 512, 0.02, 1, 512),
+    # 4096 tokens in 4 chunks of 1024 with a Zipf-like logit bias
+    "long": Workload("long", 4096, 2048, 256, 8, 512, 512, 0.02, 1, 1024, zipf=True),
+    # diffusion canvas: 256 positions x 30 layers, 128 experts top-8, I = 768, no shared expert
+    "diffusion": Workload("diffusion", 256, 2048, 128, 8, 768, 0, 0.02, 30, 256),
+}
+
+
+def _proj(seed: int, layer: int, t_codes: int, t_sb: int, n_mat: int, out_dim: int, in_dim: int,
+          out: Optional[dict] = None) -> dict:
+    n_codes = n_mat * out_dim * in_dim // 2
+    n_sb = n_mat * out_dim * in_dim // GROUP
+    if out is None:
+        out = {"codes": np.empty(n_codes, np.uint8), "scales": np.empty(n_sb, np.uint16),
+               "biases": np.empty(n_sb, np.uint16)}
+    rand_bytes(key(seed, layer, t_codes), n_codes, out=out["codes"].reshape(-1))
+    scale_bias(key(seed, layer, t_sb), n_sb, out_s=out["scales"].reshape(-1), out_b=out["biases"].reshape(-1))
+    out["codes"] = out["codes"].reshape(n_mat, out_dim, in_dim // 2)
+    out["scales"] = out["scales"].reshape(n_mat, out_dim, in_dim // GROUP)
+    out["biases"] = out["biases"].reshape(n_mat, out_dim, in_dim // GROUP)
+    return out
+
+
+def expert_weights(w: Workload, layer: int, shared: bool = False, out: Optional[dict] = None) -> dict:
+    """Packed gate/up/down of all routed experts (or of the shared expert) of one layer."""
+    seed = w.seed
+    if shared:
+        n, I, ids = 1, w.Is, (T_SH_GATE_CODES, T_SH_GATE_SB, T_SH_UP_CODES, T_SH_UP_SB, T_SH_DOWN_CODES, T_SH_DOWN_SB)
+    else:
+        n, I, ids = w.E, w.I, (T_GATE_CODES, T_GATE_SB, T_UP_CODES, T_UP_SB, T_DOWN_CODES, T_DOWN_SB)
+    out = out or {}
+    return {
+        "gate": _proj(seed, layer, ids[0], ids[1], n, I, w.d, out.get("gate")),
+        "up": _proj(seed, layer, ids[2], ids[3], n, I, w.d, out.get("up")),
+        "down": _proj(seed, layer, ids[4], ids[5], n, w.d, I, out.get("down")),
+    }
+
+
+def router(w: Workload, layer: int) -> np.ndarray:
+    return normal_f32(key(w.seed, layer, T_ROUTER), w.d * w.E, w.router_sigma).reshape(w.d, w.E)
+
+
+def logit_bias(w: Workload, permuted: bool = False) -> Optional[np.ndarray]:
+    if not w.zipf:
+        return None
+    rank = None
+    if permuted:
+        rank = permutation(key(w.seed, 0, T_PERM), w.E) + 1
+    return zipf_bias(w.E, 1.5, rank)
+
+
+def tokens(w: Workload, layer: int, chunk: int, T: Optional[int] = None) -> np.ndarray:
+    T = w.chunk if T is None else T
+    return normal_bf16(key(w.seed, layer, T_X + chunk), T * w.d, 1.0).reshape(T, w.d)
+
+
+def layer(w: Workload, layer_idx: int = 0) -> dict:
+    """All inputs of one layer except the activations."""
+    return {
+        "w_router": router(w, layer_idx),
+        "logit_bias": logit_bias(w),
+        "routed": expert_weights(w, layer_idx),
+        "shared": expert_weights(w, layer_idx, shared=True) if w.Is > 0 else None,
+    }
