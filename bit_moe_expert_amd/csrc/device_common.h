@@ -1,0 +1,147 @@
+// Device helpers shared by the gfx950 kernels of the routed int4 MoE FFN.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_int4.h"
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 64;      // quantisation group along the input dimension
+constexpr int kTileRows = 128;  // block-map tile height
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (low half = a), hardware round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float a) { return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu); }
+
+// Groupwise-affine dequantisation of one 32-bit word of codes (8 inputs, byte j holds input
+// 2j in its low nibble and 2j+1 in its high nibble): w = bf16(fp32(s * q + b)). s * q is exact
+// in fp32, so fmaf gives the single fp32 rounding the definition asks for; the conversion to
+// bf16 rounds to nearest even. out[j] = packed bf16 pair (input 2j, input 2j+1).
+__device__ __forceinline__ void dequant_word(uint32_t w, float s, float b, uint32_t out[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = fmaf(s, (float)((lo >> (8 * j)) & 0xffu), b);
+    const float c = fmaf(s, (float)((hi >> (8 * j)) & 0xffu), b);
+    out[j] = pack_bf16x2(a, c);
+  }
+}
+
+// Dequantise one 64-input group (32 bytes of codes) into 32 packed bf16 pairs.
+__device__ __forceinline__ void dequant_group(const uint4& c0, const uint4& c1, float s, float b, uint32_t out[32]) {
+  dequant_word(c0.x, s, b, out + 0);
+  dequant_word(c0.y, s, b, out + 4);
+  dequant_word(c0.z, s, b, out + 8);
+  dequant_word(c0.w, s, b, out + 12);
+  dequant_word(c1.x, s, b, out + 16);
+  dequant_word(c1.y, s, b, out + 20);
+  dequant_word(c1.z, s, b, out + 24);
+  dequant_word(c1.w, s, b, out + 28);
+}
+
+// "128 + q" as bf16: 0x4300 is 128.0 and its 7 mantissa bits hold q exactly. From a word of
+// 8 codes, pair n (n = 0..3) holds inputs (n, n + 4) of the word.
+__device__ __forceinline__ uint32_t magic_pair(uint32_t w, int n) {
+  return ((w >> (4 * n)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Re-pair 8 bf16 values (4 dwords in natural order) to match magic_pair: pair n = (v[n], v[n+4]).
+__device__ __forceinline__ void repair8(const uint32_t v[4], uint32_t p[4]) {
+  p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+  p[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+  p[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+  p[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+}
+
+// fp32 += a.lo * b.lo + a.hi * b.hi over bf16 pairs.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const uint32_t l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Order-preserving key: larger logit first, then lower expert index. Key 0 means "empty".
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int topk_key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((int)(uint32_t)v, m, 64);
+  uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One wave: top-k of logits lg[0..E) (E <= 1024, k <= 16) by (logit desc, index asc), then the
+// softmax over the chosen logits. Lane j < k writes slot j. Must be called by a whole wave.
+__device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
+  const int lane = (int)lane_id();
+  uint64_t key[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int e = lane + 64 * s;
+    key[s] = e < E ? topk_key(lg[e], e) : 0ull;
+  }
+  int my_e = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) best = key[s] > best ? key[s] : best;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, m);
+      best = o > best ? o : best;
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (key[s] == best) key[s] = 0ull;
+    if (lane == j) {
+      my_e = topk_key_index(best);
+      my_l = lg[my_e];
+    }
+  }
+  const float top = __shfl(my_l, 0, 64);
+  const float ex = lane < k ? expf(my_l - top) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    ids_out[lane] = my_e;
+    w_out[lane] = ex / sum;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,43 @@
+// Host-side launch interface of the gfx950 kernels (internal to libmoe_int4.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_int4.h"
+
+namespace moe {
+
+// Everything one layer call needs, resolved to device pointers by the C-ABI layer.
+struct Ctx {
+  int d, E, k, I, Is, T, P, max_tiles;
+  const uint16_t* x;
+  const float* w_router;
+  const float* logit_bias;
+  moe_ffn_q4 routed;
+  moe_ffn_q4 shared;  // all-null when Is == 0
+  moe_routing r;      // routing arrays (caller's or carved from the workspace)
+  float* router_parts;    // [d/64][E] decode router chunk partials
+  unsigned* counter;      // decode router arrival counter (zero between calls)
+  uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1)
+  uint16_t* hs;           // [T][Is] bf16
+  float* y_rows;          // [P + T][d] fp32, grouped order, shared rows last
+  uint16_t* y;            // [T][d] bf16
+  hipStream_t stream;
+};
+
+hipError_t launch_router_decode(const Ctx& c);
+hipError_t launch_router_prefill(const Ctx& c);
+hipError_t launch_route_meta(const Ctx& c);
+hipError_t launch_gemv_gateup(const Ctx& c);
+hipError_t launch_gemv_down_combine(const Ctx& c);
+hipError_t launch_gateup_gemm(const Ctx& c);
+hipError_t launch_down_gemm(const Ctx& c);
+hipError_t launch_combine(const Ctx& c);
+hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* out, hipStream_t stream);
+
+// The GEMV decode path keeps all selected experts' h in LDS: (k*I + Is) bf16 values.
+constexpr int kGemvMaxH = 28672;
+
+}  // namespace moe

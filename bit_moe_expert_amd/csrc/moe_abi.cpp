@@ -1,0 +1,358 @@
+// C ABI of libmoe_int4.so: argument validation (before any HIP call), workspace layout and the
+// stage sequence of each entry point. The kernels live in route.hip, gemv.hip, gemm.hip and
+// dequant.hip.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+#include "moe_int4.h"
+
+namespace moe {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_dims(const moe_dims* dm, int32_t T) {
+  if (!dm) return fail(MOE_EINVAL, "dims is NULL");
+  if (T < 0) return fail(MOE_EINVAL, "T = %d is negative", T);
+  if (T > 65536) return fail(MOE_EUNSUPPORTED, "T = %d exceeds 65536", T);
+  if (dm->group_size != 64) return fail(MOE_EUNSUPPORTED, "group_size = %d, only 64 is supported", dm->group_size);
+  if (dm->d_model < 64 || dm->d_model > 16384 || dm->d_model % 64)
+    return fail(MOE_EUNSUPPORTED, "d_model = %d must be a multiple of 64 in [64, 16384]", dm->d_model);
+  if (dm->n_experts < 1 || dm->n_experts > 1024)
+    return fail(MOE_EUNSUPPORTED, "n_experts = %d must be in [1, 1024]", dm->n_experts);
+  if (dm->top_k < 1 || dm->top_k > 16 || dm->top_k > dm->n_experts)
+    return fail(MOE_EUNSUPPORTED, "top_k = %d must be in [1, min(n_experts, 16)]", dm->top_k);
+  if (dm->d_ff < 64 || dm->d_ff > 8192 || dm->d_ff % 64)
+    return fail(MOE_EUNSUPPORTED, "d_ff = %d must be a multiple of 64 in [64, 8192]", dm->d_ff);
+  if (dm->d_ff_shared < 0 || dm->d_ff_shared > 8192 || dm->d_ff_shared % 64)
+    return fail(MOE_EUNSUPPORTED, "d_ff_shared = %d must be 0 or a multiple of 64 up to 8192", dm->d_ff_shared);
+  return MOE_OK;
+}
+
+int32_t max_tiles_of(const moe_dims& dm, int32_t T) {
+  const int64_t P = (int64_t)T * dm.top_k;
+  const int64_t t = std::min<int64_t>(dm.n_experts, P) + P / 128 + (dm.d_ff_shared ? (T + 127) / 128 : 0);
+  return (int32_t)t;
+}
+
+bool gemv_path(const moe_dims& dm, int32_t T) {
+  return T == 1 && dm.top_k * dm.d_ff + dm.d_ff_shared <= kGemvMaxH;
+}
+
+struct Layout {
+  size_t counter, parts, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, h, hs, y_rows, total;
+};
+
+Layout layout_of(const moe_dims& dm, int32_t T) {
+  Layout L;
+  const size_t P = (size_t)T * dm.top_k, E = dm.n_experts, d = dm.d_model;
+  size_t o = 0;
+  L.counter = o;
+  o += up(256);
+  L.parts = o;
+  o += up(d / 64 * E * 4);
+  L.ids = o;
+  o += up(P * 4);
+  L.w = o;
+  o += up(P * 4);
+  L.counts = o;
+  o += up(E * 4);
+  L.offsets = o;
+  o += up((E + 1) * 4);
+  L.sorted = o;
+  o += up(P * 4);
+  L.inv_pos = o;
+  o += up(P * 4);
+  L.tiles = o;
+  o += up((size_t)max_tiles_of(dm, T) * 12);
+  L.n_tiles = o;
+  o += up(4);
+  L.h = o;
+  o += up(P * dm.d_ff * 2);
+  L.hs = o;
+  o += up((size_t)T * dm.d_ff_shared * 2);
+  L.y_rows = o;
+  o += up((P + T) * d * 4);
+  L.total = o;
+  return L;
+}
+
+int check_q4(const moe_q4& q, const char* what) {
+  if (!q.codes || !q.scales || !q.biases) return fail(MOE_EINVAL, "%s: NULL codes/scales/biases", what);
+  if (!aligned(q.codes, 16)) return fail(MOE_EINVAL, "%s: codes not 16-byte aligned", what);
+  if (!aligned(q.scales, 4) || !aligned(q.biases, 4)) return fail(MOE_EINVAL, "%s: scales/biases not 4-byte aligned", what);
+  return MOE_OK;
+}
+
+int check_ffn(const moe_ffn_q4* f, const char* what) {
+  if (!f) return fail(MOE_EINVAL, "%s weights are NULL", what);
+  char buf[64];
+  const char* names[3] = {"gate", "up", "down"};
+  const moe_q4* qs[3] = {&f->gate, &f->up, &f->down};
+  for (int i = 0; i < 3; ++i) {
+    snprintf(buf, sizeof(buf), "%s.%s", what, names[i]);
+    if (int rc = check_q4(*qs[i], buf)) return rc;
+  }
+  return MOE_OK;
+}
+
+int check_routing(const moe_routing* r) {
+  if (!r) return fail(MOE_EINVAL, "routing is NULL");
+  const void* ps[8] = {r->topk_ids, r->topk_w, r->counts, r->offsets, r->sorted_token, r->inv_pos, r->tiles, r->n_tiles};
+  for (const void* p : ps)
+    if (!p || !aligned(p, 4)) return fail(MOE_EINVAL, "routing array NULL or not 4-byte aligned");
+  return MOE_OK;
+}
+
+int check_ws(const moe_dims& dm, int32_t T, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_EINVAL, "workspace not 256-byte aligned");
+  const size_t need = layout_of(dm, T).total;
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+enum Stage { kRouterDecode, kRouterPrefill, kMeta, kGemvGateup, kGemvDown, kGemmGateup, kGemmDown, kCombine };
+const char* kStageNames[] = {"router_decode", "router_prefill", "route_meta", "gemv_gateup",
+                             "gemv_down_combine", "gateup_gemm", "down_gemm", "combine"};
+
+int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
+  int n = 0;
+  out[n++] = T == 1 ? kRouterDecode : kRouterPrefill;
+  if (gemv_path(dm, T)) {
+    out[n++] = kGemvGateup;
+    out[n++] = kGemvDown;
+  } else {
+    out[n++] = kMeta;
+    out[n++] = kGemmGateup;
+    out[n++] = kGemmDown;
+    out[n++] = kCombine;
+  }
+  return n;
+}
+
+int run_stage(Stage s, const Ctx& c) {
+  hipError_t e = hipSuccess;
+  switch (s) {
+    case kRouterDecode: e = launch_router_decode(c); break;
+    case kRouterPrefill: e = launch_router_prefill(c); break;
+    case kMeta: e = launch_route_meta(c); break;
+    case kGemvGateup: e = launch_gemv_gateup(c); break;
+    case kGemvDown: e = launch_gemv_down_combine(c); break;
+    case kGemmGateup: e = launch_gateup_gemm(c); break;
+    case kGemmDown: e = launch_down_gemm(c); break;
+    case kCombine: e = launch_combine(c); break;
+  }
+  if (e != hipSuccess) return fail(MOE_EHIP, "launch of %s failed: %s", kStageNames[s], hipGetErrorString(e));
+  return MOE_OK;
+}
+
+void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t stream) {
+  const Layout L = layout_of(dm, T);
+  char* b = static_cast<char*>(ws);
+  c.d = dm.d_model;
+  c.E = dm.n_experts;
+  c.k = dm.top_k;
+  c.I = dm.d_ff;
+  c.Is = dm.d_ff_shared;
+  c.T = T;
+  c.P = T * dm.top_k;
+  c.max_tiles = max_tiles_of(dm, T);
+  c.counter = reinterpret_cast<unsigned*>(b + L.counter);
+  c.router_parts = reinterpret_cast<float*>(b + L.parts);
+  c.h = reinterpret_cast<uint16_t*>(b + L.h);
+  c.hs = reinterpret_cast<uint16_t*>(b + L.hs);
+  c.y_rows = reinterpret_cast<float*>(b + L.y_rows);
+  c.r.topk_ids = reinterpret_cast<int32_t*>(b + L.ids);
+  c.r.topk_w = reinterpret_cast<float*>(b + L.w);
+  c.r.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  c.r.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  c.r.sorted_token = reinterpret_cast<int32_t*>(b + L.sorted);
+  c.r.inv_pos = reinterpret_cast<int32_t*>(b + L.inv_pos);
+  c.r.tiles = reinterpret_cast<int32_t*>(b + L.tiles);
+  c.r.n_tiles = reinterpret_cast<int32_t*>(b + L.n_tiles);
+  c.stream = stream;
+  c.x = nullptr;
+  c.w_router = nullptr;
+  c.logit_bias = nullptr;
+  c.y = nullptr;
+  memset(&c.routed, 0, sizeof(c.routed));
+  memset(&c.shared, 0, sizeof(c.shared));
+}
+
+int check_layer_args(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router, bool need_router,
+                     const moe_ffn_q4* routed, const moe_ffn_q4* shared, const uint16_t* y, void* ws, size_t ws_bytes) {
+  if (int rc = check_dims(dims, T)) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x NULL or not 16-byte aligned");
+  if (need_router && (!w_router || !aligned(w_router, 16)))
+    return fail(MOE_EINVAL, "w_router NULL or not 16-byte aligned");
+  if (int rc = check_ffn(routed, "routed")) return rc;
+  if (dims->d_ff_shared > 0) {
+    if (int rc = check_ffn(shared, "shared")) return rc;
+  } else if (shared) {
+    return fail(MOE_EINVAL, "shared weights given but d_ff_shared == 0");
+  }
+  if (!y || !aligned(y, 16)) return fail(MOE_EINVAL, "y NULL or not 16-byte aligned");
+  if ((const void*)y == (const void*)x) return fail(MOE_EINVAL, "y aliases x");
+  return check_ws(*dims, T, ws, ws_bytes);
+}
+
+int layer_ctx(Ctx& c, const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+              const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y, void* ws,
+              void* stream) {
+  fill_ctx(c, *dims, T, ws, static_cast<hipStream_t>(stream));
+  c.x = x;
+  c.w_router = w_router;
+  c.logit_bias = logit_bias;
+  c.routed = *routed;
+  if (shared) c.shared = *shared;
+  c.y = y;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_max_tiles(const moe_dims* dims, int32_t T) {
+  if (check_dims(dims, T)) return -1;
+  return max_tiles_of(*dims, T);
+}
+
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t T) {
+  if (check_dims(dims, T)) return 0;
+  return layout_of(*dims, T).total;
+}
+
+int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router, const float* logit_bias,
+              const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_dims(dims, T)) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x NULL or not 16-byte aligned");
+  if (!w_router || !aligned(w_router, 16)) return fail(MOE_EINVAL, "w_router NULL or not 16-byte aligned");
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(MOE_EINVAL, "logit_bias not 4-byte aligned");
+  if (int rc = check_routing(out)) return rc;
+  if (int rc = check_ws(*dims, T, ws, ws_bytes)) return rc;
+  if (T == 0) return MOE_OK;
+  Ctx c;
+  fill_ctx(c, *dims, T, ws, static_cast<hipStream_t>(stream));
+  c.x = x;
+  c.w_router = w_router;
+  c.logit_bias = logit_bias;
+  c.r = *out;
+  if (int rc = run_stage(T == 1 ? kRouterDecode : kRouterPrefill, c)) return rc;
+  return run_stage(kMeta, c);
+}
+
+int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_routing* routing,
+                   const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (int rc = check_dims(dims, T)) return rc;
+  if (T == 0) return MOE_OK;
+  if (int rc = check_routing(routing)) return rc;
+  if (int rc = check_layer_args(dims, T, x, nullptr, false, routed, shared, y, ws, ws_bytes)) return rc;
+  if (T == 0) return MOE_OK;
+  Ctx c;
+  layer_ctx(c, dims, T, x, nullptr, nullptr, routed, shared, y, ws, stream);
+  c.r = *routing;
+  if (gemv_path(*dims, T)) {
+    if (int rc = run_stage(kGemvGateup, c)) return rc;
+    return run_stage(kGemvDown, c);
+  }
+  if (int rc = run_stage(kGemmGateup, c)) return rc;
+  if (int rc = run_stage(kGemmDown, c)) return rc;
+  return run_stage(kCombine, c);
+}
+
+int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+                      const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_layer_args(dims, T, x, w_router, true, routed, shared, y, ws, ws_bytes)) return rc;
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(MOE_EINVAL, "logit_bias not 4-byte aligned");
+  if (T == 0) return MOE_OK;
+  Ctx c;
+  layer_ctx(c, dims, T, x, w_router, logit_bias, routed, shared, y, ws, stream);
+  Stage st[8];
+  const int n = layer_stages(*dims, T, st);
+  for (int i = 0; i < n; ++i)
+    if (int rc = run_stage(st[i], c)) return rc;
+  return MOE_OK;
+}
+
+int32_t moe_num_stages(const moe_dims* dims, int32_t T) {
+  if (check_dims(dims, T) || T == 0) return 0;
+  Stage st[8];
+  return layer_stages(*dims, T, st);
+}
+
+const char* moe_stage_name(const moe_dims* dims, int32_t T, int32_t stage) {
+  if (check_dims(dims, T) || T == 0) return nullptr;
+  Stage st[8];
+  const int n = layer_stages(*dims, T, st);
+  if (stage < 0 || stage >= n) return nullptr;
+  return kStageNames[st[stage]];
+}
+
+int moe_launch_stage(int32_t stage, const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+                     const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_layer_args(dims, T, x, w_router, true, routed, shared, y, ws, ws_bytes)) return rc;
+  if (T == 0) return fail(MOE_EINVAL, "no stages at T = 0");
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(MOE_EINVAL, "logit_bias not 4-byte aligned");
+  Stage st[8];
+  const int n = layer_stages(*dims, T, st);
+  if (stage < 0 || stage >= n) return fail(MOE_EINVAL, "stage %d out of range [0, %d)", stage, n);
+  Ctx c;
+  layer_ctx(c, dims, T, x, w_router, logit_bias, routed, shared, y, ws, stream);
+  return run_stage(st[stage], c);
+}
+
+int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream) {
+  if (!w) return fail(MOE_EINVAL, "weights are NULL");
+  if (int rc = check_q4(*w, "weights")) return rc;
+  if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MOE_EINVAL, "out NULL or not 16-byte aligned");
+  if (rows < 0) return fail(MOE_EINVAL, "rows < 0");
+  if (in_dim < 64 || in_dim % 64) return fail(MOE_EUNSUPPORTED, "in_dim = %d must be a positive multiple of 64", in_dim);
+  if (rows == 0) return MOE_OK;
+  if (rows * (in_dim / 64) > (int64_t)1 << 38) return fail(MOE_EUNSUPPORTED, "too many rows");
+  hipError_t e = launch_dequant(*w, rows, in_dim, out_bf16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "launch of dequant failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: dimensions outside the supported limits";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

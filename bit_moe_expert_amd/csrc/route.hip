@@ -1,0 +1,265 @@
+// Router, top-k and routing metadata on the GPU (no host round trip).
+//
+// The method keeps histogram, prefix scan, scatter and block map inside one GPU submission
+// ("Perplexity's Lily Beats MLX-LM on MacBook M5. Because It Only Runs One Model.", section
+// "Prefill: keep routing on the GPU, dequantize in flight"); the router scores every expert
+// and keeps the top k (same page, "Why Qwen3.6-35B-A3B is a weird workload").
+//
+// Logit order (fixed so the top-k choice is unique): the input dimension is cut into chunks of
+// 64; a chunk partial is an fp32 fma chain over ascending inputs from +0; partials are added in
+// ascending chunk order to a +0 accumulator; the bias is added last.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// Decode (T == 1): one wave per (chunk, 64 experts) so the 4*d*E bytes of router weights are
+// read by many CUs at once. The last block to arrive sums the partials in chunk order, then one
+// wave takes the top-k and the softmax. The arrival counter is reset by that block.
+__global__ __launch_bounds__(64) void k_router_decode(int d, int E, int k, const uint16_t* __restrict__ x,
+                                                      const float* __restrict__ wr, const float* __restrict__ bias,
+                                                      float* __restrict__ parts, unsigned* __restrict__ counter,
+                                                      int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int nchunks = d / kGroup;
+  const int c = blockIdx.x % nchunks;
+  const int e = (blockIdx.x / nchunks) * 64 + threadIdx.x;
+  if (e < E) {
+    const float* wp = wr + (size_t)c * kGroup * E + e;
+    const uint16_t* xp = x + c * kGroup;
+    float v[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) part = fmaf(bf16_to_f32(xp[i]), v[i], part);
+    parts[(size_t)c * E + e] = part;
+  }
+  __shared__ int s_last;
+  __shared__ float s_lg[kMaxExperts];
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int ee = threadIdx.x; ee < E; ee += 64) {
+    float acc = 0.0f;
+    for (int cc = 0; cc < nchunks; ++cc)
+      acc = acc + __hip_atomic_load(parts + (size_t)cc * E + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (bias) acc = acc + bias[ee];
+    s_lg[ee] = acc;
+  }
+  __syncthreads();
+  wave_topk_softmax(s_lg, E, k, ids, w);
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_router_decode(const Ctx& c) {
+  const int nchunks = c.d / kGroup;
+  const int nblk = nchunks * ((c.E + 63) / 64);
+  hipLaunchKernelGGL(k_router_decode, dim3(nblk), dim3(64), 0, c.stream, c.d, c.E, c.k, c.x, c.w_router,
+                     c.logit_bias, c.router_parts, c.counter, c.r.topk_ids, c.r.topk_w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Prefill (T >= 2): a block owns 4 tokens and all experts. Its 16 waves each reduce one chunk
+// for 4 tokens x 256 experts (lane owns experts lane + 64q); the chunk partials meet in LDS and
+// are added in chunk order by one thread per (token, expert). Then one wave per token takes
+// the top-k and the softmax.
+constexpr int kRpTok = 4;
+constexpr int kRpWaves = 16;
+
+__global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, int k, const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ wr, const float* __restrict__ bias,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ float s_parts[kRpWaves][kRpTok][256];          // 64 KB
+  __shared__ __attribute__((aligned(16))) float s_x[kRpWaves * kGroup][kRpTok];  // 16 KB, [input][token]
+  __shared__ float s_lg[kRpTok][kMaxExperts];               // 16 KB
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kRpTok;
+  const int nchunks = d / kGroup;
+  const int s_tok = tid >> 8, s_e = tid & 255;
+  for (int eb = 0; eb < E; eb += 256) {
+    float acc = 0.0f;
+    for (int p = 0; p < nchunks; p += kRpWaves) {
+      const int npass = min(kRpWaves, nchunks - p);
+      for (int idx = tid; idx < kRpWaves * kGroup * kRpTok; idx += 1024) {
+        const int tk = idx / (kRpWaves * kGroup), i = idx % (kRpWaves * kGroup);
+        float v = 0.0f;
+        if (t0 + tk < T && i < npass * kGroup) v = bf16_to_f32(x[(size_t)(t0 + tk) * d + p * kGroup + i]);
+        s_x[i][tk] = v;
+      }
+      __syncthreads();
+      if (wave < npass) {
+        const int c = p + wave;
+        float pr[kRpTok][4];
+#pragma unroll
+        for (int tk = 0; tk < kRpTok; ++tk)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pr[tk][q] = 0.0f;
+        const float* wp = wr + (size_t)c * kGroup * E + eb + lane;
+        for (int i = 0; i < kGroup; ++i) {
+          float wv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wv[q] = (eb + lane + 64 * q < E) ? wp[(size_t)i * E + 64 * q] : 0.0f;
+          const float4 xv = *reinterpret_cast<const float4*>(&s_x[wave * kGroup + i][0]);
+          const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int tk = 0; tk < kRpTok; ++tk)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pr[tk][q] = fmaf(xs[tk], wv[q], pr[tk][q]);
+        }
+#pragma unroll
+        for (int tk = 0; tk < kRpTok; ++tk)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s_parts[wave][tk][lane + 64 * q] = pr[tk][q];
+      }
+      __syncthreads();
+      for (int cc = 0; cc < npass; ++cc) acc = acc + s_parts[cc][s_tok][s_e];
+      __syncthreads();
+    }
+    const int e = eb + s_e;
+    if (e < E) {
+      float v = acc;
+      if (bias) v = v + bias[e];
+      s_lg[s_tok][e] = v;
+    }
+  }
+  __syncthreads();
+  if (wave < kRpTok && t0 + wave < T)
+    wave_topk_softmax(s_lg[wave], E, k, ids + (size_t)(t0 + wave) * k, w + (size_t)(t0 + wave) * k);
+}
+
+hipError_t launch_router_prefill(const Ctx& c) {
+  const int nblk = (c.T + kRpTok - 1) / kRpTok;
+  hipLaunchKernelGGL(k_router_prefill, dim3(nblk), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.k, c.x, c.w_router,
+                     c.logit_bias, c.r.topk_ids, c.r.topk_w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Histogram, prefix scan, stable scatter and block map in one 1024-thread block.
+// Wave w owns the contiguous pair range [w*span, (w+1)*span). Pass 1 counts per wave and
+// expert in LDS (atomics only for counts). A scan over experts gives offsets; a scan over waves
+// per expert gives each wave's first row in every group. Pass 2 walks the range again in steps
+// of 64 pairs: lanes with the same expert find each other with 10 ballots (one per bit of the
+// expert id), so a lane's rank is the popcount of its lower peers; the lowest peer advances the
+// wave's cursor. Rows of an expert therefore follow pair order, i.e. ascending token.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < (int)(blockDim.x >> 6) ? s_wsum[lane] : 0;
+    int ti = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(ti, o, 64);
+      if (lane >= o) ti += n;
+    }
+    if (lane < (int)(blockDim.x >> 6)) s_wsum[lane] = ti - t;
+    if (lane == 63) s_wsum[16] = ti;
+  }
+  __syncthreads();
+  const int r = s_wsum[wave] + incl - v;
+  *total = s_wsum[16];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared,
+                                                     const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
+                                                     int32_t* __restrict__ inv_pos, int32_t* __restrict__ tiles,
+                                                     int32_t* __restrict__ n_tiles) {
+  __shared__ int s_tab[16][kMaxExperts];  // 64 KB: per-wave counts, then per-wave cursors
+  __shared__ int s_wsum[17];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = T * k;
+  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&s_tab[0][0])[i] = 0;
+  __syncthreads();
+  const int span = (((P + 15) / 16) + 63) & ~63;
+  const int p_begin = min(P, wave * span), p_end = min(P, p_begin + span);
+  for (int p = p_begin + lane; p < p_end; p += 64) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_tab[wave][e], 1);
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int w2 = 0; w2 < 16; ++w2) cnt += s_tab[w2][tid];
+  int total = 0;
+  const int off = block_excl_scan(tid < E ? cnt : 0, s_wsum, &total);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    int run = off;
+    for (int w2 = 0; w2 < 16; ++w2) {
+      const int c2 = s_tab[w2][tid];
+      s_tab[w2][tid] = run;
+      run += c2;
+    }
+  }
+  if (tid == 0) offsets[E] = total;
+  // block map: routed tiles in expert order, then the shared expert's rows
+  const int nt = tid < E ? (cnt + kTileRows - 1) / kTileRows : 0;
+  int n_routed = 0;
+  const int tfirst = block_excl_scan(nt, s_wsum, &n_routed);
+  for (int j = 0; j < nt; ++j) {
+    int32_t* tl = tiles + 3 * (size_t)(tfirst + j);
+    tl[0] = tid;
+    tl[1] = off + j * kTileRows;
+    tl[2] = min(kTileRows, cnt - j * kTileRows);
+  }
+  const int n_shared = has_shared ? (T + kTileRows - 1) / kTileRows : 0;
+  for (int j = tid; j < n_shared; j += 1024) {
+    int32_t* tl = tiles + 3 * (size_t)(n_routed + j);
+    tl[0] = E;
+    tl[1] = P + j * kTileRows;
+    tl[2] = min(kTileRows, T - j * kTileRows);
+  }
+  if (tid == 0) *n_tiles = n_routed + n_shared;
+  __syncthreads();
+  // pass 2: stable ranks
+  for (int base = p_begin; base < p_end; base += 64) {
+    const int p = base + lane;
+    const bool act = p < p_end;
+    int e = act ? ids[p] : 0;
+    const bool valid = act && (unsigned)e < (unsigned)E;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(valid && bit);
+      peers &= bit ? bb : ~bb;
+    }
+    int pos = 0;
+    if (valid) pos = s_tab[wave][e] + __popcll(peers & lanemask_lt());
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      sorted_token[pos] = p / k;
+      inv_pos[p] = pos;
+    }
+  }
+}
+
+hipError_t launch_route_meta(const Ctx& c) {
+  hipLaunchKernelGGL(k_route_meta, dim3(1), dim3(1024), 0, c.stream, c.T, c.E, c.k, c.Is > 0 ? 1 : 0, c.r.topk_ids,
+                     c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos, c.r.tiles, c.r.n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,275 @@
+"""Python binding of libmoe_int4.so (the routed int4 MoE FFN for MI355X).
+
+Argument marshalling only: tensors are checked for device, dtype and contiguity, then
+their data pointers and torch's current HIP stream go to the C ABI (include/moe_int4.h).
+Every step of the computation runs in the library's gfx950 kernels; there is no CPU
+fallback, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Dict, Optional
+
+import torch  # imported first: the library must bind to the HIP runtime torch already loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        L = lib()
+        super().__init__(f"{where}: {L.moe_status_str(status).decode()} ({L.moe_last_error().decode()})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class Q4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class FFNQ4(ctypes.Structure):
+    _fields_ = [("gate", Q4), ("up", Q4), ("down", Q4)]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_ids", "topk_w", "counts", "offsets", "sorted_token", "inv_pos", "tiles", "n_tiles")]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library once. Raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with bit_moe_expert_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, vp, i32, i64, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.moe_max_tiles.argtypes = [P(Dims), i32]
+        L.moe_max_tiles.restype = i32
+        L.moe_workspace_bytes.argtypes = [P(Dims), i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_route.argtypes = [P(Dims), i32, vp, vp, vp, P(Routing), vp, sz, vp]
+        L.moe_expert_ffn.argtypes = [P(Dims), i32, vp, P(Routing), P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
+        L.moe_forward_layer.argtypes = [P(Dims), i32, vp, vp, vp, P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
+        L.moe_debug_dequant.argtypes = [P(Q4), i64, i32, vp, vp]
+        L.moe_num_stages.argtypes = [P(Dims), i32]
+        L.moe_num_stages.restype = i32
+        L.moe_stage_name.argtypes = [P(Dims), i32, i32]
+        L.moe_stage_name.restype = ctypes.c_char_p
+        L.moe_launch_stage.argtypes = [i32, P(Dims), i32, vp, vp, vp, P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_launch_stage"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def make_dims(d: int, E: int, k: int, I: int, Is: int) -> Dims:
+    return Dims(d, E, k, I, Is, 64)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, device=None) -> Optional[int]:
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+@dataclasses.dataclass
+class QProj:
+    """One projection of n experts: codes [n][out][in/2] uint8, scales/biases [n][out][in/64] bf16."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+
+    def struct(self, device=None) -> Q4:
+        return Q4(_ptr(self.codes, torch.uint8, "codes", device), _ptr(self.scales, torch.bfloat16, "scales", device),
+                  _ptr(self.biases, torch.bfloat16, "biases", device))
+
+
+@dataclasses.dataclass
+class QuantFFN:
+    gate: QProj
+    up: QProj
+    down: QProj
+
+    def struct(self, device=None) -> FFNQ4:
+        return FFNQ4(self.gate.struct(device), self.up.struct(device), self.down.struct(device))
+
+    @property
+    def n_experts(self) -> int:
+        return self.gate.codes.shape[0]
+
+    @property
+    def d_ff(self) -> int:
+        return self.gate.codes.shape[1]
+
+    @property
+    def d_model(self) -> int:
+        return self.down.codes.shape[1]
+
+
+def _dims_for(x: torch.Tensor, routed: QuantFFN, shared: Optional[QuantFFN], k: int) -> Dims:
+    return make_dims(x.shape[1], routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff)
+
+
+def max_tiles(dims: Dims, T: int) -> int:
+    return lib().moe_max_tiles(ctypes.byref(dims), T)
+
+
+def workspace_bytes(dims: Dims, T: int) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(dims), T)
+
+
+def new_workspace(dims: Dims, T: int, device) -> torch.Tensor:
+    """Zero-filled workspace (the ABI needs its first 256 bytes zero before first use)."""
+    n = workspace_bytes(dims, T)
+    if n == 0:
+        raise MoeError(MOE_EUNSUPPORTED, "workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def new_routing(dims: Dims, T: int, device) -> Dict[str, torch.Tensor]:
+    k, E = dims.top_k, dims.n_experts
+    i32 = dict(dtype=torch.int32, device=device)
+    return {
+        "topk_ids": torch.empty((T, k), **i32), "topk_w": torch.empty((T, k), dtype=torch.float32, device=device),
+        "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+        "sorted_token": torch.empty(T * k, **i32), "inv_pos": torch.empty((T, k), **i32),
+        "tiles": torch.empty((max(max_tiles(dims, T), 1), 3), **i32), "n_tiles": torch.empty(1, **i32),
+    }
+
+
+def _routing_struct(r: Dict[str, torch.Tensor], device) -> Routing:
+    return Routing(*[_ptr(r[n], torch.float32 if n == "topk_w" else torch.int32, n, device)
+                     for n, _ in Routing._fields_])
+
+
+def route(x: torch.Tensor, w_router: torch.Tensor, k: int, d_ff: int, d_ff_shared: int,
+          logit_bias: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """moe_route: top-k, gate weights and the routing metadata of T tokens."""
+    T, d = x.shape
+    dims = make_dims(d, w_router.shape[1], k, d_ff, d_ff_shared)
+    dev = x.device
+    ws = new_workspace(dims, T, dev) if ws is None else ws
+    r = new_routing(dims, T, dev)
+    rs = _routing_struct(r, dev)
+    rc = lib().moe_route(ctypes.byref(dims), T, _ptr(x, torch.bfloat16, "x", dev),
+                         _ptr(w_router, torch.float32, "w_router", dev), _ptr(logit_bias, torch.float32, "logit_bias", dev),
+                         ctypes.byref(rs), _ptr(ws, torch.uint8, "ws", dev), ws.numel(), _stream(dev))
+    _check(rc, "moe_route")
+    return r
+
+
+def expert_ffn(x: torch.Tensor, routing: Dict[str, torch.Tensor], routed: QuantFFN, shared: Optional[QuantFFN],
+               ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_expert_ffn: the expert FFN of routed tokens (grouped GEMM for T >= 2, GEMV at T = 1)."""
+    T, d = x.shape
+    k = routing["topk_ids"].shape[1]
+    dims = _dims_for(x, routed, shared, k)
+    dev = x.device
+    ws = new_workspace(dims, T, dev) if ws is None else ws
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if y is None else y
+    rs = _routing_struct(routing, dev)
+    rf = routed.struct(dev)
+    sf = shared.struct(dev) if shared is not None else None
+    rc = lib().moe_expert_ffn(ctypes.byref(dims), T, _ptr(x, torch.bfloat16, "x", dev), ctypes.byref(rs),
+                              ctypes.byref(rf), ctypes.byref(sf) if sf is not None else None,
+                              _ptr(y, torch.bfloat16, "y", dev), _ptr(ws, torch.uint8, "ws", dev), ws.numel(),
+                              _stream(dev))
+    _check(rc, "moe_expert_ffn")
+    return y
+
+
+class Layer:
+    """Marshalled arguments of moe_forward_layer for one layer, reusable across calls."""
+
+    def __init__(self, w_router: torch.Tensor, routed: QuantFFN, shared: Optional[QuantFFN], k: int,
+                 logit_bias: Optional[torch.Tensor] = None):
+        self.dev = w_router.device
+        self.w_router, self.routed, self.shared, self.k, self.logit_bias = w_router, routed, shared, k, logit_bias
+        self.dims = make_dims(routed.d_model, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff)
+        if w_router.shape != (self.dims.d_model, self.dims.n_experts):
+            raise ValueError(f"w_router shape {tuple(w_router.shape)} does not match the experts")
+        self._wr = _ptr(w_router, torch.float32, "w_router", self.dev)
+        self._bias = _ptr(logit_bias, torch.float32, "logit_bias", self.dev)
+        self._rf = routed.struct(self.dev)
+        self._sf = shared.struct(self.dev) if shared is not None else None
+
+    def args(self, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor):
+        T = x.shape[0]
+        if x.shape[1] != self.dims.d_model or y.shape != x.shape:
+            raise ValueError("x / y shape mismatch")
+        return (ctypes.byref(self.dims), T, _ptr(x, torch.bfloat16, "x", self.dev), self._wr, self._bias,
+                ctypes.byref(self._rf), ctypes.byref(self._sf) if self._sf is not None else None,
+                _ptr(y, torch.bfloat16, "y", self.dev), _ptr(ws, torch.uint8, "ws", self.dev), ws.numel(),
+                _stream(self.dev))
+
+    def workspace(self, T: int) -> torch.Tensor:
+        return new_workspace(self.dims, T, self.dev)
+
+    def forward(self, x: torch.Tensor, ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+        T = x.shape[0]
+        ws = self.workspace(T) if ws is None else ws
+        y = torch.empty_like(x) if y is None else y
+        _check(lib().moe_forward_layer(*self.args(x, y, ws)), "moe_forward_layer")
+        return y
+
+    def stages(self, T: int):
+        L = lib()
+        n = L.moe_num_stages(ctypes.byref(self.dims), T)
+        return [L.moe_stage_name(ctypes.byref(self.dims), T, s).decode() for s in range(n)]
+
+    def launch_stage(self, stage: int, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor) -> None:
+        _check(lib().moe_launch_stage(stage, *self.args(x, y, ws)), "moe_launch_stage")
+
+
+def forward_layer(x: torch.Tensor, w_router: torch.Tensor, routed: QuantFFN, shared: Optional[QuantFFN], k: int,
+                  logit_bias: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_forward_layer: route + expert FFN + combine for T tokens."""
+    return Layer(w_router, routed, shared, k, logit_bias).forward(x, ws, y)
+
+
+def debug_dequant(p: QProj) -> torch.Tensor:
+    """moe_debug_dequant: bf16 expansion of a projection, with the grouped GEMM's own routine."""
+    codes = p.codes
+    in_dim = codes.shape[-1] * 2
+    rows = codes.numel() // codes.shape[-1]
+    dev = codes.device
+    out = torch.empty(tuple(codes.shape[:-1]) + (in_dim,), dtype=torch.bfloat16, device=dev)
+    q = p.struct(dev)
+    rc = lib().moe_debug_dequant(ctypes.byref(q), rows, in_dim, _ptr(out, torch.bfloat16, "out", dev), _stream(dev))
+    _check(rc, "moe_debug_dequant")
+    return out

@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, sizes its
+workspace, and rejects bad arguments before any HIP call (CPU only, no kernel launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import bit_moe_expert_amd as pkg
+from bit_moe_expert_amd import moe
+
+HEADER = os.path.join(ROOT, "include", "moe_int4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char\s*\*)\s+(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and nothing of the oracle is linked in
+    syms = open(moe.LIB_PATH, "rb").read()
+    assert b"oracle_" not in syms
+
+
+def _dims(d=2048, E=256, k=8, I=512, Is=512, g=64):
+    return moe.Dims(d, E, k, I, Is, g)
+
+
+def test_sizing_helpers():
+    d = _dims()
+    assert moe.max_tiles(d, 512) == 256 + 4096 // 128 + 4
+    assert moe.max_tiles(d, 1) == 8 + 0 + 1
+    assert moe.max_tiles(_dims(E=128, I=768, Is=0), 256) == 128 + 16
+    ws = moe.workspace_bytes(d, 512)
+    assert ws % 256 == 0 and ws >= (4096 + 512) * 2048 * 4 + 4096 * 512 * 2
+    assert moe.workspace_bytes(d, 0) > 0
+    assert moe.workspace_bytes(_dims(g=32), 8) == 0
+    assert moe.max_tiles(_dims(k=17), 8) == -1
+
+
+def test_stage_lists():
+    L = moe.lib()
+    d = _dims()
+    n1 = L.moe_num_stages(ctypes.byref(d), 1)
+    assert [L.moe_stage_name(ctypes.byref(d), 1, s).decode() for s in range(n1)] == \
+        ["router_decode", "gemv_gateup", "gemv_down_combine"]
+    n2 = L.moe_num_stages(ctypes.byref(d), 512)
+    assert [L.moe_stage_name(ctypes.byref(d), 512, s).decode() for s in range(n2)] == \
+        ["router_prefill", "route_meta", "gateup_gemm", "down_gemm", "combine"]
+    assert L.moe_stage_name(ctypes.byref(d), 512, 5) is None
+    big = _dims(k=16, I=2048)  # too much h for the GEMV path: T = 1 runs the grouped GEMM
+    assert L.moe_num_stages(ctypes.byref(big), 1) == 5
+
+
+class _Fake:
+    """Non-null, suitably aligned fake device addresses: validation never dereferences them."""
+
+    def __init__(self):
+        self.base = 1 << 40
+        self.n = 0
+
+    def __call__(self, align=256):
+        self.n += 1
+        return self.base + self.n * (1 << 20)
+
+
+def _ffn(f):
+    q = lambda: moe.Q4(f(), f(), f())  # noqa: E731
+    return moe.FFNQ4(q(), q(), q())
+
+
+def _layer_call(dims, T, f, **over):
+    a = dict(x=f(), wr=f(), bias=None, routed=_ffn(f), shared=_ffn(f), y=f(), ws=f(), ws_bytes=1 << 40)
+    a.update(over)
+    L = moe.lib()
+    return L.moe_forward_layer(ctypes.byref(dims), T, a["x"], a["wr"], a["bias"],
+                               ctypes.byref(a["routed"]) if a["routed"] is not None else None,
+                               ctypes.byref(a["shared"]) if a["shared"] is not None else None,
+                               a["y"], a["ws"], a["ws_bytes"], None)
+
+
+def test_validation_codes_before_any_hip_call():
+    f = _Fake()
+    d = _dims()
+    L = moe.lib()
+    assert _layer_call(d, 0, f) == moe.MOE_OK  # T = 0: no-op
+    assert _layer_call(d, -1, f) == moe.MOE_EINVAL
+    assert _layer_call(_dims(g=32), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(_dims(d=100), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(_dims(k=9, E=8), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(_dims(k=17, E=64), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(_dims(E=2048), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(_dims(I=96), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(d, 70000, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(d, 4, f, x=None) == moe.MOE_EINVAL
+    assert _layer_call(d, 4, f, x=f() + 2) == moe.MOE_EINVAL          # misaligned
+    assert _layer_call(d, 4, f, wr=None) == moe.MOE_EINVAL
+    assert _layer_call(d, 4, f, shared=None) == moe.MOE_EINVAL        # d_ff_shared > 0 needs them
+    assert _layer_call(_dims(Is=0), 4, f) == moe.MOE_EINVAL            # given but not expected
+    assert _layer_call(d, 4, f, y=None) == moe.MOE_EINVAL
+    x = f()
+    assert _layer_call(d, 4, f, x=x, y=x) == moe.MOE_EINVAL           # y aliases x
+    assert _layer_call(d, 4, f, ws=f() + 64) == moe.MOE_EINVAL        # ws alignment
+    assert _layer_call(d, 4, f, ws_bytes=1000) == moe.MOE_EWORKSPACE
+    bad = _ffn(f)
+    bad.down.codes = f() + 8
+    assert _layer_call(d, 4, f, routed=bad) == moe.MOE_EINVAL
+    assert "codes" in L.moe_last_error().decode()
+    assert L.moe_status_str(moe.MOE_EWORKSPACE).decode().startswith("MOE_EWORKSPACE")
+    # route and expert_ffn validate the same way
+    r = moe.Routing(*[f() for _ in range(8)])
+    assert L.moe_route(ctypes.byref(_dims(k=0)), 4, f(), f(), None, ctypes.byref(r), f(), 1 << 40, None) == \
+        moe.MOE_EUNSUPPORTED
+    r0 = moe.Routing(*([None] + [f() for _ in range(7)]))
+    assert L.moe_route(ctypes.byref(d), 4, f(), f(), None, ctypes.byref(r0), f(), 1 << 40, None) == moe.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), 0, f(), f(), None, ctypes.byref(r), f(), 1 << 40, None) == moe.MOE_OK
+    rf = _ffn(f)
+    assert L.moe_expert_ffn(ctypes.byref(d), 4, f(), ctypes.byref(r), ctypes.byref(rf), None, f(), f(), 1 << 40,
+                            None) == moe.MOE_EINVAL
+    assert L.moe_expert_ffn(ctypes.byref(d), 0, f(), ctypes.byref(r), ctypes.byref(rf), ctypes.byref(rf), f(), f(),
+                            1 << 40, None) == moe.MOE_OK
+    q = moe.Q4(f(), f(), f())
+    assert L.moe_debug_dequant(ctypes.byref(q), 4, 96, f(), None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_debug_dequant(ctypes.byref(q), 0, 128, f(), None) == moe.MOE_OK
+    assert L.moe_launch_stage(7, ctypes.byref(d), 4, f(), f(), None, ctypes.byref(rf), ctypes.byref(rf), f(), f(),
+                              1 << 40, None) == moe.MOE_EINVAL
+
+
+def test_binding_refuses_cpu_tensors_and_has_no_fallback():
+    import torch
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        moe._ptr(x, torch.bfloat16, "x")
+    # the product package never imports the oracle
+    src = "".join(open(os.path.join(ROOT, "bit_moe_expert_amd", n)).read() for n in ("moe.py", "__init__.py"))
+    assert "oracle" not in src.replace("oracle_", "")
+    assert pkg.moe.LIB_PATH.endswith("libmoe_int4.so")

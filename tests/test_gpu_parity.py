@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Bar: bit-exact routing (ids, counts, offsets, scatter order, inv_pos, block map) and
+dequantised weights; gate weights within 1e-5; outputs within 1e-2 * max|ref| + 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from workload import gen
+from bit_moe_expert_amd import moe
+from gpu_inputs import (DEV, bf16_dev, bits_host, check_routing, check_y, f32_dev, ffn_dev, layer_dev, proj_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need the MI355X"
+    yield
+    torch.cuda.synchronize()
+
+
+def _oracle_routing(x, wr, bias, k, has_shared):
+    logits = oracle.router_logits(x, wr, bias)
+    ids, w = oracle.topk_softmax(logits, k)
+    m = oracle.route_meta(ids, wr.shape[1], has_shared)
+    m.update(topk_ids=ids, topk_w=w)
+    return m
+
+
+def _custom(T, d, E, k, I, Is, sigma=0.05, seed=0, zipf=False):
+    return gen.Workload("custom", T, d, E, k, I, Is, sigma, 1, T, zipf=zipf, seed=seed)
+
+
+# ------------------------------------------------------------------ dequantisation (bit-exact)
+def test_dequant_bit_exact_workload_and_exhaustive_scales():
+    w = gen.WORKLOADS["prefill"]
+    L = gen.expert_weights(w, 0)
+    sl = slice(0, 3)
+    for name in ("gate", "down"):
+        p = {kk: v[sl] for kk, v in L[name].items()}
+        got = bits_host(moe.debug_dequant(proj_dev(p)))
+        assert (got == oracle.dequant(p["codes"], p["scales"], p["biases"])).all(), name
+    # every normal bf16 scale with 16*scale finite, all 16 codes, bias -8*scale and random biases
+    sbits = np.arange(0x0080, 0x7D00, dtype=np.uint32).astype(np.uint16)
+    n = sbits.size
+    q = np.tile(np.arange(16, dtype=np.uint8), 4)
+    codes = np.broadcast_to((q[0::2] | (q[1::2] << 4)).astype(np.uint8), (n, 32)).copy()
+    sf = (sbits.astype(np.uint32) << 16).view(np.float32)
+    b = oracle.round_bf16(-8.0 * sf)
+    rng = np.random.default_rng(5)
+    b2 = oracle.round_bf16(rng.standard_normal(n).astype(np.float32) * sf * rng.uniform(0, 20, n).astype(np.float32))
+    for bias in (b, b2):
+        p = {"codes": codes, "scales": sbits.reshape(n, 1), "biases": bias.reshape(n, 1)}
+        got = bits_host(moe.debug_dequant(proj_dev(p)))
+        assert (got == oracle.dequant(codes, p["scales"], p["biases"])).all()
+
+
+# ------------------------------------------------------------------ routing (bit-exact)
+ROUTE_CASES = [("tiny", 0, 0), ("decode", 0, 0), ("decode", 17, 0), ("decode", 39, 0), ("prefill", 0, 0),
+               ("long", 0, 0), ("long", 0, 3), ("diffusion", 0, 0), ("diffusion", 29, 0)]
+
+
+@pytest.mark.parametrize("name,layer,chunk", ROUTE_CASES)
+def test_route_workloads(name, layer, chunk):
+    w = gen.WORKLOADS[name]
+    x = gen.tokens(w, layer, chunk)
+    wr = gen.router(w, layer)
+    bias = gen.logit_bias(w)
+    r = moe.route(bf16_dev(x), f32_dev(wr), w.k, w.I, w.Is, f32_dev(bias))
+    check_routing(r, _oracle_routing(x, wr, bias, w.k, w.Is > 0), f"{name} layer {layer} chunk {chunk}")
+
+
+SMALL = [(T, E, k, Is) for T in (1, 2, 3, 8, 33, 257) for E, k in ((1, 1), (2, 1), (2, 2), (4, 2), (16, 1), (16, 4),
+                                                                    (16, 16)) for Is in (0, 64)]
+
+
+@pytest.mark.parametrize("T,E,k,Is", SMALL)
+def test_route_small_shapes(T, E, k, Is):
+    w = _custom(T, 128, E, k, 64, Is, seed=T * 131 + E * 7 + k)
+    x = gen.tokens(w, 0, 0)
+    wr = gen.router(w, 0)
+    r = moe.route(bf16_dev(x), f32_dev(wr), k, 64, Is)
+    check_routing(r, _oracle_routing(x, wr, None, k, Is > 0), f"T={T} E={E} k={k} Is={Is}")
+
+
+def test_route_ties_skew_and_large_groups():
+    w = _custom(300, 256, 64, 8, 64, 64, seed=3)
+    x = gen.tokens(w, 0, 0)
+    wr = gen.router(w, 0)
+    wr[:, 5] = wr[:, 2]    # exact ties: expert 2 must win over 5
+    wr[:, 40] = wr[:, 9]
+    r = moe.route(bf16_dev(x), f32_dev(wr), 8, 64, 64)
+    check_routing(r, _oracle_routing(x, wr, None, 8, True), "ties")
+    bias = np.zeros(64, np.float32)
+    bias[11] = 1e4         # every token picks expert 11 first: one group of 300 rows (3 tiles)
+    r = moe.route(bf16_dev(x), f32_dev(wr), 8, 64, 64, f32_dev(bias))
+    ref = _oracle_routing(x, wr, bias, 8, True)
+    check_routing(r, ref, "one big group")
+    assert ref["counts"][11] == 300
+    wl = gen.WORKLOADS["long"]
+    xb = gen.tokens(wl, 0, 1)
+    wrb = gen.router(wl, 0)
+    pb = gen.logit_bias(wl, permuted=True)
+    r = moe.route(bf16_dev(xb), f32_dev(wrb), 8, 512, 512, f32_dev(pb))
+    check_routing(r, _oracle_routing(xb, wrb, pb, 8, True), "permuted zipf")
+
+
+# ------------------------------------------------------------------ whole layer (tolerance)
+def _forward_check(w, layer=0, chunk=0, T=None, sel=None):
+    L = gen.layer(w, layer)
+    x = gen.tokens(w, layer, chunk, T)
+    lay = layer_dev(L, w.k)
+    y = lay.forward(bf16_dev(x))
+    torch.cuda.synchronize()
+    if sel is None:
+        ref = oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])
+        return check_y(y, ref["y"], f"{w.name} layer {layer} chunk {chunk}"), y, x, L
+    ref = oracle.forward_tokens(x, L["w_router"], L["routed"], L["shared"], w.k, sel, L["logit_bias"])
+    return check_y(y[torch.as_tensor(sel, device=DEV)], ref["y"], f"{w.name} sampled"), y, x, L
+
+
+def test_forward_tiny():
+    _forward_check(gen.WORKLOADS["tiny"])
+
+
+@pytest.mark.parametrize("layer", [0, 1, 20, 39])
+def test_forward_decode_layers(layer):
+    _forward_check(gen.WORKLOADS["decode"], layer=layer)
+
+
+def test_forward_prefill_full():
+    _forward_check(gen.WORKLOADS["prefill"])
+
+
+def test_forward_long_chunks():
+    w = gen.WORKLOADS["long"]
+    _forward_check(w, chunk=0)
+    rng = np.random.default_rng(0)
+    for c in (1, 2, 3):
+        _forward_check(w, chunk=c, sel=np.sort(rng.choice(w.chunk, 6, replace=False)))
+
+
+@pytest.mark.parametrize("layer", [0, 29])
+def test_forward_diffusion(layer):
+    _forward_check(gen.WORKLOADS["diffusion"], layer=layer)
+
+
+SHAPES = [
+    # (T, d, E, k, I, Is): ragged T, K tails (d or I = 64 mod 128), shared size != routed, no shared
+    (1, 256, 16, 4, 128, 128), (1, 192, 8, 2, 192, 64), (2, 256, 16, 4, 128, 128), (3, 192, 4, 2, 192, 0),
+    (33, 256, 8, 3, 64, 128), (257, 128, 16, 2, 128, 64), (130, 320, 2, 2, 64, 192), (5, 64, 1, 1, 64, 64),
+    (40, 128, 4, 4, 256, 0), (1, 128, 1, 1, 64, 0),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,I,Is", SHAPES)
+def test_forward_small_shapes(T, d, E, k, I, Is):
+    _forward_check(_custom(T, d, E, k, I, Is, seed=T + d + E))
+
+
+def test_decode_falls_back_to_grouped_gemm_when_h_is_large():
+    w = _custom(1, 256, 32, 16, 2048, 0, seed=9)
+    lay = layer_dev(gen.layer(w, 0), w.k)
+    assert lay.stages(1)[1] == "route_meta"
+    _forward_check(w)
+
+
+# ------------------------------------------------------------------ composition and determinism
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_route_then_expert_ffn_equals_forward_and_is_deterministic(name):
+    w = gen.WORKLOADS[name]
+    L = gen.layer(w, 0)
+    x = bf16_dev(gen.tokens(w, 0, 0))
+    lay = layer_dev(L, w.k)
+    y1 = lay.forward(x)
+    y2 = lay.forward(x)
+    r = moe.route(x, lay.w_router, w.k, w.I, w.Is, lay.logit_bias)
+    y3 = moe.expert_ffn(x, r, lay.routed, lay.shared)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    # the stages launched one by one reproduce the layer
+    ws = lay.workspace(x.shape[0])
+    y4 = torch.empty_like(x)
+    for s in range(len(lay.stages(x.shape[0]))):
+        lay.launch_stage(s, x, y4, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y4.view(torch.int16))
+
+
+def test_zero_tokens_is_a_noop():
+    w = gen.WORKLOADS["tiny"]
+    lay = layer_dev(gen.layer(w, 0), w.k)
+    x = torch.empty((0, w.d), dtype=torch.bfloat16, device=DEV)
+    y = lay.forward(x, ws=lay.workspace(1))
+    assert y.shape == (0, w.d)
