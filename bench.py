@@ -1,0 +1,332 @@
+"""Benchmark of the routed int4 MoE layer on one MI355X.
+
+Default workload (decode): one token through 40 distinct MoE layers (d=2048, 256 experts
+top-8 + shared, I=512, int4 groups of 64), so the 18.2 GB of expert weights stream from HBM
+rather than from the 256 MB cache. A step is one pass over the 40 layers, replayed as a HIP
+graph; value = MoE-layer tokens per second.
+
+Also reported, on the same stream with HIP events: each kernel's average duration, the
+dominant kernel's algorithmic bytes (or flops) per launch and its roofline fraction, and the
+CPU oracle timed on the host cores on a bounded sample of the same workload.
+
+Other workloads (--workload prefill|long|diffusion|tiny) exist for measurement; the one-line
+JSON contract is the same.
+
+Fail-closed: nothing is reported unless layer outputs match the CPU oracle and the graph
+replays reproduce the eager results bit for bit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402  (before the library: bind to torch's HIP runtime)
+
+from bit_moe_expert_amd import moe  # noqa: E402
+from workload import gen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+
+DESCR = {
+    "tiny": "tiny: T=8, d=256, 16 experts top-4 + shared (I=I_s=128), int4 g64",
+    "decode": "decode: T=1, d=2048, 256 experts top-8 + shared, I=I_s=512, int4 g64, 40 layers cycled",
+    "prefill": "prefill: T=512, d=2048, 256 experts top-8 + shared, I=I_s=512, int4 g64, 4 layers cycled",
+    "long": "long: T=4096 as 4 chunks of 1024 (one layer each), Zipf logit bias, d=2048, 256 experts top-8 + shared, I=512",
+    "diffusion": "diffusion: T=256 canvas x 30 layers, d=2048, 128 experts top-8, I=768, no shared expert",
+}
+# layers held on the GPU and calls per step
+PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "diffusion": (30, 30)}
+DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gateup_gemm", "long": "gateup_gemm",
+            "diffusion": "gateup_gemm"}
+STAGE_SOURCE = {"router_decode": "route.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
+                "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
+                "gemv_down_combine": "gemv.hip", "gateup_gemm": "gemm.hip",
+                "down_gemm": "gemm.hip", "combine": "gemm.hip"}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bf16_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def to_layer(L: dict, k: int, dev) -> moe.Layer:
+    def proj(p):
+        return moe.QProj(torch.from_numpy(p["codes"]).to(dev), bf16_dev(p["scales"], dev), bf16_dev(p["biases"], dev))
+
+    def ffn(f):
+        return None if f is None else moe.QuantFFN(proj(f["gate"]), proj(f["up"]), proj(f["down"]))
+
+    wr = torch.from_numpy(L["w_router"]).to(dev)
+    bias = None if L["logit_bias"] is None else torch.from_numpy(L["logit_bias"]).to(dev)
+    return moe.Layer(wr, ffn(L["routed"]), ffn(L["shared"]), k, bias)
+
+
+def f32_of_bits(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------------- algorithmic work per launch
+def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
+    """(bytes, flops) the method must move / do in one launch of a stage, from the routing of that
+    call. Weight bytes count only experts with at least one row; activations are counted once."""
+    d, E, k, I, Is, T = w.d, w.E, w.k, w.I, w.Is, w.chunk
+    P = T * k
+    act = int((counts > 0).sum())
+    per_w = lambda out, inn: out * inn // 2 + 2 * 2 * out * inn // 64  # noqa: E731  codes + scales + biases
+    if name == "router_decode":  # router partials + the shared expert's gate/up rows
+        return 4 * d * E + 2 * T * d + 4 * (d // 64) * E + (2 * per_w(Is, d) + 2 * Is if Is else 0), \
+            2 * T * d * E + 4 * d * Is
+    if name == "router_prefill":
+        return 4 * d * E + 2 * T * d + 8 * P, 2 * T * d * E
+    if name == "decode_topk":
+        return 4 * (d // 64) * E + 8 * k, 0
+    if name == "gemv_gateup_topk":  # routed slots only; reads the router partials
+        return 2 * k * per_w(I, d) + 2 * d + 2 * k * I + 4 * (d // 64) * E, 4 * d * k * I
+    if name == "route_meta":
+        return 4 * P * 3 + 4 * (2 * E + 1), 0
+    if name == "gemv_gateup":
+        return 2 * (k * per_w(I, d) + (per_w(Is, d) if Is else 0)) + 2 * d + 2 * (k * I + Is), 4 * d * (k * I + Is)
+    if name == "gemv_down_combine":
+        return (k * per_w(d, I) + (per_w(d, Is) if Is else 0)) + 2 * (k * I + Is) + 2 * d, 2 * d * (k * I + Is)
+    if name == "gateup_gemm":
+        wb = 2 * (act * per_w(I, d) + (per_w(Is, d) if Is else 0))
+        return wb + 2 * T * d + 2 * (P * I + T * Is), 4 * d * (P * I + T * Is)
+    if name == "down_gemm":
+        wb = act * per_w(d, I) + (per_w(d, Is) if Is else 0)
+        return wb + 2 * (P * I + T * Is) + 4 * (P + (T if Is else 0)) * d, 2 * d * (P * I + T * Is)
+    if name == "combine":
+        return 4 * (P + (T if Is else 0)) * d + 2 * T * d + 8 * P, 2 * P * d
+    raise KeyError(name)
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "bit_moe_expert_amd", "csrc", STAGE_SOURCE[name])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, kernel: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when absent or
+    when the kernel's source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m_sha = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+# ------------------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(w: gen.Workload, host_layers, seconds: float):
+    from oracle import oracle
+    n_calls, tokens, t0 = 0, 0, time.perf_counter()
+    i = 0
+    while True:
+        L, x = host_layers[i % len(host_layers)]
+        oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])
+        n_calls += 1
+        tokens += x.shape[0]
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": tokens / el, "unit": "MoE-layer tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_calls} layer calls of the same workload ({tokens} layer-tokens, first "
+                      f"{len(host_layers)} layers cycled), {el:.1f} s"}
+
+
+# ------------------------------------------------------------------------- main
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=sorted(PLAN))
+    ap.add_argument("--stage-reps", type=int, default=200, help="timed launches per stage")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the sharding design is described "
+              "in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    w = gen.WORKLOADS[args.workload]
+    n_layers, calls = PLAN[args.workload]
+    T = w.chunk
+
+    # ---- inputs (seeded, synthetic), resident in HBM before timing
+    t0 = time.perf_counter()
+    layers, xs, host_keep = [], [], []
+    for li in range(n_layers):
+        L = gen.layer(w, li)
+        x = gen.tokens(w, li, li if w.calls > 1 else 0)
+        layers.append(to_layer(L, w.k, dev))
+        xs.append(bf16_dev(x, dev))
+        if li < 4:
+            host_keep.append((L, x))
+        del L
+    ys = [torch.empty_like(x) for x in xs]
+    wss = [lay.workspace(T) for lay in layers]
+    torch.cuda.synchronize()
+    log(f"{n_layers} layers resident on {torch.cuda.get_device_name(dev)} in {time.perf_counter() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated(dev) / 1e9:.2f} GB)")
+    order = [(i % n_layers) for i in range(calls)]
+
+    # ---- eager pass + parity gate against the oracle (fail-closed)
+    for c, li in enumerate(order):
+        layers[li].forward(xs[li], wss[li], ys[li])
+    torch.cuda.synchronize()
+    eager = [ys[li].clone() for li in range(n_layers)]
+    from oracle import oracle
+    worst = 0.0
+    for li in range(min(2, n_layers)):
+        L, x = host_keep[li]
+        if T <= 512:
+            ref = oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])["y"]
+            got = bits_of(eager[li])
+        else:
+            sel = np.linspace(0, T - 1, 8).astype(np.int32)
+            ref = oracle.forward_tokens(x, L["w_router"], L["routed"], L["shared"], w.k, sel, L["logit_bias"])["y"]
+            got = bits_of(eager[li])[sel]
+        r, g = f32_of_bits(ref), f32_of_bits(got)
+        tol = 1e-2 * np.abs(r).max() + 1e-3
+        err = float(np.abs(g - r).max())
+        worst = max(worst, err / tol)
+        if not err <= tol:
+            log(f"PARITY FAILED on layer {li}: max err {err} > {tol}; no throughput reported")
+            return 1
+    log(f"parity vs oracle ok (worst error {worst:.3f} of the allowance)")
+
+    # ---- HIP graph of one step
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        for li in order:  # warm the capture stream once eagerly
+            layers[li].forward(xs[li], wss[li], ys[li])
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for li in order:
+            layers[li].forward(xs[li], wss[li], ys[li])
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    for li in range(n_layers):  # replays must reproduce the eager results
+        if not torch.equal(ys[li].view(torch.int16), eager[li].view(torch.int16)):
+            log(f"graph replay differs from eager on layer {li}; no throughput reported")
+            return 1
+    tokens_per_step = calls * T
+    value = tokens_per_step / (ms_step / 1e3)
+    log(f"step {ms_step * 1e3:.1f} us for {calls} layer calls -> {value:,.0f} MoE-layer tokens/s")
+
+    # ---- per-kernel durations: each stage alone, captured as a HIP graph of back-to-back launches
+    # that cycle the layers (so weights stream from HBM), timed with events on the launch stream
+    names = layers[0].stages(T)
+    counts = []
+    for li in range(n_layers):
+        r = moe.route(xs[li], layers[li].w_router, w.k, w.I, w.Is, layers[li].logit_bias)
+        counts.append(r["counts"].cpu().numpy())
+    per_graph = n_layers * max(1, 40 // n_layers)
+    launch_layers = [i % n_layers for i in range(per_graph)]
+    reps = max(1, args.stage_reps // per_graph)
+    stages = {}
+    for s, name in enumerate(names):
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            for li in launch_layers:
+                layers[li].launch_stage(s, xs[li], ys[li], wss[li])
+        gs.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            gs.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * per_graph)
+        wb = float(np.mean([stage_work(w, name, counts[li])[0] for li in launch_layers]))
+        wf = float(np.mean([stage_work(w, name, counts[li])[1] for li in launch_layers]))
+        stages[name] = {"us": round(us, 3), "bytes": int(wb), "flops": int(wf),
+                        "GBps": round(wb / us / 1e3, 1), "TFLOPs": round(wf / us / 1e6, 2)}
+        log(f"  {name:18s} {us:8.2f} us  {wb / 1e6:9.3f} MB  {wb / us / 1e3:8.1f} GB/s  {wf / us / 1e6:7.2f} TFLOP/s")
+        del gs
+    for li in range(n_layers):  # the stage loop leaves every layer's outputs as the eager pass did
+        if not torch.equal(ys[li].view(torch.int16), eager[li].view(torch.int16)):
+            log(f"stage launches changed layer {li}'s output")
+            return 1
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- roofline of the dominant kernel
+    dom = DOMINANT[args.workload]
+    st = stages[dom]
+    bound = "hbm"
+    if args.workload == "long":
+        bound = "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": st["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(st["GBps"] / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": st["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(st["TFLOPs"] / MFMA_BF16_PEAK_TFS, 4)}
+    roof["kernel"] = dom
+    roof["bytes_per_launch"] = st["bytes"]
+    roof["flops_per_launch"] = st["flops"]
+    roof["avg_us"] = st["us"]
+    roof["traffic"] = traffic_from_profiles(args.workload, dom)
+
+    out = {
+        "metric": "MoE-layer tokens/s", "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded generator)",
+        "config": {"workload": DESCR[args.workload], "tokens_per_call": T, "layer_calls_per_step": calls,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "stages": stages,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, host_keep, args.cpu_seconds)
+        log(f"cpu oracle: {out['cpu_baseline']['value']:.2f} tokens/s on {out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

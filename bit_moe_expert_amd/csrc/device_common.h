@@ -106,13 +106,14 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One wave: top-k of logits lg[0..E) (E <= 1024, k <= 16) by (logit desc, index asc), then the
-// softmax over the chosen logits. Lane j < k writes slot j. Must be called by a whole wave.
-__device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
+// One wave: top-k of logits lg[0..E) (E <= 64 * SLOTS, k <= 16) by (logit desc, index asc),
+// then the softmax over the chosen logits. Lane j < k writes slot j. Call with a whole wave.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_softmax_n(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
   const int lane = (int)lane_id();
-  uint64_t key[16];
+  uint64_t key[SLOTS];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
+  for (int s = 0; s < SLOTS; ++s) {
     const int e = lane + 64 * s;
     key[s] = e < E ? topk_key(lg[e], e) : 0ull;
   }
@@ -121,14 +122,14 @@ __device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k,
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) best = key[s] > best ? key[s] : best;
+    for (int s = 0; s < SLOTS; ++s) best = key[s] > best ? key[s] : best;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
       const uint64_t o = shfl_xor_u64(best, m);
       best = o > best ? o : best;
     }
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
+    for (int s = 0; s < SLOTS; ++s)
       if (key[s] == best) key[s] = 0ull;
     if (lane == j) {
       my_e = topk_key_index(best);
@@ -141,6 +142,38 @@ __device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k,
   if (lane < k) {
     ids_out[lane] = my_e;
     w_out[lane] = ex / sum;
+  }
+}
+
+__device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
+  if (E <= 64)
+    wave_topk_softmax_n<1>(lg, E, k, ids_out, w_out);
+  else if (E <= 128)
+    wave_topk_softmax_n<2>(lg, E, k, ids_out, w_out);
+  else if (E <= 256)
+    wave_topk_softmax_n<4>(lg, E, k, ids_out, w_out);
+  else
+    wave_topk_softmax_n<16>(lg, E, k, ids_out, w_out);
+}
+
+// Router logits of one token from its chunk partials parts[c][e] (c = 0 .. nchunks-1): the
+// partials are added in ascending chunk order to +0, then the bias. Threads of the block take
+// experts tid, tid + blockDim.x, ...; results go to lg[e]. Every load of a thread's 32-chunk
+// batch is issued before the adds.
+__device__ __forceinline__ void sum_chunk_partials(const float* __restrict__ parts, const float* __restrict__ bias,
+                                                   int nchunks, int E, float* lg) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    float acc = 0.0f;
+    for (int cb = 0; cb < nchunks; cb += 32) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = cb + i < nchunks ? parts[(size_t)(cb + i) * E + e] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (cb + i < nchunks) acc = acc + v[i];
+    }
+    if (bias) acc = acc + bias[e];
+    lg[e] = acc;
   }
 }
 

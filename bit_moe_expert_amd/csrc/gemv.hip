@@ -12,13 +12,17 @@
 //   sum_i x_i (s q_i + b) = s * sum_i x_i (128 + q_i) + (b - 128 s) * sum_i x_i,
 // where "128 + q" is built as a bf16 value straight from the code bits (one and-or per pair)
 // and the inner sum runs on v_dot2_f32_bf16. No weight is rounded to bf16 on this path.
+//
+// Latency discipline: the kernels are a few microseconds long, so every index that is the same
+// across a wave is made scalar (readfirstlane), kernel arguments are plain pointers selected by
+// scalar conditions, and all loads of a wave are issued before its first arithmetic use.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kGvWaves = 4;     // waves per block
-constexpr int kGvRows = 2;      // h entries (each = one gate row + one up row) per wave
+constexpr int kGvWaves = 4;  // waves per block
+constexpr int kGvRows = 4;   // h entries (each = one gate row + one up row) per wave
 
 // Segment of 32 consecutive inputs as 16 re-paired bf16 dwords (magic_pair order) + their sum.
 struct Seg32 {
@@ -46,43 +50,49 @@ __device__ __forceinline__ float seg_dot(const uint4& cw, const Seg32& a) {
   return acc;
 }
 
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Stop the compiler from sinking the loads above below this point.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+struct GemvPtrs {
+  const uint8_t *gc, *uc, *dc;       // routed gate/up/down codes
+  const uint16_t *gs, *gb, *us, *ub, *ds, *db;
+  const uint8_t *sgc, *suc, *sdc;    // shared expert
+  const uint16_t *sgs, *sgb, *sus, *sub, *sds, *sdb;
+};
+
+static GemvPtrs gemv_ptrs(const Ctx& c) {
+  GemvPtrs p;
+  p.gc = c.routed.gate.codes;
+  p.gs = c.routed.gate.scales;
+  p.gb = c.routed.gate.biases;
+  p.uc = c.routed.up.codes;
+  p.us = c.routed.up.scales;
+  p.ub = c.routed.up.biases;
+  p.dc = c.routed.down.codes;
+  p.ds = c.routed.down.scales;
+  p.db = c.routed.down.biases;
+  p.sgc = c.shared.gate.codes;
+  p.sgs = c.shared.gate.scales;
+  p.sgb = c.shared.gate.biases;
+  p.suc = c.shared.up.codes;
+  p.sus = c.shared.up.scales;
+  p.sub = c.shared.up.biases;
+  p.sdc = c.shared.down.codes;
+  p.sds = c.shared.down.scales;
+  p.sdb = c.shared.down.biases;
+  return p;
+}
+
 // ---------------------------------------------------------------------------------------------
-// h[j][i] = bf16(silu(x . Wg[e_j][i]) * (x . Wu[e_j][i])) for the k routed slots (e_j =
-// topk_ids[j]) and the shared slot. One wave owns kGvRows consecutive i of one slot; lane l
-// takes the 16-byte code pieces l, l+64, ... of each of its rows.
-__global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int k, int I, int Is,
-                                                               const uint16_t* __restrict__ x,
-                                                               const int32_t* __restrict__ ids, moe_ffn_q4 routed,
-                                                               moe_ffn_q4 shared, uint16_t* __restrict__ h,
-                                                               uint16_t* __restrict__ hs) {
-  extern __shared__ uint32_t s_x[];  // x as d/2 dwords
+// One wave computes h[i0 .. i0 + kGvRows) = bf16(silu(x . Wg[row]) * (x . Wu[row])) for the
+// weight rows row0 .. row0 + kGvRows of one expert's gate and up matrices; lane l takes the
+// 16-byte code pieces l, l+64, ... of each row.
+__device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* gc, const uint16_t* gs,
+                                            const uint16_t* gb, const uint8_t* uc, const uint16_t* us,
+                                            const uint16_t* ub, const uint16_t* __restrict__ x, uint16_t* hout) {
   const int lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < d / 2; i += blockDim.x) s_x[i] = reinterpret_cast<const uint32_t*>(x)[i];
-  __syncthreads();
-  const int wave_g = blockIdx.x * kGvWaves + (threadIdx.x >> 6);
-  const int r0 = wave_g * kGvRows;
-  const int total = k * I + Is;
-  if (r0 >= total) return;
-  int Ie, mat, i0;
-  moe_q4 G, U;
-  uint16_t* hout;
-  if (r0 < k * I) {
-    const int j = r0 / I;
-    i0 = r0 - j * I;
-    Ie = I;
-    mat = ids[j];
-    if ((unsigned)mat >= (unsigned)E) mat = 0;  // keeps a corrupt routing from reading out of bounds
-    G = routed.gate;
-    U = routed.up;
-    hout = h + (size_t)j * I + i0;
-  } else {
-    i0 = r0 - k * I;
-    Ie = Is;
-    mat = 0;
-    G = shared.gate;
-    U = shared.up;
-    hout = hs + i0;
-  }
   const int nseg = d / 32;
   const size_t cstride = (size_t)d / 2, sstride = (size_t)d / kGroup;
   float acc[2 * kGvRows];
@@ -93,120 +103,300 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
     uint16_t sr[2 * kGvRows], br[2 * kGvRows];
 #pragma unroll
     for (int r = 0; r < 2 * kGvRows; ++r) {
-      const moe_q4& Q = r < kGvRows ? G : U;
-      const size_t row = (size_t)mat * Ie + i0 + (r % kGvRows);
-      cw[r] = *reinterpret_cast<const uint4*>(Q.codes + row * cstride + (size_t)seg * 16);
-      sr[r] = Q.scales[row * sstride + seg / 2];
-      br[r] = Q.biases[row * sstride + seg / 2];
+      const size_t row = row0 + (r % kGvRows);
+      const uint8_t* cp = r < kGvRows ? gc : uc;
+      cw[r] = *reinterpret_cast<const uint4*>(cp + row * cstride + (size_t)seg * 16);
     }
+#pragma unroll
+    for (int r = 0; r < 2 * kGvRows; ++r) {
+      const size_t row = row0 + (r % kGvRows);
+      sr[r] = (r < kGvRows ? gs : us)[row * sstride + seg / 2];
+      br[r] = (r < kGvRows ? gb : ub)[row * sstride + seg / 2];
+    }
+    uint32_t xv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 t = reinterpret_cast<const uint4*>(x + (size_t)seg * 32)[q];
+      xv[4 * q] = t.x;
+      xv[4 * q + 1] = t.y;
+      xv[4 * q + 2] = t.z;
+      xv[4 * q + 3] = t.w;
+    }
+    issue_fence();
     Seg32 a;
-    make_seg(s_x + seg * 16, a);
+    make_seg(xv, a);
 #pragma unroll
     for (int r = 0; r < 2 * kGvRows; ++r) {
       const float s = bf16_to_f32(sr[r]), b = bf16_to_f32(br[r]);
-      const float p = seg_dot(cw[r], a);
-      acc[r] = fmaf(s, p, acc[r]);
+      const float pd = seg_dot(cw[r], a);
+      acc[r] = fmaf(s, pd, acc[r]);
       acc[r] = fmaf(fmaf(-128.0f, s, b), a.sum, acc[r]);
     }
   }
 #pragma unroll
   for (int r = 0; r < 2 * kGvRows; ++r) acc[r] = wave_sum(acc[r]);
-  if (lane == 0) {
-    uint32_t packed = pack_bf16x2(silu_mul(acc[0], acc[kGvRows]), silu_mul(acc[1], acc[kGvRows + 1]));
-    *reinterpret_cast<uint32_t*>(hout) = packed;
+  if (lane < kGvRows / 2) {
+    // lane q writes h entries 2q, 2q + 1 (acc is the same in every lane after the sums)
+    float hv[kGvRows];
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r) hv[r] = silu_mul(acc[r], acc[kGvRows + r]);
+    float a0 = hv[0], a1 = hv[1];
+#pragma unroll
+    for (int q = 1; q < kGvRows / 2; ++q)
+      if (lane == q) {
+        a0 = hv[2 * q];
+        a1 = hv[2 * q + 1];
+      }
+    reinterpret_cast<uint32_t*>(hout)[lane] = pack_bf16x2(a0, a1);
   }
 }
 
-hipError_t launch_gemv_gateup(const Ctx& c) {
-  const int waves = (c.k * c.I + c.Is) / kGvRows;
+// ---------------------------------------------------------------------------------------------
+// Decode router: chunk partials of the logits (see route.hip for the fixed order) and, when the
+// shared expert's weights are given, its gate/up rows in the same launch (they do not depend on
+// the routing, so they overlap the router's reads). Blocks [0, n_part) hold one (chunk, 64
+// experts) item per wave; the blocks after them hold kGvRows shared h entries per wave.
+__global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int Is, int n_part_blocks,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 const float* __restrict__ wr,
+                                                                 float* __restrict__ parts, GemvPtrs p,
+                                                                 uint16_t* __restrict__ hs) {
+  const int wave = uniform(threadIdx.x >> 6);
+  if ((int)blockIdx.x < n_part_blocks) {
+    const int nchunks = d / kGroup;
+    const int item = uniform(blockIdx.x * kGvWaves + wave);
+    if (item >= nchunks * ((E + 63) / 64)) return;
+    const int c = item % nchunks;
+    const int e = (item / nchunks) * 64 + (threadIdx.x & 63);
+    if (e >= E) return;
+    const float* wp = wr + (size_t)c * kGroup * E + e;
+    const uint16_t* xp = x + c * kGroup;
+    float v[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) part = fmaf(bf16_to_f32(xp[i]), v[i], part);
+    parts[(size_t)c * E + e] = part;
+    return;
+  }
+  const int i0 = uniform(((blockIdx.x - n_part_blocks) * kGvWaves + wave) * kGvRows);
+  if (i0 >= Is) return;
+  gateup_wave(d, (size_t)i0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x, hs + i0);
+}
+
+hipError_t launch_router_decode(const Ctx& c) {
+  const bool with_shared = c.Is > 0 && c.shared.gate.codes != nullptr;
+  const int items = (c.d / kGroup) * ((c.E + 63) / 64);
+  const int n_part = (items + kGvWaves - 1) / kGvWaves;
+  const int n_shared = with_shared ? (c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
+  hipLaunchKernelGGL(k_router_decode, dim3(n_part + n_shared), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E,
+                     with_shared ? c.Is : 0, n_part, c.x, c.w_router, c.router_parts, gemv_ptrs(c), c.hs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// h[j][i] for the k routed slots (e_j = topk_ids[j]) and, if include_shared, the shared slot.
+// FUSED_TOPK: every block first sums the router's chunk partials (in chunk order) and takes the
+// top-k itself, so no kernel boundary or atomic sits between the router and the experts' reads;
+// all blocks reach bit-identical choices, and block 0 publishes them for the down kernel.
+template <bool FUSED_TOPK>
+__global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int k, int I, int Is, int include_shared,
+                                                               const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ parts,
+                                                               const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                                               float* __restrict__ wts, GemvPtrs p,
+                                                               uint16_t* __restrict__ h, uint16_t* __restrict__ hs) {
+  __shared__ int s_ids[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
+  __shared__ float s_lg[FUSED_TOPK ? kMaxExperts : 1];
+  if (FUSED_TOPK) {
+    sum_chunk_partials(parts, bias, d / kGroup, E, s_lg);
+    __syncthreads();
+    if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, s_ids, s_w);
+    __syncthreads();
+    if (blockIdx.x == 0 && (int)threadIdx.x < k) {
+      ids[threadIdx.x] = s_ids[threadIdx.x];
+      wts[threadIdx.x] = s_w[threadIdx.x];
+    }
+  }
+  const int r0 = uniform((blockIdx.x * kGvWaves + (threadIdx.x >> 6)) * kGvRows);
+  const int total = k * I + (include_shared ? Is : 0);
+  if (r0 >= total) return;
+  const bool routed = r0 < k * I;
+  const int j = routed ? r0 / I : k;
+  const int i0 = routed ? r0 - j * I : r0 - k * I;
+  const int Ie = routed ? I : Is;
+  int mat = 0;
+  if (routed) {
+    mat = FUSED_TOPK ? s_ids[j] : ids[j];
+    if ((unsigned)mat >= (unsigned)E) mat = 0;  // a corrupt routing must not read out of bounds
+  }
+  gateup_wave(d, (size_t)mat * Ie + i0, routed ? p.gc : p.sgc, routed ? p.gs : p.sgs, routed ? p.gb : p.sgb,
+              routed ? p.uc : p.suc, routed ? p.us : p.sus, routed ? p.ub : p.sub, x,
+              routed ? h + (size_t)j * I + i0 : hs + i0);
+}
+
+hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
+  const int include_shared = fused_topk ? 0 : (c.Is > 0 ? 1 : 0);
+  const int waves = (c.k * c.I + (include_shared ? c.Is : 0)) / kGvRows;
   const int nblk = (waves + kGvWaves - 1) / kGvWaves;
-  const size_t lds = (size_t)c.d * 2;
-  hipLaunchKernelGGL(k_gemv_gateup, dim3(nblk), dim3(kGvWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is, c.x,
-                     c.r.topk_ids, c.routed, c.shared, c.h, c.hs);
+  if (fused_topk)
+    hipLaunchKernelGGL(k_gemv_gateup<true>, dim3(nblk), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
+                       include_shared, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
+                       c.h, c.hs);
+  else
+    hipLaunchKernelGGL(k_gemv_gateup<false>, dim3(nblk), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
+                       include_shared, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
+                       c.h, c.hs);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
 // y[o] = bf16( sum_j w_j * (h_j . Wd[e_j][o]) + h_s . Wd_s[o] ). A block keeps every slot's h
-// in LDS (re-paired) with per-segment sums; a wave owns 4 outputs, 16 lanes per output, and
-// those lanes walk the (slot, 32-input segment) pieces of that output's rows. Each output is
-// reduced inside its 16 lanes, so there are no atomics.
-constexpr int kGdOut = 16;  // outputs per block (4 waves x 4)
+// in LDS (re-paired) with per-segment sums. A wave owns 4 outputs (16 lanes each) and walks the
+// slots in step: at slot j every lane takes 16-byte pieces l16, l16 + 16, ... of row o of
+// expert e_j, so the slot, its expert and its weight are wave-uniform. Slots are taken in
+// batches of kGdBatch whose loads are all in flight together. Each output is reduced inside
+// its 16 lanes: no atomics.
+constexpr int kGdOut = 16;   // outputs per block (4 waves x 4)
+constexpr int kGdBatch = 9;  // slots per batch (k = 8 routed + the shared expert in one batch)
 
+template <int PIECES>  // 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
 __global__ __launch_bounds__(256) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
                                                            const int32_t* __restrict__ ids,
-                                                           const float* __restrict__ wts, moe_ffn_q4 routed,
-                                                           moe_ffn_q4 shared, const uint16_t* __restrict__ h,
+                                                           const float* __restrict__ wts, GemvPtrs p,
+                                                           const uint16_t* __restrict__ h,
                                                            const uint16_t* __restrict__ hs, uint16_t* __restrict__ y) {
-  extern __shared__ uint32_t s_h[];  // nseg_total * 16 dwords of re-paired h, then nseg_total sums
+  extern __shared__ uint32_t s_h[];  // nseg * 16 dwords of re-paired h, then nseg sums
   const int S = I / 32, Ss = Is / 32;
+  const int nslot = k + (Is > 0 ? 1 : 0);
   const int nseg = k * S + Ss;
   float* s_sum = reinterpret_cast<float*>(s_h + (size_t)nseg * 16);
-  for (int g = threadIdx.x; g < nseg; g += blockDim.x) {
-    const uint32_t* src = g < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)g * 16
-                                    : reinterpret_cast<const uint32_t*>(hs) + (size_t)(g - k * S) * 16;
-    uint32_t v[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 t = reinterpret_cast<const uint4*>(src)[q];
-      v[4 * q] = t.x;
-      v[4 * q + 1] = t.y;
-      v[4 * q + 2] = t.z;
-      v[4 * q + 3] = t.w;
-    }
-    Seg32 a;
-    make_seg(v, a);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) s_h[(size_t)g * 16 + q] = a.p[q];
-    s_sum[g] = a.sum;
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, l16 = lane & 15;
   const int o = blockIdx.x * kGdOut + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  const bool ovalid = o < d;
+  const int orow = ovalid ? o : 0;
+  // every routed slot's expert and weight with one load per wave; slots read them by lane
+  const int lj = lane < k ? lane : 0;
+  const int id_lane = ids[lj];
+  const float w_lane = wts[lj];
   float acc = 0.0f;
-  if (o < d) {
-    for (int tau = l16; tau < nseg; tau += 16) {
-      int mat, seg, Ie;
-      moe_q4 D;
-      float wj;
-      if (tau < k * S) {
-        const int j = tau / S;
-        seg = tau - j * S;
-        Ie = I;
-        mat = ids[j];
-        if ((unsigned)mat >= (unsigned)E) mat = 0;
-        D = routed.down;
-        wj = wts[j];
-      } else {
-        seg = tau - k * S;
-        Ie = Is;
-        mat = 0;
-        D = shared.down;
-        wj = 1.0f;
-      }
-      const size_t row = (size_t)mat * d + o;
-      const uint4 cw = *reinterpret_cast<const uint4*>(D.codes + row * (size_t)(Ie / 2) + (size_t)seg * 16);
-      const float s = bf16_to_f32(D.scales[row * (size_t)(Ie / kGroup) + seg / 2]);
-      const float b = bf16_to_f32(D.biases[row * (size_t)(Ie / kGroup) + seg / 2]);
-      Seg32 a;
+  for (int j0 = 0; j0 < nslot; j0 += kGdBatch) {
+    // 1. this thread's h segment for the LDS staging (first batch only; clamped, never out of bounds)
+    const int g0 = threadIdx.x;
+    const bool stage = (j0 == 0) && g0 < nseg;
+    const int gs0 = stage ? g0 : 0;
+    const uint32_t* src0 = gs0 < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)gs0 * 16
+                                       : reinterpret_cast<const uint32_t*>(hs) + (size_t)(gs0 - k * S) * 16;
+    uint32_t hv[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) a.p[q] = s_h[(size_t)tau * 16 + q];
-      a.sum = s_sum[tau];
-      const float p = seg_dot(cw, a);
-      acc = fmaf(wj, fmaf(s, p, fmaf(-128.0f, s, b) * a.sum), acc);
+    for (int q = 0; q < 4; ++q) {
+      const uint4 t = reinterpret_cast<const uint4*>(src0)[q];
+      hv[4 * q] = t.x;
+      hv[4 * q + 1] = t.y;
+      hv[4 * q + 2] = t.z;
+      hv[4 * q + 3] = t.w;
+    }
+    // 2. the batch's code pieces, scales and biases: every load unconditional, addresses clamped
+    uint4 cw[kGdBatch * PIECES];
+    uint32_t sb[kGdBatch * PIECES];  // scale | bias << 16
+    float wj[kGdBatch];
+#pragma unroll
+    for (int b = 0; b < kGdBatch; ++b) {
+      const int jj = j0 + b;  // wave-uniform
+      const bool valid = jj < nslot;
+      const bool sh = valid && jj >= k;
+      const int Ie = sh ? Is : I;
+      const int jl = (valid && !sh) ? jj : 0;
+      int mat = __builtin_amdgcn_readlane(id_lane, jl);
+      if (!valid || sh || (unsigned)mat >= (unsigned)E) mat = 0;
+      const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), jl));
+      wj[b] = !valid ? 0.0f : (sh ? 1.0f : wr);
+      const uint8_t* dc = sh ? p.sdc : p.dc;
+      const uint16_t* ds = sh ? p.sds : p.ds;
+      const uint16_t* db = sh ? p.sdb : p.db;
+      const size_t row = (size_t)mat * d + orow;
+#pragma unroll
+      for (int q = 0; q < PIECES; ++q) {
+        int seg = l16 + 16 * q;
+        seg = seg < Ie / 32 ? seg : 0;
+        cw[b * PIECES + q] = *reinterpret_cast<const uint4*>(dc + row * (size_t)(Ie / 2) + (size_t)seg * 16);
+        sb[b * PIECES + q] = (uint32_t)ds[row * (size_t)(Ie / kGroup) + seg / 2] |
+                             ((uint32_t)db[row * (size_t)(Ie / kGroup) + seg / 2] << 16);
+      }
+    }
+    issue_fence();
+    // 3. stage h into LDS (first batch only)
+    if (j0 == 0) {
+      for (int g = g0; g < nseg; g += blockDim.x) {
+        if (g != g0) {
+          const uint32_t* src = g < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)g * 16
+                                          : reinterpret_cast<const uint32_t*>(hs) + (size_t)(g - k * S) * 16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 t = reinterpret_cast<const uint4*>(src)[q];
+            hv[4 * q] = t.x;
+            hv[4 * q + 1] = t.y;
+            hv[4 * q + 2] = t.z;
+            hv[4 * q + 3] = t.w;
+          }
+        }
+        Seg32 a;
+        make_seg(hv, a);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s_h[(size_t)g * 16 + q] = a.p[q];
+        s_sum[g] = a.sum;
+      }
+      __syncthreads();
+    }
+    // 4. arithmetic
+#pragma unroll
+    for (int b = 0; b < kGdBatch; ++b) {
+      const int jj = j0 + b;
+      const bool valid = jj < nslot;
+      const bool sh = valid && jj >= k;
+      const int Sj = sh ? Ss : S;
+      const int gbase = sh ? k * S : (valid ? jj * S : 0);
+#pragma unroll
+      for (int q = 0; q < PIECES; ++q) {
+        const int seg = l16 + 16 * q;
+        const bool use = valid && seg < Sj;
+        const int gi = use ? gbase + seg : 0;
+        Seg32 a;
+        const uint4* hp = reinterpret_cast<const uint4*>(s_h + (size_t)gi * 16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 v = hp[t];
+          a.p[4 * t] = v.x;
+          a.p[4 * t + 1] = v.y;
+          a.p[4 * t + 2] = v.z;
+          a.p[4 * t + 3] = v.w;
+        }
+        a.sum = s_sum[gi];
+        const uint32_t w2 = sb[b * PIECES + q];
+        const float s = bf16lo(w2), bb = bf16hi(w2);
+        const float pd = seg_dot(cw[b * PIECES + q], a);
+        const float c = fmaf(s, pd, fmaf(-128.0f, s, bb) * a.sum);
+        acc = fmaf(use ? wj[b] : 0.0f, c, acc);
+      }
     }
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (o < d && l16 == 0) y[o] = f32_to_bf16(acc);
+  if (ovalid && l16 == 0) y[o] = f32_to_bf16(acc);
 }
 
 hipError_t launch_gemv_down_combine(const Ctx& c) {
   const int nseg = c.k * (c.I / 32) + c.Is / 32;
   const size_t lds = (size_t)nseg * 16 * 4 + (size_t)nseg * 4;
   const int nblk = (c.d + kGdOut - 1) / kGdOut;
-  hipLaunchKernelGGL(k_gemv_down_combine, dim3(nblk), dim3(256), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                     c.r.topk_ids, c.r.topk_w, c.routed, c.shared, c.h, c.hs, c.y);
+  if (c.I <= 512 && c.Is <= 512)
+    hipLaunchKernelGGL(k_gemv_down_combine<1>, dim3(nblk), dim3(256), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
+                       c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
+  else
+    hipLaunchKernelGGL(k_gemv_down_combine<2>, dim3(nblk), dim3(256), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
+                       c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
   return hipGetLastError();
 }
 

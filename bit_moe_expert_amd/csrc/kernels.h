@@ -19,7 +19,6 @@ struct Ctx {
   moe_ffn_q4 shared;  // all-null when Is == 0
   moe_routing r;      // routing arrays (caller's or carved from the workspace)
   float* router_parts;    // [d/64][E] decode router chunk partials
-  unsigned* counter;      // decode router arrival counter (zero between calls)
   uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1)
   uint16_t* hs;           // [T][Is] bf16
   float* y_rows;          // [P + T][d] fp32, grouped order, shared rows last
@@ -27,10 +26,14 @@ struct Ctx {
   hipStream_t stream;
 };
 
+// decode router chunk partials (+ the shared expert's gate/up rows when its weights are set)
 hipError_t launch_router_decode(const Ctx& c);
+hipError_t launch_decode_topk(const Ctx& c);
 hipError_t launch_router_prefill(const Ctx& c);
 hipError_t launch_route_meta(const Ctx& c);
-hipError_t launch_gemv_gateup(const Ctx& c);
+// fused_topk: take the top-k from the router partials in every block (routed slots only);
+// otherwise read topk_ids and also compute the shared slot
+hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk);
 hipError_t launch_gemv_down_combine(const Ctx& c);
 hipError_t launch_gateup_gemm(const Ctx& c);
 hipError_t launch_down_gemm(const Ctx& c);
@@ -39,5 +42,7 @@ hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* o
 
 // The GEMV decode path keeps all selected experts' h in LDS: (k*I + Is) bf16 values.
 constexpr int kGemvMaxH = 28672;
+// ... and its down kernel keeps two 16-lane rounds of 32-input pieces per row in registers.
+constexpr int kGemvMaxFF = 1024;
 
 }  // namespace moe

@@ -54,19 +54,22 @@ int32_t max_tiles_of(const moe_dims& dm, int32_t T) {
 }
 
 bool gemv_path(const moe_dims& dm, int32_t T) {
-  return T == 1 && dm.top_k * dm.d_ff + dm.d_ff_shared <= kGemvMaxH;
+  return T == 1 && dm.top_k * dm.d_ff + dm.d_ff_shared <= kGemvMaxH && dm.d_ff <= kGemvMaxFF &&
+         dm.d_ff_shared <= kGemvMaxFF;
+}
+
+bool gemv_path_ctx(const Ctx& c) {
+  return c.T == 1 && c.k * c.I + c.Is <= kGemvMaxH && c.I <= kGemvMaxFF && c.Is <= kGemvMaxFF;
 }
 
 struct Layout {
-  size_t counter, parts, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, h, hs, y_rows, total;
+  size_t parts, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, h, hs, y_rows, total;
 };
 
 Layout layout_of(const moe_dims& dm, int32_t T) {
   Layout L;
   const size_t P = (size_t)T * dm.top_k, E = dm.n_experts, d = dm.d_model;
   size_t o = 0;
-  L.counter = o;
-  o += up(256);
   L.parts = o;
   o += up(d / 64 * E * 4);
   L.ids = o;
@@ -130,32 +133,56 @@ int check_ws(const moe_dims& dm, int32_t T, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
-enum Stage { kRouterDecode, kRouterPrefill, kMeta, kGemvGateup, kGemvDown, kGemmGateup, kGemmDown, kCombine };
-const char* kStageNames[] = {"router_decode", "router_prefill", "route_meta", "gemv_gateup",
-                             "gemv_down_combine", "gateup_gemm", "down_gemm", "combine"};
+enum Stage {
+  kRouterDecode,      // chunk partials of the logits (+ shared expert gate/up when its weights are set)
+  kDecodeTopk,        // partials -> top-k (moe_route at T == 1)
+  kRouterPrefill,     // logits + top-k for T >= 2
+  kMeta,              // histogram, scan, scatter, block map
+  kGemvGateupTopk,    // decode gate/up of the routed slots, top-k fused in
+  kGemvGateup,        // decode gate/up from given routing, shared slot included
+  kGemvDown,          // decode down + weighted combine + shared
+  kGemmGateup,
+  kGemmDown,
+  kCombine
+};
+const char* kStageNames[] = {"router_decode", "decode_topk", "router_prefill", "route_meta", "gemv_gateup_topk",
+                             "gemv_gateup", "gemv_down_combine", "gateup_gemm", "down_gemm", "combine"};
 
 int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
   int n = 0;
-  out[n++] = T == 1 ? kRouterDecode : kRouterPrefill;
   if (gemv_path(dm, T)) {
-    out[n++] = kGemvGateup;
+    out[n++] = kRouterDecode;
+    out[n++] = kGemvGateupTopk;
     out[n++] = kGemvDown;
-  } else {
-    out[n++] = kMeta;
-    out[n++] = kGemmGateup;
-    out[n++] = kGemmDown;
-    out[n++] = kCombine;
+    return n;
   }
+  if (T == 1) {
+    out[n++] = kRouterDecode;
+    out[n++] = kDecodeTopk;
+  } else {
+    out[n++] = kRouterPrefill;
+  }
+  out[n++] = kMeta;
+  out[n++] = kGemmGateup;
+  out[n++] = kGemmDown;
+  out[n++] = kCombine;
   return n;
 }
 
-int run_stage(Stage s, const Ctx& c) {
+int run_stage(Stage s, const Ctx& c0, bool layer_call) {
+  Ctx c = c0;
   hipError_t e = hipSuccess;
   switch (s) {
-    case kRouterDecode: e = launch_router_decode(c); break;
+    case kRouterDecode:
+      // the shared expert's gate/up rides along only where the GEMV path consumes it
+      if (!(layer_call && gemv_path_ctx(c))) memset(&c.shared, 0, sizeof(c.shared));
+      e = launch_router_decode(c);
+      break;
+    case kDecodeTopk: e = launch_decode_topk(c); break;
     case kRouterPrefill: e = launch_router_prefill(c); break;
     case kMeta: e = launch_route_meta(c); break;
-    case kGemvGateup: e = launch_gemv_gateup(c); break;
+    case kGemvGateupTopk: e = launch_gemv_gateup(c, true); break;
+    case kGemvGateup: e = launch_gemv_gateup(c, false); break;
     case kGemvDown: e = launch_gemv_down_combine(c); break;
     case kGemmGateup: e = launch_gateup_gemm(c); break;
     case kGemmDown: e = launch_down_gemm(c); break;
@@ -176,7 +203,6 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.T = T;
   c.P = T * dm.top_k;
   c.max_tiles = max_tiles_of(dm, T);
-  c.counter = reinterpret_cast<unsigned*>(b + L.counter);
   c.router_parts = reinterpret_cast<float*>(b + L.parts);
   c.h = reinterpret_cast<uint16_t*>(b + L.h);
   c.hs = reinterpret_cast<uint16_t*>(b + L.hs);
@@ -262,8 +288,13 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
   c.w_router = w_router;
   c.logit_bias = logit_bias;
   c.r = *out;
-  if (int rc = run_stage(T == 1 ? kRouterDecode : kRouterPrefill, c)) return rc;
-  return run_stage(kMeta, c);
+  if (T == 1) {
+    if (int rc = run_stage(kRouterDecode, c, false)) return rc;
+    if (int rc = run_stage(kDecodeTopk, c, false)) return rc;
+  } else if (int rc = run_stage(kRouterPrefill, c, false)) {
+    return rc;
+  }
+  return run_stage(kMeta, c, false);
 }
 
 int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_routing* routing,
@@ -278,12 +309,12 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe
   layer_ctx(c, dims, T, x, nullptr, nullptr, routed, shared, y, ws, stream);
   c.r = *routing;
   if (gemv_path(*dims, T)) {
-    if (int rc = run_stage(kGemvGateup, c)) return rc;
-    return run_stage(kGemvDown, c);
+    if (int rc = run_stage(kGemvGateup, c, false)) return rc;
+    return run_stage(kGemvDown, c, false);
   }
-  if (int rc = run_stage(kGemmGateup, c)) return rc;
-  if (int rc = run_stage(kGemmDown, c)) return rc;
-  return run_stage(kCombine, c);
+  if (int rc = run_stage(kGemmGateup, c, false)) return rc;
+  if (int rc = run_stage(kGemmDown, c, false)) return rc;
+  return run_stage(kCombine, c, false);
 }
 
 int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
@@ -297,7 +328,7 @@ int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const 
   Stage st[8];
   const int n = layer_stages(*dims, T, st);
   for (int i = 0; i < n; ++i)
-    if (int rc = run_stage(st[i], c)) return rc;
+    if (int rc = run_stage(st[i], c, true)) return rc;
   return MOE_OK;
 }
 
@@ -326,7 +357,7 @@ int moe_launch_stage(int32_t stage, const moe_dims* dims, int32_t T, const uint1
   if (stage < 0 || stage >= n) return fail(MOE_EINVAL, "stage %d out of range [0, %d)", stage, n);
   Ctx c;
   layer_ctx(c, dims, T, x, w_router, logit_bias, routed, shared, y, ws, stream);
-  return run_stage(st[stage], c);
+  return run_stage(st[stage], c, true);
 }
 
 int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream) {

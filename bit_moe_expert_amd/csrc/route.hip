@@ -14,55 +14,20 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// Decode (T == 1): one wave per (chunk, 64 experts) so the 4*d*E bytes of router weights are
-// read by many CUs at once. The last block to arrive sums the partials in chunk order, then one
-// wave takes the top-k and the softmax. The arrival counter is reset by that block.
-__global__ __launch_bounds__(64) void k_router_decode(int d, int E, int k, const uint16_t* __restrict__ x,
-                                                      const float* __restrict__ wr, const float* __restrict__ bias,
-                                                      float* __restrict__ parts, unsigned* __restrict__ counter,
-                                                      int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int nchunks = d / kGroup;
-  const int c = blockIdx.x % nchunks;
-  const int e = (blockIdx.x / nchunks) * 64 + threadIdx.x;
-  if (e < E) {
-    const float* wp = wr + (size_t)c * kGroup * E + e;
-    const uint16_t* xp = x + c * kGroup;
-    float v[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) part = fmaf(bf16_to_f32(xp[i]), v[i], part);
-    parts[(size_t)c * E + e] = part;
-  }
-  __shared__ int s_last;
+// Decode (T == 1) top-k for moe_route: one block adds the decode router's chunk partials in
+// chunk order and takes the top-k. (moe_forward_layer fuses this step into its gate/up kernel.)
+__global__ __launch_bounds__(256) void k_decode_topk(int d, int E, int k, const float* __restrict__ parts,
+                                                     const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w) {
   __shared__ float s_lg[kMaxExperts];
-  __threadfence();
+  sum_chunk_partials(parts, bias, d / kGroup, E, s_lg);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int ee = threadIdx.x; ee < E; ee += 64) {
-    float acc = 0.0f;
-    for (int cc = 0; cc < nchunks; ++cc)
-      acc = acc + __hip_atomic_load(parts + (size_t)cc * E + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (bias) acc = acc + bias[ee];
-    s_lg[ee] = acc;
-  }
-  __syncthreads();
-  wave_topk_softmax(s_lg, E, k, ids, w);
-  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, ids, w);
 }
 
-hipError_t launch_router_decode(const Ctx& c) {
-  const int nchunks = c.d / kGroup;
-  const int nblk = nchunks * ((c.E + 63) / 64);
-  hipLaunchKernelGGL(k_router_decode, dim3(nblk), dim3(64), 0, c.stream, c.d, c.E, c.k, c.x, c.w_router,
-                     c.logit_bias, c.router_parts, c.counter, c.r.topk_ids, c.r.topk_w);
+hipError_t launch_decode_topk(const Ctx& c) {
+  hipLaunchKernelGGL(k_decode_topk, dim3(1), dim3(256), 0, c.stream, c.d, c.E, c.k, c.router_parts, c.logit_bias,
+                     c.r.topk_ids, c.r.topk_w);
   return hipGetLastError();
 }
 

@@ -153,7 +153,7 @@ def workspace_bytes(dims: Dims, T: int) -> int:
 
 
 def new_workspace(dims: Dims, T: int, device) -> torch.Tensor:
-    """Zero-filled workspace (the ABI needs its first 256 bytes zero before first use)."""
+    """Workspace of the size the library asks for (zero-filled, though the ABI does not need it)."""
     n = workspace_bytes(dims, T)
     if n == 0:
         raise MoeError(MOE_EUNSUPPORTED, "workspace_bytes")

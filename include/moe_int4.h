@@ -32,10 +32,8 @@
  *     faults surface at the caller's next synchronisation, as for any HIP launch.
  *   - Determinism. The same inputs give bit-identical outputs on every call (atomics are
  *     used only for counts and for an arrival counter, never for floating-point sums).
- *   - Workspace. `ws` is device memory of at least moe_workspace_bytes() bytes. Its first 256
- *     bytes hold an arrival counter that must be zero before the first call that uses the
- *     workspace (allocate it zero-filled); every call leaves it zero again. The rest is
- *     scratch whose contents on entry do not matter.
+ *   - Workspace. `ws` is device scratch of at least moe_workspace_bytes() bytes; its contents
+ *     on entry do not matter.
  *   - Concurrency. No global mutable state. Calls on different streams with different
  *     workspaces may overlap; calls sharing one workspace must be ordered by the caller.
  *   - T = 0 is a no-op that returns MOE_OK once the dims are valid (pointers are not checked).
@@ -156,7 +154,8 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe
                    size_t ws_bytes, void* stream);
 
 /* moe_route followed by moe_expert_ffn, with the routing arrays carved from `ws`. At T == 1
- * the block-map steps are skipped (the GEMV path does not read them). */
+ * the block-map steps are skipped (the GEMV path does not read them), the top-k is taken
+ * inside the gate/up kernel, and only topk_ids/topk_w of the carved routing are written. */
 int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
                       const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared,
                       uint16_t* y, void* ws, size_t ws_bytes, void* stream);

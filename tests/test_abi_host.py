@@ -52,13 +52,14 @@ def test_stage_lists():
     d = _dims()
     n1 = L.moe_num_stages(ctypes.byref(d), 1)
     assert [L.moe_stage_name(ctypes.byref(d), 1, s).decode() for s in range(n1)] == \
-        ["router_decode", "gemv_gateup", "gemv_down_combine"]
+        ["router_decode", "gemv_gateup_topk", "gemv_down_combine"]
     n2 = L.moe_num_stages(ctypes.byref(d), 512)
     assert [L.moe_stage_name(ctypes.byref(d), 512, s).decode() for s in range(n2)] == \
         ["router_prefill", "route_meta", "gateup_gemm", "down_gemm", "combine"]
     assert L.moe_stage_name(ctypes.byref(d), 512, 5) is None
     big = _dims(k=16, I=2048)  # too much h for the GEMV path: T = 1 runs the grouped GEMM
-    assert L.moe_num_stages(ctypes.byref(big), 1) == 5
+    assert [L.moe_stage_name(ctypes.byref(big), 1, s).decode() for s in range(L.moe_num_stages(ctypes.byref(big), 1))] \
+        == ["router_decode", "decode_topk", "route_meta", "gateup_gemm", "down_gemm", "combine"]
 
 
 class _Fake:

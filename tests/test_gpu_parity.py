@@ -164,7 +164,7 @@ def test_forward_small_shapes(T, d, E, k, I, Is):
 def test_decode_falls_back_to_grouped_gemm_when_h_is_large():
     w = _custom(1, 256, 32, 16, 2048, 0, seed=9)
     lay = layer_dev(gen.layer(w, 0), w.k)
-    assert lay.stages(1)[1] == "route_meta"
+    assert lay.stages(1)[1:3] == ["decode_topk", "route_meta"]
     _forward_check(w)
 
 
