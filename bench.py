@@ -51,6 +51,7 @@ DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gat
             "diffusion": "gateup_gemm"}
 STAGE_SOURCE = {"router_decode": "route.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
+                "topk_prefill": "route.hip",
                 "gemv_down_combine": "gemv.hip", "gateup_gemm": "gemm.hip",
                 "down_gemm": "gemm.hip", "combine": "gemm.hip"}
 
@@ -94,8 +95,10 @@ def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
     if name == "router_decode":  # router partials + the shared expert's gate/up rows
         return 4 * d * E + 2 * T * d + 4 * (d // 64) * E + (2 * per_w(Is, d) + 2 * Is if Is else 0), \
             2 * T * d * E + 4 * d * Is
-    if name == "router_prefill":
-        return 4 * d * E + 2 * T * d + 8 * P, 2 * T * d * E
+    if name == "router_prefill":  # router weights, x, logits out
+        return 4 * d * E + 2 * T * d + 4 * T * E, 2 * T * d * E
+    if name == "topk_prefill":
+        return 4 * T * E + 8 * P, 0
     if name == "decode_topk":
         return 4 * (d // 64) * E + 8 * k, 0
     if name == "gemv_gateup_topk":  # routed slots only; reads the router partials

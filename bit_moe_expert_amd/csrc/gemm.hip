@@ -67,20 +67,33 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& nb, int& e, i
 struct StepRegs {
   uint4 c0, c1;
   uint16_t s, b;
+  bool gv, av;  // group present / A chunk inside K (applied when the slot is consumed)
 };
+
+// K steps kept in flight per thread (codes, scale, bias and A chunks in registers), sized so the
+// ring stays near 100 registers: HBM latency is several K steps long.
+template <int MT>
+constexpr int ring_depth() {
+  return MT == 1 ? 4 : MT == 2 ? 4 : MT == 4 ? 2 : 1;
+}
 
 template <int MT>
 __device__ __forceinline__ void store_step(uint16_t* Bs, uint16_t* As, int wr, int wh, const StepRegs& w,
-                                          const uint4 (&areg)[MT]) {
+                                          const uint4 (&areg)[MT], const bool (&amask)[MT]) {
   uint32_t dq[32];
-  dequant_group(w.c0, w.c1, bf16_to_f32(w.s), bf16_to_f32(w.b), dq);
+  const float s = w.gv ? bf16_to_f32(w.s) : 0.0f, b = w.gv ? bf16_to_f32(w.b) : 0.0f;
+  dequant_group(w.c0, w.c1, s, b, dq);
   uint4* dst = reinterpret_cast<uint4*>(Bs + wr * kLds + wh * 64);
 #pragma unroll
   for (int q = 0; q < 8; ++q) dst[q] = make_uint4(dq[4 * q], dq[4 * q + 1], dq[4 * q + 2], dq[4 * q + 3]);
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm)
-    *reinterpret_cast<uint4*>(As + ((tid >> 4) + 16 * mm) * kLds + (tid & 15) * 8) = areg[mm];
+  for (int mm = 0; mm < MT; ++mm) {
+    const bool keep = w.av && amask[mm];
+    const uint4 v = areg[mm];
+    *reinterpret_cast<uint4*>(As + ((tid >> 4) + 16 * mm) * kLds + (tid & 15) * 8) =
+        make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -103,30 +116,35 @@ __device__ __forceinline__ void gateup_body(const GemmArgs& a, int n0, int e, in
   const uint16_t* bp = Q.biases + wrow * (size_t)(d / kGroup) + wh;
   // this thread's A chunks: row (tid >> 4) + 16 mm, inputs 8 (tid & 15) .. +7 of the step
   const uint16_t* ap[MT];
+  bool amask[MT];
 #pragma unroll
   for (int mm = 0; mm < MT; ++mm) {
     const int r = (tid >> 4) + 16 * mm;
     int tok = -1;
     if (r < rows) tok = sh ? (row0 - a.P + r) : a.sorted_token[row0 + r];
-    ap[mm] = ((unsigned)tok < (unsigned)a.T) ? a.x + (size_t)tok * d + (tid & 15) * 8 : nullptr;
+    amask[mm] = (unsigned)tok < (unsigned)a.T;
+    ap[mm] = a.x + (size_t)(amask[mm] ? tok : 0) * d;
   }
   const int S = (d + kBK - 1) / kBK;
-  StepRegs w;
-  uint4 areg[MT];
-  auto load = [&](int s) {
-    if (s * kBK + wh * 64 < d) {
-      w.c0 = *reinterpret_cast<const uint4*>(cp + s * 64);
-      w.c1 = *reinterpret_cast<const uint4*>(cp + s * 64 + 16);
-      w.s = sp[2 * s];
-      w.b = bp[2 * s];
-    } else {
-      w.c0 = w.c1 = make_uint4(0, 0, 0, 0);
-      w.s = w.b = 0;
-    }
+  constexpr int D = ring_depth<MT>();
+  StepRegs w[D];
+  uint4 areg[D][MT];
+  // Every slot load is unconditional (step index clamped, A rows of absent tokens read row 0),
+  // so the compiler can count outstanding loads exactly; padding steps and absent rows are
+  // zeroed with selects instead of branches.
+  const int kh_last = (d / 64) - 1;  // last 64-input group index
+  auto load = [&](int s, StepRegs& wd, uint4 (&ad)[MT]) {
+    const int g = min(2 * s + wh, kh_last);
+    const bool gv = 2 * s + wh <= kh_last;
+    wd.c0 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32);
+    wd.c1 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32 + 16);
+    wd.s = sp[g - wh];
+    wd.b = bp[g - wh];
+    wd.gv = gv;
+    const int ka = min(s * kBK + (tid & 15) * 8, d - 8);
+    wd.av = s * kBK + (tid & 15) * 8 < d;
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-      areg[mm] = (ap[mm] && s * kBK + (tid & 15) * 8 < d) ? *reinterpret_cast<const uint4*>(ap[mm] + s * kBK)
-                                                         : make_uint4(0, 0, 0, 0);
+    for (int mm = 0; mm < MT; ++mm) ad[mm] = *reinterpret_cast<const uint4*>(ap[mm] + ka);
   };
   f32x4_t accg[MT], accu[MT];
 #pragma unroll
@@ -134,25 +152,29 @@ __device__ __forceinline__ void gateup_body(const GemmArgs& a, int n0, int e, in
     accg[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     accu[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  load(0);
-  for (int s = 0; s < S; ++s) {
-    store_step<MT>(Bs, As, wr, wh, w, areg);
-    __syncthreads();
-    if (s + 1 < S) load(s + 1);
-    const int kofs = (lane >> 4) * 8;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const uint4 bg = *reinterpret_cast<const uint4*>(Bs + (16 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
-      const uint4 bu =
-          *reinterpret_cast<const uint4*>(Bs + (kGuCols + 16 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
+  for (int u = 0; u < D; ++u) load(u, w[u], areg[u]);
+  for (int s0 = 0; s0 < S; s0 += D) {
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) {
-        const uint4 av = *reinterpret_cast<const uint4*>(As + (16 * mm + (lane & 15)) * kLds + kk * 32 + kofs);
-        accg[mm] = mfma16x16x32(av, bg, accg[mm]);
-        accu[mm] = mfma16x16x32(av, bu, accu[mm]);
+    for (int u = 0; u < D; ++u) {
+      store_step<MT>(Bs, As, wr, wh, w[u], areg[u], amask);
+      __syncthreads();
+      load(s0 + u + D, w[u], areg[u]);
+      const int kofs = (lane >> 4) * 8;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 32; ++kk) {
+        const uint4 bg = *reinterpret_cast<const uint4*>(Bs + (16 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
+        const uint4 bu =
+            *reinterpret_cast<const uint4*>(Bs + (kGuCols + 16 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) {
+          const uint4 av = *reinterpret_cast<const uint4*>(As + (16 * mm + (lane & 15)) * kLds + kk * 32 + kofs);
+          accg[mm] = mfma16x16x32(av, bg, accg[mm]);
+          accu[mm] = mfma16x16x32(av, bu, accu[mm]);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
   const int col = n0 + 16 * wave + (lane & 15);
@@ -201,50 +223,57 @@ __device__ __forceinline__ void down_body(const GemmArgs& a, int n0, int e, int 
   const uint16_t* bp = Q.biases + wrow * (size_t)(Ie / kGroup) + wh;
   const uint16_t* hbase = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
   const uint16_t* ap[MT];
+  bool amask[MT];
 #pragma unroll
   for (int mm = 0; mm < MT; ++mm) {
     const int r = (tid >> 4) + 16 * mm;
-    ap[mm] = r < rows ? hbase + (size_t)r * Ie + (tid & 15) * 8 : nullptr;
+    amask[mm] = r < rows;
+    ap[mm] = hbase + (size_t)(amask[mm] ? r : 0) * Ie;
   }
   const int S = (Ie + kBK - 1) / kBK;
-  StepRegs w;
-  uint4 areg[MT];
-  auto load = [&](int s) {
-    if (wvalid && s * kBK + wh * 64 < Ie) {
-      w.c0 = *reinterpret_cast<const uint4*>(cp + s * 64);
-      w.c1 = *reinterpret_cast<const uint4*>(cp + s * 64 + 16);
-      w.s = sp[2 * s];
-      w.b = bp[2 * s];
-    } else {
-      w.c0 = w.c1 = make_uint4(0, 0, 0, 0);
-      w.s = w.b = 0;
-    }
+  constexpr int D = ring_depth<MT>();
+  StepRegs w[D];
+  uint4 areg[D][MT];
+  const int kh_last = (Ie / 64) - 1;
+  auto load = [&](int s, StepRegs& wd, uint4 (&ad)[MT]) {
+    const int g = min(2 * s + wh, kh_last);
+    const bool gv = wvalid && 2 * s + wh <= kh_last;
+    wd.c0 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32);
+    wd.c1 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32 + 16);
+    wd.s = sp[g - wh];
+    wd.b = bp[g - wh];
+    wd.gv = gv;
+    const int ka = min(s * kBK + (tid & 15) * 8, Ie - 8);
+    wd.av = s * kBK + (tid & 15) * 8 < Ie;
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-      areg[mm] = (ap[mm] && s * kBK + (tid & 15) * 8 < Ie) ? *reinterpret_cast<const uint4*>(ap[mm] + s * kBK)
-                                                          : make_uint4(0, 0, 0, 0);
+    for (int mm = 0; mm < MT; ++mm) ad[mm] = *reinterpret_cast<const uint4*>(ap[mm] + ka);
   };
   f32x4_t acc[MT][2];
 #pragma unroll
   for (int mm = 0; mm < MT; ++mm) acc[mm][0] = acc[mm][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  load(0);
-  for (int s = 0; s < S; ++s) {
-    store_step<MT>(Bs, As, wr, wh, w, areg);
-    __syncthreads();
-    if (s + 1 < S) load(s + 1);
-    const int kofs = (lane >> 4) * 8;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const uint4 b0 = *reinterpret_cast<const uint4*>(Bs + (32 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(Bs + (32 * wave + 16 + (lane & 15)) * kLds + kk * 32 + kofs);
+  for (int u = 0; u < D; ++u) load(u, w[u], areg[u]);
+  for (int s0 = 0; s0 < S; s0 += D) {
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) {
-        const uint4 av = *reinterpret_cast<const uint4*>(As + (16 * mm + (lane & 15)) * kLds + kk * 32 + kofs);
-        acc[mm][0] = mfma16x16x32(av, b0, acc[mm][0]);
-        acc[mm][1] = mfma16x16x32(av, b1, acc[mm][1]);
+    for (int u = 0; u < D; ++u) {
+      store_step<MT>(Bs, As, wr, wh, w[u], areg[u], amask);
+      __syncthreads();
+      load(s0 + u + D, w[u], areg[u]);
+      const int kofs = (lane >> 4) * 8;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 32; ++kk) {
+        const uint4 b0 = *reinterpret_cast<const uint4*>(Bs + (32 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
+        const uint4 b1 =
+            *reinterpret_cast<const uint4*>(Bs + (32 * wave + 16 + (lane & 15)) * kLds + kk * 32 + kofs);
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) {
+          const uint4 av = *reinterpret_cast<const uint4*>(As + (16 * mm + (lane & 15)) * kLds + kk * 32 + kofs);
+          acc[mm][0] = mfma16x16x32(av, b0, acc[mm][0]);
+          acc[mm][1] = mfma16x16x32(av, b1, acc[mm][1]);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int mm = 0; mm < MT; ++mm)

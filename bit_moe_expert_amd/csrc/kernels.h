@@ -19,6 +19,7 @@ struct Ctx {
   moe_ffn_q4 shared;  // all-null when Is == 0
   moe_routing r;      // routing arrays (caller's or carved from the workspace)
   float* router_parts;    // [d/64][E] decode router chunk partials
+  float* logits;          // [T][E] router logits (T >= 2)
   uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1)
   uint16_t* hs;           // [T][Is] bf16
   float* y_rows;          // [P + T][d] fp32, grouped order, shared rows last
@@ -29,7 +30,8 @@ struct Ctx {
 // decode router chunk partials (+ the shared expert's gate/up rows when its weights are set)
 hipError_t launch_router_decode(const Ctx& c);
 hipError_t launch_decode_topk(const Ctx& c);
-hipError_t launch_router_prefill(const Ctx& c);
+hipError_t launch_router_prefill(const Ctx& c);  // logits [T][E]
+hipError_t launch_topk_prefill(const Ctx& c);    // logits -> topk_ids, topk_w
 hipError_t launch_route_meta(const Ctx& c);
 // fused_topk: take the top-k from the router partials in every block (routed slots only);
 // otherwise read topk_ids and also compute the shared slot

@@ -63,7 +63,7 @@ bool gemv_path_ctx(const Ctx& c) {
 }
 
 struct Layout {
-  size_t parts, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, h, hs, y_rows, total;
+  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, h, hs, y_rows, total;
 };
 
 Layout layout_of(const moe_dims& dm, int32_t T) {
@@ -72,6 +72,8 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   size_t o = 0;
   L.parts = o;
   o += up(d / 64 * E * 4);
+  L.logits = o;
+  o += up((size_t)T * E * 4);
   L.ids = o;
   o += up(P * 4);
   L.w = o;
@@ -136,7 +138,8 @@ int check_ws(const moe_dims& dm, int32_t T, void* ws, size_t ws_bytes) {
 enum Stage {
   kRouterDecode,      // chunk partials of the logits (+ shared expert gate/up when its weights are set)
   kDecodeTopk,        // partials -> top-k (moe_route at T == 1)
-  kRouterPrefill,     // logits + top-k for T >= 2
+  kRouterPrefill,     // logits for T >= 2
+  kTopkPrefill,       // logits -> top-k for T >= 2
   kMeta,              // histogram, scan, scatter, block map
   kGemvGateupTopk,    // decode gate/up of the routed slots, top-k fused in
   kGemvGateup,        // decode gate/up from given routing, shared slot included
@@ -145,7 +148,7 @@ enum Stage {
   kGemmDown,
   kCombine
 };
-const char* kStageNames[] = {"router_decode", "decode_topk", "router_prefill", "route_meta", "gemv_gateup_topk",
+const char* kStageNames[] = {"router_decode", "decode_topk", "router_prefill", "topk_prefill", "route_meta", "gemv_gateup_topk",
                              "gemv_gateup", "gemv_down_combine", "gateup_gemm", "down_gemm", "combine"};
 
 int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
@@ -161,6 +164,7 @@ int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
     out[n++] = kDecodeTopk;
   } else {
     out[n++] = kRouterPrefill;
+    out[n++] = kTopkPrefill;
   }
   out[n++] = kMeta;
   out[n++] = kGemmGateup;
@@ -180,6 +184,7 @@ int run_stage(Stage s, const Ctx& c0, bool layer_call) {
       break;
     case kDecodeTopk: e = launch_decode_topk(c); break;
     case kRouterPrefill: e = launch_router_prefill(c); break;
+    case kTopkPrefill: e = launch_topk_prefill(c); break;
     case kMeta: e = launch_route_meta(c); break;
     case kGemvGateupTopk: e = launch_gemv_gateup(c, true); break;
     case kGemvGateup: e = launch_gemv_gateup(c, false); break;
@@ -204,6 +209,7 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.P = T * dm.top_k;
   c.max_tiles = max_tiles_of(dm, T);
   c.router_parts = reinterpret_cast<float*>(b + L.parts);
+  c.logits = reinterpret_cast<float*>(b + L.logits);
   c.h = reinterpret_cast<uint16_t*>(b + L.h);
   c.hs = reinterpret_cast<uint16_t*>(b + L.hs);
   c.y_rows = reinterpret_cast<float*>(b + L.y_rows);
@@ -291,8 +297,9 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
   if (T == 1) {
     if (int rc = run_stage(kRouterDecode, c, false)) return rc;
     if (int rc = run_stage(kDecodeTopk, c, false)) return rc;
-  } else if (int rc = run_stage(kRouterPrefill, c, false)) {
-    return rc;
+  } else {
+    if (int rc = run_stage(kRouterPrefill, c, false)) return rc;
+    if (int rc = run_stage(kTopkPrefill, c, false)) return rc;
   }
   return run_stage(kMeta, c, false);
 }

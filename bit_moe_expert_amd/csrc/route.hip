@@ -32,78 +32,88 @@ hipError_t launch_decode_topk(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill (T >= 2): a block owns 4 tokens and all experts. Its 16 waves each reduce one chunk
-// for 4 tokens x 256 experts (lane owns experts lane + 64q); the chunk partials meet in LDS and
-// are added in chunk order by one thread per (token, expert). Then one wave per token takes
-// the top-k and the softmax.
-constexpr int kRpTok = 4;
+// Prefill (T >= 2) logits: a block owns 8 tokens x 64 experts (lane = expert) and its 16 waves
+// split the 64-input chunks (wave w takes chunks w, w + 16, ...). A wave issues the 64 router
+// loads of its chunk before the fma chains (one per token, ascending inputs); the chunk partials
+// meet in LDS and one thread per (token, expert) adds them in chunk order, then the bias.
+constexpr int kRpTok = 8;
 constexpr int kRpWaves = 16;
+constexpr int kRpPass = kRpWaves * kGroup;  // inputs staged per pass
 
-__global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, int k, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, const uint16_t* __restrict__ x,
                                                          const float* __restrict__ wr, const float* __restrict__ bias,
-                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
-  __shared__ float s_parts[kRpWaves][kRpTok][256];          // 64 KB
-  __shared__ __attribute__((aligned(16))) float s_x[kRpWaves * kGroup][kRpTok];  // 16 KB, [input][token]
-  __shared__ float s_lg[kRpTok][kMaxExperts];               // 16 KB
+                                                         float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) float s_x[kRpPass][kRpTok];       // 32 KB, [input][token]
+  __shared__ float s_parts[kRpWaves][kRpTok][64];                           // 32 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * kRpTok;
+  const int e = blockIdx.y * 64 + lane;
   const int nchunks = d / kGroup;
-  const int s_tok = tid >> 8, s_e = tid & 255;
-  for (int eb = 0; eb < E; eb += 256) {
-    float acc = 0.0f;
-    for (int p = 0; p < nchunks; p += kRpWaves) {
-      const int npass = min(kRpWaves, nchunks - p);
-      for (int idx = tid; idx < kRpWaves * kGroup * kRpTok; idx += 1024) {
-        const int tk = idx / (kRpWaves * kGroup), i = idx % (kRpWaves * kGroup);
-        float v = 0.0f;
-        if (t0 + tk < T && i < npass * kGroup) v = bf16_to_f32(x[(size_t)(t0 + tk) * d + p * kGroup + i]);
-        s_x[i][tk] = v;
-      }
-      __syncthreads();
-      if (wave < npass) {
-        const int c = p + wave;
-        float pr[kRpTok][4];
-#pragma unroll
-        for (int tk = 0; tk < kRpTok; ++tk)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) pr[tk][q] = 0.0f;
-        const float* wp = wr + (size_t)c * kGroup * E + eb + lane;
-        for (int i = 0; i < kGroup; ++i) {
-          float wv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) wv[q] = (eb + lane + 64 * q < E) ? wp[(size_t)i * E + 64 * q] : 0.0f;
-          const float4 xv = *reinterpret_cast<const float4*>(&s_x[wave * kGroup + i][0]);
-          const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-          for (int tk = 0; tk < kRpTok; ++tk)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) pr[tk][q] = fmaf(xs[tk], wv[q], pr[tk][q]);
-        }
-#pragma unroll
-        for (int tk = 0; tk < kRpTok; ++tk)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) s_parts[wave][tk][lane + 64 * q] = pr[tk][q];
-      }
-      __syncthreads();
-      for (int cc = 0; cc < npass; ++cc) acc = acc + s_parts[cc][s_tok][s_e];
-      __syncthreads();
+  const int s_tok = tid >> 6, s_e = blockIdx.y * 64 + lane;  // sum phase: threads 0..511
+  float acc = 0.0f;
+  for (int p = 0; p < nchunks; p += kRpWaves) {
+    const int npass = min(kRpWaves, nchunks - p);
+    for (int idx = tid; idx < kRpPass * kRpTok; idx += 1024) {
+      const int tk = idx / kRpPass, i = idx % kRpPass;
+      float v = 0.0f;
+      if (t0 + tk < T && i < npass * kGroup) v = bf16_to_f32(x[(size_t)(t0 + tk) * d + p * kGroup + i]);
+      s_x[i][tk] = v;
     }
-    const int e = eb + s_e;
-    if (e < E) {
-      float v = acc;
-      if (bias) v = v + bias[e];
-      s_lg[s_tok][e] = v;
+    __syncthreads();
+    if (wave < npass) {
+      const int c = p + wave;
+      float wv[kGroup];
+      const float* wp = wr + (size_t)c * kGroup * E + (e < E ? e : 0);
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) wv[i] = wp[(size_t)i * E];
+      float pr[kRpTok];
+#pragma unroll
+      for (int tk = 0; tk < kRpTok; ++tk) pr[tk] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const float4 xa = *reinterpret_cast<const float4*>(&s_x[wave * kGroup + i][0]);
+        const float4 xb = *reinterpret_cast<const float4*>(&s_x[wave * kGroup + i][4]);
+        const float xs[kRpTok] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int tk = 0; tk < kRpTok; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
+      }
+#pragma unroll
+      for (int tk = 0; tk < kRpTok; ++tk) s_parts[wave][tk][lane] = pr[tk];
     }
+    __syncthreads();
+    if (tid < kRpTok * 64)
+      for (int cc = 0; cc < npass; ++cc) acc = acc + s_parts[cc][s_tok][lane];
+    __syncthreads();
   }
-  __syncthreads();
-  if (wave < kRpTok && t0 + wave < T)
-    wave_topk_softmax(s_lg[wave], E, k, ids + (size_t)(t0 + wave) * k, w + (size_t)(t0 + wave) * k);
+  if (tid < kRpTok * 64 && t0 + s_tok < T && s_e < E) {
+    float v = acc;
+    if (bias) v = v + bias[s_e];
+    logits[(size_t)(t0 + s_tok) * E + s_e] = v;
+  }
 }
 
 hipError_t launch_router_prefill(const Ctx& c) {
-  const int nblk = (c.T + kRpTok - 1) / kRpTok;
-  hipLaunchKernelGGL(k_router_prefill, dim3(nblk), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.k, c.x, c.w_router,
-                     c.logit_bias, c.r.topk_ids, c.r.topk_w);
+  const dim3 grid((c.T + kRpTok - 1) / kRpTok, (c.E + 63) / 64);
+  hipLaunchKernelGGL(k_router_prefill, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router, c.logit_bias,
+                     c.logits);
+  return hipGetLastError();
+}
+
+// Top-k and gate weights of T tokens from their logits, one wave per token.
+__global__ __launch_bounds__(256) void k_topk_prefill(int T, int E, int k, const float* __restrict__ logits,
+                                                      int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ float s_lg[4][kMaxExperts];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  for (int e = lane; e < E; e += 64) s_lg[wave][e] = logits[(size_t)t * E + e];
+  __builtin_amdgcn_wave_barrier();
+  wave_topk_softmax(s_lg[wave], E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+hipError_t launch_topk_prefill(const Ctx& c) {
+  hipLaunchKernelGGL(k_topk_prefill, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, c.T, c.E, c.k, c.logits,
+                     c.r.topk_ids, c.r.topk_w);
   return hipGetLastError();
 }
 

@@ -55,8 +55,8 @@ def test_stage_lists():
         ["router_decode", "gemv_gateup_topk", "gemv_down_combine"]
     n2 = L.moe_num_stages(ctypes.byref(d), 512)
     assert [L.moe_stage_name(ctypes.byref(d), 512, s).decode() for s in range(n2)] == \
-        ["router_prefill", "route_meta", "gateup_gemm", "down_gemm", "combine"]
-    assert L.moe_stage_name(ctypes.byref(d), 512, 5) is None
+        ["router_prefill", "topk_prefill", "route_meta", "gateup_gemm", "down_gemm", "combine"]
+    assert L.moe_stage_name(ctypes.byref(d), 512, 6) is None
     big = _dims(k=16, I=2048)  # too much h for the GEMV path: T = 1 runs the grouped GEMM
     assert [L.moe_stage_name(ctypes.byref(big), 1, s).decode() for s in range(L.moe_num_stages(ctypes.byref(big), 1))] \
         == ["router_decode", "decode_topk", "route_meta", "gateup_gemm", "down_gemm", "combine"]
