@@ -14,7 +14,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 64;      // quantisation group along the input dimension
-constexpr int kTileRows = 128;  // block-map tile height
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 

@@ -1,28 +1,25 @@
-// Prefill: grouped GEMM over the expert groups of the block map, with the 4-bit weights
-// dequantised tile by tile into LDS as bf16 and multiplied on the matrix cores with fp32
-// accumulation; the expanded weights never reach HBM ("Perplexity's Lily Beats MLX-LM on MacBook
+// Prefill: grouped GEMM over the expert groups of the block map. The 4-bit weights of one K
+// step are staged in LDS a tile at a time and multiplied on the matrix cores with fp32
+// accumulation; no expanded weight ever reaches HBM ("Perplexity's Lily Beats MLX-LM on MacBook
 // M5. Because It Only Runs One Model.", section "Prefill: keep routing on the GPU, dequantize in
 // flight"). Gate and up share a block so SwiGLU is applied in registers and h is written once,
 // in bf16. The shared expert is one more group of T rows in the same launch.
 //
 // Tiling (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
-//   - a block is 4 waves; K advances 128 inputs (two quantisation groups) per step;
-//   - each thread dequantises one 64-input group of one weight row per step (32 bytes of codes,
-//     one scale, one bias) into LDS, while the next step's codes are already in flight;
-//   - the A rows (tokens, gathered through sorted_token) are staged in LDS as they are in HBM;
-//   - the M extent of a tile is 16, 32, 64 or 128 rows, the smallest that covers the tile's
-//     rows, so small expert groups are not padded to a large tile;
+//   - a tile is at most 32 rows of one expert group; its M extent is 16 or 32 rows, the
+//     smallest that covers it (the same section's note that 32-row tiles beat 16-row ones);
+//   - a block is 4 waves and covers 128 weight rows (gate/up: 64 gate + 64 up rows, giving 64 h
+//     columns; down: 128 output columns); K advances 128 inputs (two quantisation groups) a step;
 //   - the grid is an upper bound (moe_max_tiles x column blocks); blocks past the device-side
 //     tile count exit at once. Blocks are renumbered so that each XCD (blocks are dealt to the
 //     8 XCDs round-robin) gets a contiguous range ordered (column block, tile): tiles of one
-//     large expert that read the same weight rows then run on the same XCD and share its L2.
+//     expert that read the same weight rows then run on the same XCD and share its L2.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int kBK = 128;             // inputs per K step
-constexpr int kLds = kBK + 8;        // LDS row stride in bf16 (16-byte pad)
 constexpr int kGuCols = 64;          // h columns per gate/up block (64 gate + 64 up weight rows)
 constexpr int kDnCols = 128;         // output columns per down block
 
@@ -57,252 +54,298 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& nb, int& e, i
   row0 = a.tiles[3 * ti + 1];
   rows = a.tiles[3 * ti + 2];
   // a corrupt block map must not turn into out-of-bounds accesses
-  if (e < 0 || e > a.E || (e == a.E && a.Is == 0) || rows < 1 || rows > kTileRows || row0 < 0 ||
-      row0 + rows > a.P + (a.Is ? a.T : 0) || (e < a.E && row0 + rows > a.P) || (e == a.E && row0 < a.P))
-    return false;
-  return true;
+  return !(e < 0 || e > a.E || (e == a.E && a.Is == 0) || rows < 1 || rows > kTileRows || row0 < 0 ||
+           row0 + rows > a.P + (a.Is ? a.T : 0) || (e < a.E && row0 + rows > a.P) || (e == a.E && row0 < a.P));
 }
 
-// Load the next K step of one thread's weight group and A chunks.
-struct StepRegs {
-  uint4 c0, c1;
-  uint16_t s, b;
-  bool gv, av;  // group present / A chunk inside K (applied when the slot is consumed)
+// ---------------------------------------------------------------------------------------------
+// The matrix cores take the 4-bit codes themselves. Over one 64-input group with scale s and bias b,
+//   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * X_g,   X_g = sum_k x_k,
+// and "128 + q" is an exact bf16 made from the code bits with one and-or per pair. So each group
+// runs its two MFMA K-steps into a fresh accumulator, then two FMAs fold the group's scale and
+// bias into the running sum; X_g comes from one more MFMA of the same A rows against ones. The
+// weight enters as s * q + b evaluated in fp32 without rounding the weight itself to bf16 first
+// (a difference of at most half a bf16 ulp per weight).
+//
+// Pipeline: every input of K step s (128 inputs) goes straight from memory to LDS with direct
+// loads (no registers on the way), three steps ahead, into a ring of four stages:
+//   - codes: 128 weight rows x 64 bytes; each row's four 16-byte quarters are XOR-swizzled by
+//     row so the MFMA-side 8-byte reads spread over the banks;
+//   - scales and biases: one 16-bit load per (weight row, group), each landing zero-extended in
+//     its own dword; a group past K or a weight row past the matrix loads from a zero word, so
+//     its codes and A values (read from clamped, in-bounds addresses) add exactly 0;
+//   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes; the 16-byte chunks of a row are
+//     XOR-swizzled by row. A rows past the tile's rows repeat its last row and only reach
+//     accumulator rows that are never written out.
+// A is permuted to the code pair order as it is read for the MFMA. Loads complete in issue
+// order, so before each barrier a wave waits until at most the two younger steps' loads are
+// outstanding: its part of the next stage has then landed.
+constexpr int kCodeStages = 4;               // LDS ring depth (3 steps in flight)
+constexpr int kCodeStageBytes = 128 * 64;    // 128 weight rows x 128 inputs of codes
+constexpr int kSbStageWords = 2 * 256;       // scale dwords [128 rows][2 groups], then biases
+constexpr int kAStageBytes = 32 * 256;       // 32 A rows x 128 bf16
+
+__device__ const uint16_t kZeroHalf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// The stages are separate LDS arrays so that the compiler can tell a direct load into one stage
+// from reads of another and does not wait for loads that a read does not depend on.
+struct GemmLds {
+  uint8_t* c[kCodeStages];
+  uint32_t* sb[kCodeStages];
+  uint8_t* a[kCodeStages];
 };
 
-// K steps kept in flight per thread (codes, scale, bias and A chunks in registers), sized so the
-// ring stays near 100 registers: HBM latency is several K steps long.
-template <int MT>
-constexpr int ring_depth() {
-  return MT == 1 ? 4 : MT == 2 ? 4 : MT == 4 ? 2 : 1;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int a_swz(int r) { return r & 7; }
+
+// Direct loads are written as inline assembly: the compiler's own wait insertion cannot follow
+// them across the loop back-edge and would drain every outstanding load before the first LDS
+// read of each unrolled round. Completion is handled explicitly (step_barrier, and a full wait
+// before the block ends).
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
+  // wave-uniform by construction; readfirstlane puts it in a scalar register for m0
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)l);
+}
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(const void* g, void* l) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
 }
 
-template <int MT>
-__device__ __forceinline__ void store_step(uint16_t* Bs, uint16_t* As, int wr, int wh, const StepRegs& w,
-                                          const uint4 (&areg)[MT], const bool (&amask)[MT]) {
-  uint32_t dq[32];
-  const float s = w.gv ? bf16_to_f32(w.s) : 0.0f, b = w.gv ? bf16_to_f32(w.b) : 0.0f;
-  dequant_group(w.c0, w.c1, s, b, dq);
-  uint4* dst = reinterpret_cast<uint4*>(Bs + wr * kLds + wh * 64);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dst[q] = make_uint4(dq[4 * q], dq[4 * q + 1], dq[4 * q + 2], dq[4 * q + 3]);
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    const bool keep = w.av && amask[mm];
-    const uint4 v = areg[mm];
-    *reinterpret_cast<uint4*>(As + ((tid >> 4) + 16 * mm) * kLds + (tid & 15) * 8) =
-        make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
-  }
+// Waits until at most N of this wave's vector memory loads are outstanding and its LDS reads
+// have completed, then joins the workgroup barrier. No LDS release fence: a fence would also
+// wait for every direct load.
+template <int N>
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));  // vmcnt(N) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// ---------------------------------------------------------------------------------------------
-// gate/up: h[row][n0 + c] = bf16(silu(g) * u) for the 64 columns n0..n0+63 of one tile.
-template <int MT>
-__device__ __forceinline__ void gateup_body(const GemmArgs& a, int n0, int e, int row0, int rows, uint16_t* Bs,
-                                            uint16_t* As) {
+// GU: gate/up (A = gathered x rows, 64 gate + 64 up weight rows, SwiGLU epilogue to h);
+// otherwise down (A = h rows, 128 weight rows of the down matrix, fp32 y_rows epilogue).
+template <int MT, bool GU>
+__device__ __forceinline__ void tile_body(const GemmArgs& a, int n0, int e, int row0, int rows, const GemmLds& L) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool sh = (e == a.E);
   const int Ie = sh ? a.Is : a.I;
   const int mat = sh ? 0 : e;
-  const moe_ffn_q4& F = sh ? a.shared : a.routed;
   const int d = a.d;
-  // this thread's weight group: row wr of the 128 (64 gate rows, then 64 up rows), half wh
-  const int wr = tid >> 1, wh = tid & 1;
-  const moe_q4& Q = wr < kGuCols ? F.gate : F.up;
-  const size_t wrow = (size_t)mat * Ie + n0 + (wr & (kGuCols - 1));
-  const uint8_t* cp = Q.codes + wrow * (size_t)(d / 2) + wh * 32;
-  const uint16_t* sp = Q.scales + wrow * (size_t)(d / kGroup) + wh;
-  const uint16_t* bp = Q.biases + wrow * (size_t)(d / kGroup) + wh;
-  // this thread's A chunks: row (tid >> 4) + 16 mm, inputs 8 (tid & 15) .. +7 of the step
-  const uint16_t* ap[MT];
-  bool amask[MT];
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    const int r = (tid >> 4) + 16 * mm;
-    int tok = -1;
-    if (r < rows) tok = sh ? (row0 - a.P + r) : a.sorted_token[row0 + r];
-    amask[mm] = (unsigned)tok < (unsigned)a.T;
-    ap[mm] = a.x + (size_t)(amask[mm] ? tok : 0) * d;
+  const int K = GU ? d : Ie;        // reduction length
+  const int ldc = K / 2;            // code bytes per weight row
+  const int ldg = K / kGroup;       // groups per weight row
+  const int nrows_w = GU ? Ie : d;  // weight rows of the matrix
+  const int S = (K + kBK - 1) / kBK;
+
+  // ---- codes: wave w fills block rows 32w .. 32w+31 (two 16-row loads per step). For GU, block
+  // rows 0..63 are gate rows (waves 0, 1) and 64..127 up rows (waves 2, 3).
+  const uint8_t *gate_c, *up_c;
+  const uint16_t *gate_s, *up_s, *gate_b, *up_b;
+  if (GU) {
+    gate_c = sh ? a.shared.gate.codes : a.routed.gate.codes;
+    up_c = sh ? a.shared.up.codes : a.routed.up.codes;
+    gate_s = sh ? a.shared.gate.scales : a.routed.gate.scales;
+    up_s = sh ? a.shared.up.scales : a.routed.up.scales;
+    gate_b = sh ? a.shared.gate.biases : a.routed.gate.biases;
+    up_b = sh ? a.shared.up.biases : a.routed.up.biases;
+  } else {
+    gate_c = up_c = sh ? a.shared.down.codes : a.routed.down.codes;
+    gate_s = up_s = sh ? a.shared.down.scales : a.routed.down.scales;
+    gate_b = up_b = sh ? a.shared.down.biases : a.routed.down.biases;
   }
-  const int S = (d + kBK - 1) / kBK;
-  constexpr int D = ring_depth<MT>();
-  StepRegs w[D];
-  uint4 areg[D][MT];
-  // Every slot load is unconditional (step index clamped, A rows of absent tokens read row 0),
-  // so the compiler can count outstanding loads exactly; padding steps and absent rows are
-  // zeroed with selects instead of branches.
-  const int kh_last = (d / 64) - 1;  // last 64-input group index
-  auto load = [&](int s, StepRegs& wd, uint4 (&ad)[MT]) {
-    const int g = min(2 * s + wh, kh_last);
-    const bool gv = 2 * s + wh <= kh_last;
-    wd.c0 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32);
-    wd.c1 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32 + 16);
-    wd.s = sp[g - wh];
-    wd.b = bp[g - wh];
-    wd.gv = gv;
-    const int ka = min(s * kBK + (tid & 15) * 8, d - 8);
-    wd.av = s * kBK + (tid & 15) * 8 < d;
+  const size_t mrow0 = (size_t)mat * nrows_w + n0;  // first weight row of the block in its matrix
+  const uint8_t* cbase = (GU && wave >= 2 ? up_c : gate_c) + mrow0 * (size_t)ldc;
+  uint32_t coff[2];
+  int cq16[2];
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm) ad[mm] = *reinterpret_cast<const uint4*>(ap[mm] + ka);
+  for (int t = 0; t < 2; ++t) {
+    const int r = 32 * wave + 16 * t + (lane >> 2);  // block row
+    const int rl = GU ? (r & (kGuCols - 1)) : r;     // row within this matrix's block
+    const int rc = min(rl, nrows_w - 1 - n0);        // rows past the matrix read its last row
+    coff[t] = (uint32_t)rc * (uint32_t)ldc;
+    cq16[t] = 16 * ((lane & 3) ^ code_swz(r));
+  }
+  // ---- scales / biases: wave w loads array (w >> 1) for block rows 64 (w & 1) .. +63
+  const int sb_arr = wave >> 1;
+  const uint16_t* sb_src[2];
+  bool sb_rowvalid[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int p = 64 * (2 * (wave & 1) + t) + lane;  // index 2 * row + group within the array
+    const int r = p >> 1;
+    const int rl = GU ? (r & (kGuCols - 1)) : r;
+    const bool up = GU && r >= kGuCols;
+    sb_rowvalid[t] = n0 + rl < nrows_w;
+    const uint16_t* arr = sb_arr ? (up ? up_b : gate_b) : (up ? up_s : gate_s);
+    sb_src[t] = arr + (mrow0 + (sb_rowvalid[t] ? rl : 0)) * (size_t)ldg + (p & 1);
+  }
+  // ---- A rows: wave w loads rows 4 (w + 4 t) .. +3, lane j: row + (j >> 4), chunk slot j & 15
+  const uint8_t* arow[MT];
+  int achunk[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int r = 4 * (wave + 4 * t) + (lane >> 4);
+    const int rr = min(r, rows - 1);
+    const uint16_t* rp;
+    if (GU) {
+      int tok = sh ? (row0 - a.P + rr) : a.sorted_token[row0 + rr];
+      tok = min(max(tok, 0), a.T - 1);
+      rp = a.x + (size_t)tok * d;
+    } else {
+      rp = (sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie) + (size_t)rr * Ie;
+    }
+    arow[t] = reinterpret_cast<const uint8_t*>(rp);
+    achunk[t] = 16 * ((lane & 15) ^ a_swz(r));
+  }
+  const int amax = 2 * K - 16;  // last 16-byte chunk of a row
+
+  auto issue = [&](int s, int st) __attribute__((always_inline)) {
+    uint8_t* cdst = L.c[st] + wave * 2048;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dma16(cbase + coff[t] + min(64 * s + cq16[t], ldc - 16), cdst + 1024 * t);
+    uint32_t* sdst = L.sb[st] + sb_arr * 256 + 128 * (wave & 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int g = 2 * s + (lane & 1);
+      const bool ok = sb_rowvalid[t] && g < ldg;
+      dma2(ok ? (const void*)(sb_src[t] + 2 * s) : (const void*)kZeroHalf, sdst + 64 * t);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) dma16(arow[t] + min(256 * s + achunk[t], amax), L.a[st] + 1024 * (wave + 4 * t));
   };
-  f32x4_t accg[MT], accu[MT];
+
+  const int n = lane & 15, kb = lane >> 4;
+  // this lane's two weight rows in the block (subtiles 0 and 1)
+  const int wrow0 = GU ? 16 * wave + n : 32 * wave + n;
+  const int wrow1 = GU ? kGuCols + 16 * wave + n : 32 * wave + 16 + n;
+  const int cread0 = wrow0 * 64 + 8 * (kb & 1), cread1 = wrow1 * 64 + 8 * (kb & 1);
+  const int cswz0 = code_swz(wrow0), cswz1 = code_swz(wrow1);
+  f32x4_t acc[2][MT];
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    accg[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    accu[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-  for (int u = 0; u < D; ++u) load(u, w[u], areg[u]);
-  for (int s0 = 0; s0 < S; s0 += D) {
+    for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const uint8_t* cs = L.c[st];
+    const uint32_t* sb = L.sb[st];
+    const uint8_t* as = L.a[st];
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      store_step<MT>(Bs, As, wr, wh, w[u], areg[u], amask);
-      __syncthreads();
-      load(s0 + u + D, w[u], areg[u]);
-      const int kofs = (lane >> 4) * 8;
+    for (int gg = 0; gg < 2; ++gg) {
+      const int q = 2 * gg + (kb >> 1);
+      const uint2 w0 = *reinterpret_cast<const uint2*>(cs + cread0 + 16 * (q ^ cswz0));
+      const uint2 w1 = *reinterpret_cast<const uint2*>(cs + cread1 + 16 * (q ^ cswz1));
+      f32x4_t tmp[2][MT], xs[MT];
 #pragma unroll
-      for (int kk = 0; kk < kBK / 32; ++kk) {
-        const uint4 bg = *reinterpret_cast<const uint4*>(Bs + (16 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
-        const uint4 bu =
-            *reinterpret_cast<const uint4*>(Bs + (kGuCols + 16 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t c0 = kk ? w0.y : w0.x, c1 = kk ? w1.y : w1.x;
+        const uint4 b0 = make_uint4(magic_pair(c0, 0), magic_pair(c0, 1), magic_pair(c0, 2), magic_pair(c0, 3));
+        const uint4 b1 = make_uint4(magic_pair(c1, 0), magic_pair(c1, 1), magic_pair(c1, 2), magic_pair(c1, 3));
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) {
-          const uint4 av = *reinterpret_cast<const uint4*>(As + (16 * mm + (lane & 15)) * kLds + kk * 32 + kofs);
-          accg[mm] = mfma16x16x32(av, bg, accg[mm]);
-          accu[mm] = mfma16x16x32(av, bu, accu[mm]);
+          const int r = 16 * mm + n, c = 8 * gg + 2 * kb + kk;
+          const uint4 raw = *reinterpret_cast<const uint4*>(as + r * 256 + 16 * (c ^ a_swz(r)));
+          const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+          uint32_t pr[4];
+          repair8(v, pr);
+          const uint4 av = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+          const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          tmp[0][mm] = mfma16x16x32(av, b0, kk == 0 ? z : tmp[0][mm]);
+          tmp[1][mm] = mfma16x16x32(av, b1, kk == 0 ? z : tmp[1][mm]);
+          xs[mm] = mfma16x16x32(raw, ones, kk == 0 ? z : xs[mm]);
         }
       }
-      __syncthreads();
+      const float s0 = bf16lo(sb[2 * wrow0 + gg]), c0 = fmaf(-128.0f, s0, bf16lo(sb[256 + 2 * wrow0 + gg]));
+      const float s1 = bf16lo(sb[2 * wrow1 + gg]), c1 = fmaf(-128.0f, s1, bf16lo(sb[256 + 2 * wrow1 + gg]));
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[0][mm][r] = fmaf(c0, xs[mm][r], fmaf(s0, tmp[0][mm][r], acc[0][mm][r]));
+          acc[1][mm][r] = fmaf(c1, xs[mm][r], fmaf(s1, tmp[1][mm][r], acc[1][mm][r]));
+        }
     }
-  }
-  uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
-  const int col = n0 + 16 * wave + (lane & 15);
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * mm + 4 * (lane >> 4) + r;
-      if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(accg[mm][r], accu[mm][r]));
-    }
-}
-
-__global__ __launch_bounds__(256) void k_gateup_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * kGuCols * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t As[kTileRows * kLds];
-  int nb, e, row0, rows;
-  if (!block_tile(a, nb, e, row0, rows)) return;
-  const int n0 = nb * kGuCols;
-  if (n0 >= (e == a.E ? a.Is : a.I)) return;
-  if (rows <= 16)
-    gateup_body<1>(a, n0, e, row0, rows, Bs, As);
-  else if (rows <= 32)
-    gateup_body<2>(a, n0, e, row0, rows, Bs, As);
-  else if (rows <= 64)
-    gateup_body<4>(a, n0, e, row0, rows, Bs, As);
-  else
-    gateup_body<8>(a, n0, e, row0, rows, Bs, As);
-}
-
-// ---------------------------------------------------------------------------------------------
-// down: y_rows[row][n0 + c] = h[row] . Wd[e][n0 + c] for 128 output columns of one tile.
-template <int MT>
-__device__ __forceinline__ void down_body(const GemmArgs& a, int n0, int e, int row0, int rows, uint16_t* Bs,
-                                          uint16_t* As) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool sh = (e == a.E);
-  const int Ie = sh ? a.Is : a.I;
-  const int mat = sh ? 0 : e;
-  const moe_q4& Q = sh ? a.shared.down : a.routed.down;
-  const int d = a.d;
-  const int wr = tid >> 1, wh = tid & 1;
-  const bool wvalid = n0 + wr < d;
-  const size_t wrow = (size_t)mat * d + n0 + (wvalid ? wr : 0);
-  const uint8_t* cp = Q.codes + wrow * (size_t)(Ie / 2) + wh * 32;
-  const uint16_t* sp = Q.scales + wrow * (size_t)(Ie / kGroup) + wh;
-  const uint16_t* bp = Q.biases + wrow * (size_t)(Ie / kGroup) + wh;
-  const uint16_t* hbase = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
-  const uint16_t* ap[MT];
-  bool amask[MT];
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    const int r = (tid >> 4) + 16 * mm;
-    amask[mm] = r < rows;
-    ap[mm] = hbase + (size_t)(amask[mm] ? r : 0) * Ie;
-  }
-  const int S = (Ie + kBK - 1) / kBK;
-  constexpr int D = ring_depth<MT>();
-  StepRegs w[D];
-  uint4 areg[D][MT];
-  const int kh_last = (Ie / 64) - 1;
-  auto load = [&](int s, StepRegs& wd, uint4 (&ad)[MT]) {
-    const int g = min(2 * s + wh, kh_last);
-    const bool gv = wvalid && 2 * s + wh <= kh_last;
-    wd.c0 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32);
-    wd.c1 = *reinterpret_cast<const uint4*>(cp - wh * 32 + g * 32 + 16);
-    wd.s = sp[g - wh];
-    wd.b = bp[g - wh];
-    wd.gv = gv;
-    const int ka = min(s * kBK + (tid & 15) * 8, Ie - 8);
-    wd.av = s * kBK + (tid & 15) * 8 < Ie;
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm) ad[mm] = *reinterpret_cast<const uint4*>(ap[mm] + ka);
   };
-  f32x4_t acc[MT][2];
-#pragma unroll
-  for (int mm = 0; mm < MT; ++mm) acc[mm][0] = acc[mm][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < D; ++u) load(u, w[u], areg[u]);
-  for (int s0 = 0; s0 < S; s0 += D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      store_step<MT>(Bs, As, wr, wh, w[u], areg[u], amask);
-      __syncthreads();
-      load(s0 + u + D, w[u], areg[u]);
-      const int kofs = (lane >> 4) * 8;
-#pragma unroll
-      for (int kk = 0; kk < kBK / 32; ++kk) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(Bs + (32 * wave + (lane & 15)) * kLds + kk * 32 + kofs);
-        const uint4 b1 =
-            *reinterpret_cast<const uint4*>(Bs + (32 * wave + 16 + (lane & 15)) * kLds + kk * 32 + kofs);
-#pragma unroll
-        for (int mm = 0; mm < MT; ++mm) {
-          const uint4 av = *reinterpret_cast<const uint4*>(As + (16 * mm + (lane & 15)) * kLds + kk * 32 + kofs);
-          acc[mm][0] = mfma16x16x32(av, b0, acc[mm][0]);
-          acc[mm][1] = mfma16x16x32(av, b1, acc[mm][1]);
-        }
-      }
-      __syncthreads();
-    }
+
+  // Loads past the last step are issued anyway (clamped to it) so that every iteration issues
+  // the same sequence; their data lands in stages that are not read again.
+  constexpr int kOps = 2 + 2 + MT;  // loads one wave issues per step
+  const int Sm = S - 1;
+  issue(0, 0);
+  issue(min(1, Sm), 1);
+  issue(min(2, Sm), 2);
+  auto iter = [&](int s, int j) __attribute__((always_inline)) {
+    step_barrier<2 * kOps>();
+    issue(min(s + 3, Sm), (j + 3) & 3);
+    compute(j);
+  };
+  for (int s = 0; s < S; s += 4) {
+    iter(s, 0);
+    if (s + 1 < S) iter(s + 1, 1);
+    if (s + 2 < S) iter(s + 2, 2);
+    if (s + 3 < S) iter(s + 3, 3);
   }
+  // the clamped loads past the end must land before the block (and its LDS) is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (GU) {
+    uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
+    const int col = n0 + 16 * wave + n;
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      const int col = n0 + 32 * wave + 16 * nn + (lane & 15);
-      if (col >= d) continue;
+    for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mm + 4 * (lane >> 4) + r;
-        if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[mm][nn][r];
+        const int row = 16 * mm + 4 * kb + r;
+        if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
       }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = n0 + 32 * wave + 16 * t + n;
+      if (col >= d) continue;
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mm + 4 * kb + r;
+          if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
+        }
     }
+  }
 }
 
-__global__ __launch_bounds__(256) void k_down_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kDnCols * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t As[kTileRows * kLds];
+template <bool GU>
+__device__ __forceinline__ void gemm_block(const GemmArgs& a) {
+  __shared__ __attribute__((aligned(16))) uint8_t c0[kCodeStageBytes], c1[kCodeStageBytes], c2[kCodeStageBytes],
+      c3[kCodeStageBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s0[kSbStageWords], s1[kSbStageWords], s2[kSbStageWords],
+      s3[kSbStageWords];
+  __shared__ __attribute__((aligned(16))) uint8_t a0[kAStageBytes], a1[kAStageBytes], a2[kAStageBytes],
+      a3[kAStageBytes];
+  const GemmLds L = {{c0, c1, c2, c3}, {s0, s1, s2, s3}, {a0, a1, a2, a3}};
   int nb, e, row0, rows;
   if (!block_tile(a, nb, e, row0, rows)) return;
-  const int n0 = nb * kDnCols;
+  const int n0 = nb * (GU ? kGuCols : kDnCols);
+  if (GU && n0 >= (e == a.E ? a.Is : a.I)) return;
   if (rows <= 16)
-    down_body<1>(a, n0, e, row0, rows, Bs, As);
-  else if (rows <= 32)
-    down_body<2>(a, n0, e, row0, rows, Bs, As);
-  else if (rows <= 64)
-    down_body<4>(a, n0, e, row0, rows, Bs, As);
+    tile_body<1, GU>(a, n0, e, row0, rows, L);
   else
-    down_body<8>(a, n0, e, row0, rows, Bs, As);
+    tile_body<2, GU>(a, n0, e, row0, rows, L);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gateup_gemm(GemmArgs a) {
+  gemm_block<true>(a);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_down_gemm(GemmArgs a) {
+  gemm_block<false>(a);
 }
 
 static GemmArgs gemm_args(const Ctx& c, int nb) {

@@ -42,6 +42,9 @@ hipError_t launch_down_gemm(const Ctx& c);
 hipError_t launch_combine(const Ctx& c);
 hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* out, hipStream_t stream);
 
+// Block-map tile height (rows of one expert group per tile).
+constexpr int kTileRows = 32;
+
 // The GEMV decode path keeps all selected experts' h in LDS: (k*I + Is) bf16 values.
 constexpr int kGemvMaxH = 28672;
 // ... and its down kernel keeps two 16-lane rounds of 32-input pieces per row in registers.

@@ -49,7 +49,7 @@ int check_dims(const moe_dims* dm, int32_t T) {
 
 int32_t max_tiles_of(const moe_dims& dm, int32_t T) {
   const int64_t P = (int64_t)T * dm.top_k;
-  const int64_t t = std::min<int64_t>(dm.n_experts, P) + P / 128 + (dm.d_ff_shared ? (T + 127) / 128 : 0);
+  const int64_t t = std::min<int64_t>(dm.n_experts, P) + P / kTileRows + (dm.d_ff_shared ? (T + kTileRows - 1) / kTileRows : 0);
   return (int32_t)t;
 }
 

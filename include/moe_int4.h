@@ -106,7 +106,7 @@ typedef struct {
  *   inv_pos  [T][k]  int32  grouped row of pair (t, j)
  *   tiles    [moe_max_tiles()][3] int32  block map: (expert, first grouped row, rows);
  *                           each non-empty group in ascending expert order is cut into
- *                           tiles of at most 128 rows; the shared expert's T rows follow
+ *                           tiles of at most 32 rows; the shared expert's T rows follow
  *                           as grouped rows T*k .. T*k+T-1 tagged with expert index E
  *   n_tiles  [1]     int32  number of valid tiles (stays on the device)
  */
@@ -122,7 +122,7 @@ typedef struct {
 } moe_routing;
 
 /* Host-only, pure. Upper bound on the block map's length for T tokens:
- * min(E, T*k) + floor(T*k / 128) + (shared ? ceil(T / 128) : 0). Returns -1 on bad dims. */
+ * min(E, T*k) + floor(T*k / 32) + (shared ? ceil(T / 32) : 0). Returns -1 on bad dims. */
 int32_t moe_max_tiles(const moe_dims* dims, int32_t T);
 
 /* Host-only, pure. Bytes of workspace every entry point below needs for T tokens (the same

@@ -50,7 +50,7 @@
 #endif
 
 #define ORC_GROUP 64
-#define ORC_TILE_ROWS 128
+#define ORC_TILE_ROWS 32
 
 typedef struct {
   const uint8_t* codes;    /* [n_mat][out][in/2], low nibble = even input index */
@@ -157,10 +157,11 @@ int oracle_topk_softmax(int32_t T, int32_t E, int32_t k, const float* logits, in
  * sort of pairs by expert, so rows of one expert keep ascending token order (reading: the
  * pages do not fix the order inside a group); sorted_token[row] = token of that grouped row,
  * inv_pos[t][j] = grouped row of pair (t, j).
- * Block map (reading; the pages say only that block size follows each expert's load): each non-empty group,
- * in ascending expert order, is cut into consecutive tiles of at most 128 rows; then, when a
- * shared expert exists, its T rows (grouped rows T*k .. T*k+T-1, token order) are cut the same
- * way and tagged with expert index E. A tile is (expert, first grouped row, rows). */
+ * Block map (reading; the pages say that block size follows each expert's load and that 32-row
+ * tiles beat 16-row ones): each non-empty group, in ascending expert order, is cut into
+ * consecutive tiles of at most 32 rows; then, when a shared expert exists, its T rows (grouped
+ * rows T*k .. T*k+T-1, token order) are cut the same way and tagged with expert index E. A tile
+ * is (expert, first grouped row, rows). */
 int oracle_route_meta(int32_t T, int32_t E, int32_t k, int32_t has_shared, const int32_t* ids,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
                       int32_t* tiles, int32_t tiles_cap, int32_t* n_tiles) {

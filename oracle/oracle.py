@@ -130,7 +130,7 @@ def topk_softmax(logits, k: int):
 
 def max_tiles(T: int, E: int, k: int, has_shared: bool) -> int:
     P = T * k
-    return min(E, P) + P // 128 + ((T + 127) // 128 if has_shared else 0)
+    return min(E, P) + P // 32 + ((T + 31) // 32 if has_shared else 0)
 
 
 def route_meta(ids, E: int, has_shared: bool):

@@ -37,9 +37,9 @@ def _dims(d=2048, E=256, k=8, I=512, Is=512, g=64):
 
 def test_sizing_helpers():
     d = _dims()
-    assert moe.max_tiles(d, 512) == 256 + 4096 // 128 + 4
+    assert moe.max_tiles(d, 512) == 256 + 4096 // 32 + 16
     assert moe.max_tiles(d, 1) == 8 + 0 + 1
-    assert moe.max_tiles(_dims(E=128, I=768, Is=0), 256) == 128 + 16
+    assert moe.max_tiles(_dims(E=128, I=768, Is=0), 256) == 128 + 64
     ws = moe.workspace_bytes(d, 512)
     assert ws % 256 == 0 and ws >= (4096 + 512) * 2048 * 4 + 4096 * 512 * 2
     assert moe.workspace_bytes(d, 0) > 0

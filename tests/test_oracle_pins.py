@@ -293,12 +293,12 @@ def _check_meta(ids, E, has_shared, m):
     inv = np.empty(P, np.int64)
     inv[np.array(order)] = np.arange(P)
     assert (m["inv_pos"].ravel() == inv).all()
-    # tiles partition the grouped rows in order, never cross a group, at most 128 rows
+    # tiles partition the grouped rows in order, never cross a group, at most 32 rows
     tiles = m["tiles"]
     rows = np.concatenate([np.arange(s, s + n) for _, s, n in tiles]) if len(tiles) else np.zeros(0)
     assert (rows == np.arange(P + (T if has_shared else 0))).all()
     for e, s, n in tiles:
-        assert 1 <= n <= 128
+        assert 1 <= n <= 32
         if e < E:
             assert m["offsets"][e] <= s and s + n <= m["offsets"][e + 1]
         else:
@@ -311,10 +311,10 @@ def test_route_meta_invariants_random_and_skewed():
     for T, E, k, sh in [(37, 16, 4, True), (300, 8, 1, False), (1, 256, 8, True), (513, 64, 8, True)]:
         ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
         _check_meta(ids, E, sh, oracle.route_meta(ids, E, sh))
-    ids = np.full((300, 1), 3, np.int32)  # every token to one expert: tiles 128, 128, 44
+    ids = np.full((300, 1), 3, np.int32)  # every token to one expert: nine tiles of 32, then 12
     m = oracle.route_meta(ids, 8, False)
     _check_meta(ids, 8, False, m)
-    assert m["tiles"].tolist() == [[3, 0, 128], [3, 128, 128], [3, 256, 44]]
+    assert m["tiles"].tolist() == [[3, 32 * i, 32] for i in range(9)] + [[3, 288, 12]]
 
 
 def test_route_meta_worked_instance_from_pages():
