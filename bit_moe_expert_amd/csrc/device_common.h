@@ -76,7 +76,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and reciprocal (about 1 ulp
+// each; the division's correctly rounded sequence costs an order of magnitude more).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

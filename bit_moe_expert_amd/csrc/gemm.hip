@@ -24,7 +24,7 @@ constexpr int kGuCols = 64;          // h columns per gate/up block (64 gate + 6
 constexpr int kDnCols = 128;         // output columns per down block
 
 struct GemmArgs {
-  int d, E, k, I, Is, T, P, max_tiles, nb;
+  int d, E, k, I, Is, T, P, max_tiles, nb;  // nb: runs of column blocks
   const uint16_t* x;
   const int32_t* sorted_token;
   const int32_t* tiles;
@@ -40,14 +40,14 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
                                                  0, 0, 0);
 }
 
-// Decode the block's (column block, tile) and validate the tile. Returns false when the block
-// has nothing to do.
-__device__ __forceinline__ bool block_tile(const GemmArgs& a, int& nb, int& e, int& row0, int& rows) {
+// Decode the block's (run of column blocks, tile) and validate the tile. Returns false when the
+// block has nothing to do.
+__device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, int& row0, int& rows) {
   const int per_xcd = gridDim.x / 8;
   const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  nb = L / a.max_tiles;
+  run = L / a.max_tiles;
   const int ti = L % a.max_tiles;
-  if (nb >= a.nb) return false;
+  if (run >= a.nb) return false;
   const int nt = min(*a.n_tiles, a.max_tiles);
   if (ti >= nt) return false;
   e = a.tiles[3 * ti];
@@ -67,36 +67,38 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& nb, int& e, i
 // weight enters as s * q + b evaluated in fp32 without rounding the weight itself to bf16 first
 // (a difference of at most half a bf16 ulp per weight).
 //
-// Pipeline: every input of K step s (128 inputs) goes straight from memory to LDS with direct
-// loads (no registers on the way), three steps ahead, into a ring of four stages:
+// Work item: one tile and a run of consecutive column blocks (gate/up: 64 h columns = 64 gate +
+// 64 up weight rows; down: 128 output columns). The block streams the run's column blocks
+// through one continuous pipeline, so the load latency at the start is paid once per run.
+//
+// Pipeline: every input of a K step (128 inputs) goes straight from memory to LDS with direct
+// loads (no registers on the way), two steps ahead, into a ring of three stages:
 //   - codes: 128 weight rows x 64 bytes; each row's four 16-byte quarters are XOR-swizzled by
 //     row so the MFMA-side 8-byte reads spread over the banks;
-//   - scales and biases: one 16-bit load per (weight row, group), each landing zero-extended in
-//     its own dword; a group past K or a weight row past the matrix loads from a zero word, so
-//     its codes and A values (read from clamped, in-bounds addresses) add exactly 0;
+//   - scales and biases: with an even number of groups per row, one 4-byte load per weight row
+//     and array (the step's two groups); otherwise one 2-byte load per (row, group), each
+//     landing zero-extended in its own dword;
 //   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes; the 16-byte chunks of a row are
 //     XOR-swizzled by row. A rows past the tile's rows repeat its last row and only reach
 //     accumulator rows that are never written out.
-// A is permuted to the code pair order as it is read for the MFMA. Loads complete in issue
-// order, so before each barrier a wave waits until at most the two younger steps' loads are
-// outstanding: its part of the next stage has then landed.
-constexpr int kCodeStages = 4;               // LDS ring depth (3 steps in flight)
-constexpr int kCodeStageBytes = 128 * 64;    // 128 weight rows x 128 inputs of codes
-constexpr int kSbStageWords = 2 * 256;       // scale dwords [128 rows][2 groups], then biases
-constexpr int kAStageBytes = 32 * 256;       // 32 A rows x 128 bf16
+// Addresses are a scalar base that advances per step plus a per-lane offset fixed for the run.
+// When K is an odd number of groups, the last step's second group reads in-bounds stand-in data
+// and is given scale and bias 0 when it is multiplied. Weight rows past the down matrix repeat
+// its last row; their outputs are not written. Loads complete in issue order, so before each
+// barrier a wave waits until only the younger step's loads are outstanding: its part of the
+// next stage has then landed.
+constexpr int kStages = 3;                 // LDS ring depth (2 steps in flight)
+constexpr int kCodeStageBytes = 128 * 64;  // 128 weight rows x 128 inputs of codes
+constexpr int kAStageBytes = 32 * 256;     // 32 A rows x 128 bf16
+constexpr int kRunGu = 1;                  // column blocks per gate/up work item
+constexpr int kRunDn = 2;                  // column blocks per down work item
 
-__device__ const uint16_t kZeroHalf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-
-// The stages are separate LDS arrays so that the compiler can tell a direct load into one stage
-// from reads of another and does not wait for loads that a read does not depend on.
+// The stages are separate LDS arrays so that the compiler can tell them apart.
 struct GemmLds {
-  uint8_t* c[kCodeStages];
-  uint32_t* sb[kCodeStages];
-  uint8_t* a[kCodeStages];
+  uint8_t* c[kStages];
+  uint32_t* sb[kStages];
+  uint8_t* a[kStages];
 };
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 __device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int a_swz(int r) { return r & 7; }
@@ -104,16 +106,30 @@ __device__ __forceinline__ int a_swz(int r) { return r & 7; }
 // Direct loads are written as inline assembly: the compiler's own wait insertion cannot follow
 // them across the loop back-edge and would drain every outstanding load before the first LDS
 // read of each unrolled round. Completion is handled explicitly (step_barrier, and a full wait
-// before the block ends).
+// before the block ends). Address = 64-bit scalar base + 32-bit per-lane offset.
 __device__ __forceinline__ uint32_t lds_addr(const void* l) {
   // wave-uniform by construction; readfirstlane puts it in a scalar register for m0
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)l);
 }
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ void dma2(const void* g, void* l) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, void* l) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+               "s"(lds_addr(l))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, void* l) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+               "s"(lds_addr(l))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(const void* base, uint32_t off, void* l) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+               "s"(lds_addr(l))
+               : "memory", "m0");
 }
 
 // Waits until at most N of this wave's vector memory loads are outstanding and its LDS reads
@@ -130,8 +146,9 @@ __device__ __forceinline__ void step_barrier() {
 
 // GU: gate/up (A = gathered x rows, 64 gate + 64 up weight rows, SwiGLU epilogue to h);
 // otherwise down (A = h rows, 128 weight rows of the down matrix, fp32 y_rows epilogue).
-template <int MT, bool GU>
-__device__ __forceinline__ void tile_body(const GemmArgs& a, int n0, int e, int row0, int rows, const GemmLds& L) {
+// PAIRED: K is a multiple of 128 (whole steps; scale/bias pairs load as one dword).
+template <int MT, bool GU, bool PAIRED>
+__device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, const GemmLds& L) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool sh = (e == a.E);
   const int Ie = sh ? a.Is : a.I;
@@ -140,84 +157,108 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int n0, int e, int 
   const int K = GU ? d : Ie;        // reduction length
   const int ldc = K / 2;            // code bytes per weight row
   const int ldg = K / kGroup;       // groups per weight row
-  const int nrows_w = GU ? Ie : d;  // weight rows of the matrix
+  const int nrows_w = GU ? Ie : d;  // weight rows of the matrix (per expert)
   const int S = (K + kBK - 1) / kBK;
+  const int cols = GU ? kGuCols : kDnCols;
+  const int ncb = (nrows_w + cols - 1) / cols;  // column blocks of this matrix
+  const int R = GU ? kRunGu : kRunDn;
+  const int nb0 = run * R;
+  const int njobs = min(R, ncb - nb0);
+  if (njobs <= 0) return;
+  const int P = njobs * S;  // pipeline length in K steps
 
-  // ---- codes: wave w fills block rows 32w .. 32w+31 (two 16-row loads per step). For GU, block
-  // rows 0..63 are gate rows (waves 0, 1) and 64..127 up rows (waves 2, 3).
-  const uint8_t *gate_c, *up_c;
-  const uint16_t *gate_s, *up_s, *gate_b, *up_b;
+  // ---- weight matrices (for GU, waves 0, 1 load gate rows and waves 2, 3 up rows)
+  const uint8_t* wc;
+  const uint16_t *ws, *wb;  // scale / bias arrays of this wave's direct loads
+  const uint16_t* sb_arr;
   if (GU) {
-    gate_c = sh ? a.shared.gate.codes : a.routed.gate.codes;
-    up_c = sh ? a.shared.up.codes : a.routed.up.codes;
-    gate_s = sh ? a.shared.gate.scales : a.routed.gate.scales;
-    up_s = sh ? a.shared.up.scales : a.routed.up.scales;
-    gate_b = sh ? a.shared.gate.biases : a.routed.gate.biases;
-    up_b = sh ? a.shared.up.biases : a.routed.up.biases;
+    const bool upw = wave >= 2;
+    wc = sh ? (upw ? a.shared.up.codes : a.shared.gate.codes) : (upw ? a.routed.up.codes : a.routed.gate.codes);
+    // scale/bias loads: wave w loads array (w >> 1) for block rows 64 (w & 1) .. +63, which are
+    // gate rows for w & 1 == 0 and up rows for w & 1 == 1
+    const bool ups = (wave & 1) != 0;
+    ws = sh ? (ups ? a.shared.up.scales : a.shared.gate.scales) : (ups ? a.routed.up.scales : a.routed.gate.scales);
+    wb = sh ? (ups ? a.shared.up.biases : a.shared.gate.biases) : (ups ? a.routed.up.biases : a.routed.gate.biases);
   } else {
-    gate_c = up_c = sh ? a.shared.down.codes : a.routed.down.codes;
-    gate_s = up_s = sh ? a.shared.down.scales : a.routed.down.scales;
-    gate_b = up_b = sh ? a.shared.down.biases : a.routed.down.biases;
+    wc = sh ? a.shared.down.codes : a.routed.down.codes;
+    ws = sh ? a.shared.down.scales : a.routed.down.scales;
+    wb = sh ? a.shared.down.biases : a.routed.down.biases;
   }
-  const size_t mrow0 = (size_t)mat * nrows_w + n0;  // first weight row of the block in its matrix
-  const uint8_t* cbase = (GU && wave >= 2 ? up_c : gate_c) + mrow0 * (size_t)ldc;
-  uint32_t coff[2];
-  int cq16[2];
+  sb_arr = (wave >> 1) ? wb : ws;
+  const size_t mrow = (size_t)mat * nrows_w;  // first row of this expert's matrix
+
+  // ---- per-lane fixed offsets
+  // codes: block row r = 32 wave + 16 t + (lane >> 2), quarter slot lane & 3
+  int crow[2];
+  uint32_t cq16[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int r = 32 * wave + 16 * t + (lane >> 2);  // block row
-    const int rl = GU ? (r & (kGuCols - 1)) : r;     // row within this matrix's block
-    const int rc = min(rl, nrows_w - 1 - n0);        // rows past the matrix read its last row
-    coff[t] = (uint32_t)rc * (uint32_t)ldc;
+    const int r = 32 * wave + 16 * t + (lane >> 2);
+    crow[t] = GU ? (r & (kGuCols - 1)) : r;  // row within the column block's weight rows
     cq16[t] = 16 * ((lane & 3) ^ code_swz(r));
   }
-  // ---- scales / biases: wave w loads array (w >> 1) for block rows 64 (w & 1) .. +63
-  const int sb_arr = wave >> 1;
-  const uint16_t* sb_src[2];
-  bool sb_rowvalid[2];
+  // scale/bias: PAIRED: block row 64 (wave & 1) + lane; else (row, group) = (p >> 1, p & 1) for
+  // p = 64 (2 (wave & 1) + t) + lane
+  int srow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int p = 64 * (2 * (wave & 1) + t) + lane;  // index 2 * row + group within the array
-    const int r = p >> 1;
-    const int rl = GU ? (r & (kGuCols - 1)) : r;
-    const bool up = GU && r >= kGuCols;
-    sb_rowvalid[t] = n0 + rl < nrows_w;
-    const uint16_t* arr = sb_arr ? (up ? up_b : gate_b) : (up ? up_s : gate_s);
-    sb_src[t] = arr + (mrow0 + (sb_rowvalid[t] ? rl : 0)) * (size_t)ldg + (p & 1);
+    const int r = PAIRED ? (64 * (wave & 1) + lane) : ((64 * (2 * (wave & 1) + t) + lane) >> 1);
+    srow[t] = GU ? (r & (kGuCols - 1)) : r;
   }
-  // ---- A rows: wave w loads rows 4 (w + 4 t) .. +3, lane j: row + (j >> 4), chunk slot j & 15
-  const uint8_t* arow[MT];
-  int achunk[MT];
+  // A: row 4 (wave + 4 t) + (lane >> 4), chunk slot lane & 15
+  const uint16_t* abase;
+  uint32_t aoff[MT], achk[MT];  // row offset, swizzled chunk offset within the step
+  if (GU) {
+    abase = a.x;
+  } else {
+    abase = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int r = 4 * (wave + 4 * t) + (lane >> 4);
     const int rr = min(r, rows - 1);
-    const uint16_t* rp;
+    int arow;
     if (GU) {
-      int tok = sh ? (row0 - a.P + rr) : a.sorted_token[row0 + rr];
-      tok = min(max(tok, 0), a.T - 1);
-      rp = a.x + (size_t)tok * d;
+      arow = sh ? (row0 - a.P + rr) : a.sorted_token[row0 + rr];
+      arow = min(max(arow, 0), a.T - 1);
     } else {
-      rp = (sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie) + (size_t)rr * Ie;
+      arow = rr;
     }
-    arow[t] = reinterpret_cast<const uint8_t*>(rp);
-    achunk[t] = 16 * ((lane & 15) ^ a_swz(r));
+    aoff[t] = (uint32_t)arow * (uint32_t)(2 * K);
+    achk[t] = 16u * (uint32_t)((lane & 15) ^ a_swz(r));
   }
-  const int amax = 2 * K - 16;  // last 16-byte chunk of a row
 
-  auto issue = [&](int s, int st) __attribute__((always_inline)) {
+  // issue the direct loads of pipeline position (job j, step s) into stage st
+  auto issue = [&](int j, int s, int st) __attribute__((always_inline)) {
+    const int n0 = (nb0 + j) * cols;
+    const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
+    const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
     uint8_t* cdst = L.c[st] + wave * 2048;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) dma16(cbase + coff[t] + min(64 * s + cq16[t], ldc - 16), cdst + 1024 * t);
-    uint32_t* sdst = L.sb[st] + sb_arr * 256 + 128 * (wave & 1);
+    const uint8_t* cb = wc + (mrow + n0) * (size_t)ldc + 64 * s;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int g = 2 * s + (lane & 1);
-      const bool ok = sb_rowvalid[t] && g < ldg;
-      dma2(ok ? (const void*)(sb_src[t] + 2 * s) : (const void*)kZeroHalf, sdst + 64 * t);
+      uint32_t q = cq16[t];
+      if (tail) q &= 16u;  // the missing half-step: re-read the step's first group
+      dma16(cb, (uint32_t)min(crow[t], lim) * (uint32_t)ldc + q, cdst + 1024 * t);
     }
+    if (PAIRED) {
+      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
+      dma4(sbb, (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg), L.sb[st] + 128 * (wave >> 1) + 64 * (wave & 1));
+    } else {
+      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) dma16(arow[t] + min(256 * s + achunk[t], amax), L.a[st] + 1024 * (wave + 4 * t));
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t g = tail ? 0u : (uint32_t)(lane & 1);
+        dma2(sbb, ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + g) * 2u,
+             L.sb[st] + 256 * (wave >> 1) + 128 * (wave & 1) + 64 * t);
+      }
+    }
+    const uint16_t* ab = abase + 128 * s;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint32_t ch = tail ? (achk[t] & 127u) : achk[t];  // chunks past K re-read the first half
+      dma16(ab, aoff[t] + ch, L.a[st] + 1024 * (wave + 4 * t));
+    }
   };
 
   const int n = lane & 15, kb = lane >> 4;
@@ -233,7 +274,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int n0, int e, int 
     for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
-  auto compute = [&](int st) __attribute__((always_inline)) {
+  auto compute = [&](int st, bool half) __attribute__((always_inline)) {
     const uint8_t* cs = L.c[st];
     const uint32_t* sb = L.sb[st];
     const uint8_t* as = L.a[st];
@@ -262,8 +303,21 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int n0, int e, int 
           xs[mm] = mfma16x16x32(raw, ones, kk == 0 ? z : xs[mm]);
         }
       }
-      const float s0 = bf16lo(sb[2 * wrow0 + gg]), c0 = fmaf(-128.0f, s0, bf16lo(sb[256 + 2 * wrow0 + gg]));
-      const float s1 = bf16lo(sb[2 * wrow1 + gg]), c1 = fmaf(-128.0f, s1, bf16lo(sb[256 + 2 * wrow1 + gg]));
+      float s0, b0v, s1, b1v;
+      if (PAIRED) {
+        const uint32_t sc0 = sb[wrow0], bi0 = sb[128 + wrow0], sc1 = sb[wrow1], bi1 = sb[128 + wrow1];
+        s0 = gg ? bf16hi(sc0) : bf16lo(sc0);
+        b0v = gg ? bf16hi(bi0) : bf16lo(bi0);
+        s1 = gg ? bf16hi(sc1) : bf16lo(sc1);
+        b1v = gg ? bf16hi(bi1) : bf16lo(bi1);
+      } else {
+        s0 = bf16lo(sb[2 * wrow0 + gg]);
+        b0v = bf16lo(sb[256 + 2 * wrow0 + gg]);
+        s1 = bf16lo(sb[2 * wrow1 + gg]);
+        b1v = bf16lo(sb[256 + 2 * wrow1 + gg]);
+        if (gg == 1 && half) s0 = b0v = s1 = b1v = 0.0f;  // the group past K adds nothing
+      }
+      const float c0 = fmaf(-128.0f, s0, b0v), c1 = fmaf(-128.0f, s1, b1v);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
@@ -274,81 +328,107 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, int n0, int e, int 
     }
   };
 
-  // Loads past the last step are issued anyway (clamped to it) so that every iteration issues
-  // the same sequence; their data lands in stages that are not read again.
-  constexpr int kOps = 2 + 2 + MT;  // loads one wave issues per step
-  const int Sm = S - 1;
-  issue(0, 0);
-  issue(min(1, Sm), 1);
-  issue(min(2, Sm), 2);
-  auto iter = [&](int s, int j) __attribute__((always_inline)) {
-    step_barrier<2 * kOps>();
-    issue(min(s + 3, Sm), (j + 3) & 3);
-    compute(j);
-  };
-  for (int s = 0; s < S; s += 4) {
-    iter(s, 0);
-    if (s + 1 < S) iter(s + 1, 1);
-    if (s + 2 < S) iter(s + 2, 2);
-    if (s + 3 < S) iter(s + 3, 3);
-  }
-  // the clamped loads past the end must land before the block (and its LDS) is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  if (GU) {
-    uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
-    const int col = n0 + 16 * wave + n;
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mm + 4 * kb + r;
-        if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
-      }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = n0 + 32 * wave + 16 * t + n;
-      if (col >= d) continue;
+  auto finish = [&](int j) __attribute__((always_inline)) {
+    const int n0 = (nb0 + j) * cols;
+    if (GU) {
+      uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
+      const int col = n0 + 16 * wave + n;
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * mm + 4 * kb + r;
-          if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
+          if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
         }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = n0 + 32 * wave + 16 * t + n;
+        if (col >= d) continue;
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mm + 4 * kb + r;
+            if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
+          }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // Positions past the end issue clamped re-loads of the last position (same sequence every
+  // iteration); their data lands in a stage that is not read again.
+  constexpr int kOps = 2 + (PAIRED ? 1 : 2) + MT;  // loads one wave issues per position
+  int ij = 0, is = 0;  // position being issued (job, step); stays at the last position
+  int cj = 0, cs = 0;  // position being computed
+  issue(0, 0, 0);
+  if (P > 1) {
+    ij = S > 1 ? 0 : 1;
+    is = S > 1 ? 1 : 0;
+  }
+  issue(ij, is, 1);
+  for (int p = 0; p < P; p += kStages) {
+#pragma unroll
+    for (int q = 0; q < kStages; ++q) {
+      if (q == 0 || p + q < P) {
+        step_barrier<kOps>();
+        if (ij < njobs - 1 || is < S - 1) {
+          if (++is == S) {
+            is = 0;
+            ++ij;
+          }
+        }
+        issue(ij, is, (q + 2) % kStages);
+        compute(q, !PAIRED && cs == S - 1 && (ldg & 1));
+        if (cs == S - 1) {
+          finish(cj);
+          cs = 0;
+          ++cj;
+        } else {
+          ++cs;
+        }
+      }
     }
   }
+  // the clamped loads past the end must land before the block (and its LDS) is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool GU>
+template <bool GU, bool PAIRED>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
-  __shared__ __attribute__((aligned(16))) uint8_t c0[kCodeStageBytes], c1[kCodeStageBytes], c2[kCodeStageBytes],
-      c3[kCodeStageBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t s0[kSbStageWords], s1[kSbStageWords], s2[kSbStageWords],
-      s3[kSbStageWords];
-  __shared__ __attribute__((aligned(16))) uint8_t a0[kAStageBytes], a1[kAStageBytes], a2[kAStageBytes],
-      a3[kAStageBytes];
-  const GemmLds L = {{c0, c1, c2, c3}, {s0, s1, s2, s3}, {a0, a1, a2, a3}};
-  int nb, e, row0, rows;
-  if (!block_tile(a, nb, e, row0, rows)) return;
-  const int n0 = nb * (GU ? kGuCols : kDnCols);
-  if (GU && n0 >= (e == a.E ? a.Is : a.I)) return;
+  __shared__ __attribute__((aligned(16))) uint8_t c0[kCodeStageBytes], c1[kCodeStageBytes], c2[kCodeStageBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s0[PAIRED ? 256 : 512], s1[PAIRED ? 256 : 512],
+      s2[PAIRED ? 256 : 512];
+  __shared__ __attribute__((aligned(16))) uint8_t a0[kAStageBytes], a1[kAStageBytes], a2[kAStageBytes];
+  const GemmLds L = {{c0, c1, c2}, {s0, s1, s2}, {a0, a1, a2}};
+  int run, e, row0, rows;
+  if (!block_tile(a, run, e, row0, rows)) return;
+  // the tile is the same for the whole block: keep it (and all that derives from it) scalar
+  run = __builtin_amdgcn_readfirstlane(run);
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    tile_body<1, GU>(a, n0, e, row0, rows, L);
+    run_body<1, GU, PAIRED>(a, run, e, row0, rows, L);
   else
-    tile_body<2, GU>(a, n0, e, row0, rows, L);
+    run_body<2, GU, PAIRED>(a, run, e, row0, rows, L);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gateup_gemm(GemmArgs a) {
-  gemm_block<true>(a);
+template <bool PAIRED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_gemm(GemmArgs a) {
+  gemm_block<true, PAIRED>(a);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_down_gemm(GemmArgs a) {
-  gemm_block<false>(a);
+template <bool PAIRED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_gemm(GemmArgs a) {
+  gemm_block<false, PAIRED>(a);
 }
 
-static GemmArgs gemm_args(const Ctx& c, int nb) {
+static GemmArgs gemm_args(const Ctx& c, int nruns) {
   GemmArgs a;
   a.d = c.d;
   a.E = c.E;
@@ -358,7 +438,7 @@ static GemmArgs gemm_args(const Ctx& c, int nb) {
   a.T = c.T;
   a.P = c.P;
   a.max_tiles = c.max_tiles;
-  a.nb = nb;
+  a.nb = nruns;
   a.x = c.x;
   a.sorted_token = c.r.sorted_token;
   a.tiles = c.r.tiles;
@@ -371,17 +451,29 @@ static GemmArgs gemm_args(const Ctx& c, int nb) {
   return a;
 }
 
-static int grid_blocks(int max_tiles, int nb) { return ((max_tiles * nb + 7) / 8) * 8; }
+static int grid_blocks(int max_tiles, int nruns) { return ((max_tiles * nruns + 7) / 8) * 8; }
 
 hipError_t launch_gateup_gemm(const Ctx& c) {
-  const int nb = (max(c.I, c.Is) + kGuCols - 1) / kGuCols;
-  hipLaunchKernelGGL(k_gateup_gemm, dim3(grid_blocks(c.max_tiles, nb)), dim3(256), 0, c.stream, gemm_args(c, nb));
+  const int ncb = (max(c.I, c.Is) + kGuCols - 1) / kGuCols;
+  const int nruns = (ncb + kRunGu - 1) / kRunGu;
+  const dim3 grid(grid_blocks(c.max_tiles, nruns));
+  if (c.d % kBK == 0)
+    hipLaunchKernelGGL(k_gateup_gemm<true>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  else
+    hipLaunchKernelGGL(k_gateup_gemm<false>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
   return hipGetLastError();
 }
 
 hipError_t launch_down_gemm(const Ctx& c) {
-  const int nb = (c.d + kDnCols - 1) / kDnCols;
-  hipLaunchKernelGGL(k_down_gemm, dim3(grid_blocks(c.max_tiles, nb)), dim3(256), 0, c.stream, gemm_args(c, nb));
+  const int ncb = (c.d + kDnCols - 1) / kDnCols;
+  const int nruns = (ncb + kRunDn - 1) / kRunDn;
+  const dim3 grid(grid_blocks(c.max_tiles, nruns));
+  // both the routed and the shared matrix must be whole steps for the paired form
+  const bool paired = c.I % kBK == 0 && (c.Is == 0 || c.Is % kBK == 0);
+  if (paired)
+    hipLaunchKernelGGL(k_down_gemm<true>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  else
+    hipLaunchKernelGGL(k_down_gemm<false>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
   return hipGetLastError();
 }
 
