@@ -82,10 +82,23 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Sum over the wave, the same value in every lane: DPP within rows of 16 lanes (swap
+// neighbours, swap pairs, rotate by 4, rotate by 8), then the four row sums of lanes 0, 16, 32
+// and 48 in that order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
@@ -103,10 +116,27 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
 }
 __device__ __forceinline__ int topk_key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((int)(uint32_t)v, m, 64);
-  uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+// Max of a 64-bit key over the wave, returned in every lane. Within each row of 16 lanes the
+// DPP moves (swap neighbours, swap pairs, rotate by 4, rotate by 8) leave the row maximum in
+// every lane; the four row maxima are then read as scalars.
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
   return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm 1,0,3,2
+  v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm 2,3,0,1
+  v = umax64(v, dpp_u64<0x124>(v));  // row_ror 4
+  v = umax64(v, dpp_u64<0x128>(v));  // row_ror 8
+  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)), umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 // One wave: top-k of logits lg[0..E) (E <= 64 * SLOTS, k <= 16) by (logit desc, index asc),
@@ -123,14 +153,10 @@ __device__ __forceinline__ void wave_topk_softmax_n(const float* lg, int E, int 
   int my_e = 0;
   float my_l = 0.0f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    uint64_t loc = key[0];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) best = key[s] > best ? key[s] : best;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
+    for (int s = 1; s < SLOTS; ++s) loc = umax64(loc, key[s]);
+    const uint64_t best = wave_max_u64(loc);
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s)
       if (key[s] == best) key[s] = 0ull;

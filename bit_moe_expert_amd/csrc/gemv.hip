@@ -259,11 +259,12 @@ hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
 // expert e_j, so the slot, its expert and its weight are wave-uniform. Slots are taken in
 // batches of kGdBatch whose loads are all in flight together. Each output is reduced inside
 // its 16 lanes: no atomics.
-constexpr int kGdOut = 16;   // outputs per block (4 waves x 4)
+constexpr int kGdWaves = 2;  // waves per block
+constexpr int kGdOut = 4 * kGdWaves;  // outputs per block (4 per wave)
 constexpr int kGdBatch = 9;  // slots per batch (k = 8 routed + the shared expert in one batch)
 
 template <int PIECES>  // 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
-__global__ __launch_bounds__(256) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
+__global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
                                                            const int32_t* __restrict__ ids,
                                                            const float* __restrict__ wts, GemvPtrs p,
                                                            const uint16_t* __restrict__ h,
@@ -382,8 +383,11 @@ __global__ __launch_bounds__(256) void k_gemv_down_combine(int d, int E, int k, 
       }
     }
   }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  // sum over the output's 16 lanes (a DPP row); lane 0 of the row holds it after the rotations
+  acc += dpp_f32<0xB1>(acc);
+  acc += dpp_f32<0x4E>(acc);
+  acc += dpp_f32<0x124>(acc);
+  acc += dpp_f32<0x128>(acc);
   if (ovalid && l16 == 0) y[o] = f32_to_bf16(acc);
 }
 
@@ -392,10 +396,10 @@ hipError_t launch_gemv_down_combine(const Ctx& c) {
   const size_t lds = (size_t)nseg * 16 * 4 + (size_t)nseg * 4;
   const int nblk = (c.d + kGdOut - 1) / kGdOut;
   if (c.I <= 512 && c.Is <= 512)
-    hipLaunchKernelGGL(k_gemv_down_combine<1>, dim3(nblk), dim3(256), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
+    hipLaunchKernelGGL(k_gemv_down_combine<1>, dim3(nblk), dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
                        c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
   else
-    hipLaunchKernelGGL(k_gemv_down_combine<2>, dim3(nblk), dim3(256), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
+    hipLaunchKernelGGL(k_gemv_down_combine<2>, dim3(nblk), dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
                        c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
   return hipGetLastError();
 }
