@@ -32,38 +32,59 @@ hipError_t launch_decode_topk(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill (T >= 2) logits: a block owns 8 tokens x 64 experts (lane = expert) and its 16 waves
-// split the 64-input chunks (wave w takes chunks w, w + 16, ...). A wave issues the 64 router
-// loads of its chunk before the fma chains (one per token, ascending inputs); the chunk partials
-// meet in LDS and one thread per (token, expert) adds them in chunk order, then the bias.
+// Prefill (T >= 2) logits: a block owns 8 tokens x 64 experts (lane = expert). The block first
+// stages the 8 tokens' inputs in LDS as fp32 [input][token] (every thread issues all of its
+// loads before converting any); its 16 waves then take the 64-input chunks w, w + 16, ...: a
+// wave loads the chunk's 64 router values of its expert and runs one fma chain per token over
+// ascending inputs. The chunk partials meet in LDS and one thread per (token, expert) adds them
+// in chunk order, then the bias. Up to kRpMaxD inputs are staged at once (larger d in passes).
 constexpr int kRpTok = 8;
 constexpr int kRpWaves = 16;
-constexpr int kRpPass = kRpWaves * kGroup;  // inputs staged per pass
+constexpr int kRpMaxD = 2048;                    // inputs staged per pass
+constexpr int kRpMaxChunks = kRpMaxD / kGroup;   // 32 chunks per pass
 
 __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, const uint16_t* __restrict__ x,
                                                          const float* __restrict__ wr, const float* __restrict__ bias,
                                                          float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) float s_x[kRpPass][kRpTok];       // 32 KB, [input][token]
-  __shared__ float s_parts[kRpWaves][kRpTok][64];                           // 32 KB
+  __shared__ __attribute__((aligned(16))) float s_x[kRpMaxD][kRpTok];           // 64 KB, [input][token]
+  __shared__ float s_parts[kRpMaxChunks][kRpTok][64];                           // 64 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * kRpTok;
   const int e = blockIdx.y * 64 + lane;
+  const int ec = e < E ? e : E - 1;  // experts past E compute a copy that is never stored
   const int nchunks = d / kGroup;
   const int s_tok = tid >> 6, s_e = blockIdx.y * 64 + lane;  // sum phase: threads 0..511
   float acc = 0.0f;
-  for (int p = 0; p < nchunks; p += kRpWaves) {
-    const int npass = min(kRpWaves, nchunks - p);
-    for (int idx = tid; idx < kRpPass * kRpTok; idx += 1024) {
-      const int tk = idx / kRpPass, i = idx % kRpPass;
-      float v = 0.0f;
-      if (t0 + tk < T && i < npass * kGroup) v = bf16_to_f32(x[(size_t)(t0 + tk) * d + p * kGroup + i]);
-      s_x[i][tk] = v;
+  for (int p = 0; p < nchunks; p += kRpMaxChunks) {
+    const int npass = min(kRpMaxChunks, nchunks - p);
+    const int nin = npass * kGroup;
+    // stage inputs p*64 .. p*64 + nin of the 8 tokens: thread i takes inputs i and i + 1024
+    constexpr int kH = kRpMaxD / 1024;
+    uint16_t v[kH][kRpTok];
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      const int i = tid + 1024 * h;
+      const int ic = i < nin ? i : 0;
+#pragma unroll
+      for (int tk = 0; tk < kRpTok; ++tk) {
+        const int t = min(t0 + tk, T - 1);
+        v[h][tk] = x[(size_t)t * d + (size_t)p * kGroup + ic];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      const int i = tid + 1024 * h;
+      if (i < nin) {
+        float4* dst = reinterpret_cast<float4*>(&s_x[i][0]);
+        dst[0] = make_float4(bf16_to_f32(v[h][0]), bf16_to_f32(v[h][1]), bf16_to_f32(v[h][2]), bf16_to_f32(v[h][3]));
+        dst[1] = make_float4(bf16_to_f32(v[h][4]), bf16_to_f32(v[h][5]), bf16_to_f32(v[h][6]), bf16_to_f32(v[h][7]));
+      }
     }
     __syncthreads();
-    if (wave < npass) {
-      const int c = p + wave;
+    for (int cc = wave; cc < npass; cc += kRpWaves) {
+      const int c = p + cc;
       float wv[kGroup];
-      const float* wp = wr + (size_t)c * kGroup * E + (e < E ? e : 0);
+      const float* wp = wr + (size_t)c * kGroup * E + ec;
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) wv[i] = wp[(size_t)i * E];
       float pr[kRpTok];
@@ -71,14 +92,14 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
       for (int tk = 0; tk < kRpTok; ++tk) pr[tk] = 0.0f;
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        const float4 xa = *reinterpret_cast<const float4*>(&s_x[wave * kGroup + i][0]);
-        const float4 xb = *reinterpret_cast<const float4*>(&s_x[wave * kGroup + i][4]);
+        const float4 xa = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][0]);
+        const float4 xb = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][4]);
         const float xs[kRpTok] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
         for (int tk = 0; tk < kRpTok; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
       }
 #pragma unroll
-      for (int tk = 0; tk < kRpTok; ++tk) s_parts[wave][tk][lane] = pr[tk];
+      for (int tk = 0; tk < kRpTok; ++tk) s_parts[cc][tk][lane] = pr[tk];
     }
     __syncthreads();
     if (tid < kRpTok * 64)
