@@ -108,63 +108,61 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// Order-preserving key: larger logit first, then lower expert index. Key 0 means "empty".
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+// Order-preserving 32-bit key of a logit: a larger logit gives a larger key; -0 is first turned
+// into +0 so that equal logits give equal keys. Key 0 means "empty" (no finite logit maps to 0).
+__device__ __forceinline__ uint32_t topk_key(float v) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ int topk_key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-// Max of a 64-bit key over the wave, returned in every lane. Within each row of 16 lanes the
-// DPP moves (swap neighbours, swap pairs, rotate by 4, rotate by 8) leave the row maximum in
-// every lane; the four row maxima are then read as scalars.
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// Max of a 32-bit value over the wave, returned uniform: DPP steps within each row of 16 lanes
+// (swap neighbours, swap pairs, rotate by 4, rotate by 8) leave the row maximum in every lane;
+// the four row maxima are then read as scalars.
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm 1,0,3,2
-  v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm 2,3,0,1
-  v = umax64(v, dpp_u64<0x124>(v));  // row_ror 4
-  v = umax64(v, dpp_u64<0x128>(v));  // row_ror 8
-  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)), umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm 1,0,3,2
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm 2,3,0,1
+  v = max(v, dpp_u32<0x124>(v));  // row_ror 4
+  v = max(v, dpp_u32<0x128>(v));  // row_ror 8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 // One wave: top-k of logits lg[0..E) (E <= 64 * SLOTS, k <= 16) by (logit desc, index asc),
-// then the softmax over the chosen logits. Lane j < k writes slot j. Call with a whole wave.
+// then the softmax over the chosen logits. Lane l holds experts l + 64 s. Each round takes the
+// largest key over the wave, then the lowest expert index holding it (ballots over the slots in
+// ascending order, lowest lane first). Lane j < k writes slot j. Call with a whole wave.
 template <int SLOTS>
 __device__ __forceinline__ void wave_topk_softmax_n(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
   const int lane = (int)lane_id();
-  uint64_t key[SLOTS];
+  uint32_t key[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     const int e = lane + 64 * s;
-    key[s] = e < E ? topk_key(lg[e], e) : 0ull;
+    key[s] = e < E ? topk_key(lg[e]) : 0u;
   }
   int my_e = 0;
-  float my_l = 0.0f;
   for (int j = 0; j < k; ++j) {
-    uint64_t loc = key[0];
+    uint32_t loc = key[0];
 #pragma unroll
-    for (int s = 1; s < SLOTS; ++s) loc = umax64(loc, key[s]);
-    const uint64_t best = wave_max_u64(loc);
+    for (int s = 1; s < SLOTS; ++s) loc = max(loc, key[s]);
+    const uint32_t best = wave_max_u32(loc);
+    int win = -1;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const uint64_t m = __ballot(key[s] == best);
+      if (win < 0 && m != 0) win = 64 * s + (int)__builtin_ctzll(m);
+    }
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s)
-      if (key[s] == best) key[s] = 0ull;
-    if (lane == j) {
-      my_e = topk_key_index(best);
-      my_l = lg[my_e];
-    }
+      if (lane + 64 * s == win) key[s] = 0u;
+    if (lane == j) my_e = win;
   }
+  const float my_l = lane < k ? lg[my_e] : 0.0f;
   const float top = __shfl(my_l, 0, 64);
   const float ex = lane < k ? expf(my_l - top) : 0.0f;
   const float sum = wave_sum(ex);

@@ -143,9 +143,9 @@ hipError_t launch_topk_prefill(const Ctx& c) {
 // Wave w owns the contiguous pair range [w*span, (w+1)*span). Pass 1 counts per wave and
 // expert in LDS (atomics only for counts). A scan over experts gives offsets; a scan over waves
 // per expert gives each wave's first row in every group. Pass 2 walks the range again in steps
-// of 64 pairs: lanes with the same expert find each other with 10 ballots (one per bit of the
-// expert id), so a lane's rank is the popcount of its lower peers; the lowest peer advances the
-// wave's cursor. Rows of an expert therefore follow pair order, i.e. ascending token.
+// of 64 pairs: lanes with the same expert find each other with one ballot per bit of the expert
+// id, so a lane's rank is the popcount of its lower peers; the lowest peer advances the wave's
+// cursor. Rows of an expert therefore follow pair order, i.e. ascending token.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int incl = v;
@@ -174,6 +174,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
   return r;
 }
 
+constexpr int kMetaBatch = 8;  // pairs per lane whose ids are loaded together
+
 __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared,
                                                      const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
@@ -183,13 +185,21 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
   __shared__ int s_wsum[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
-  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&s_tab[0][0])[i] = 0;
+  for (int i = tid; i < 16 * E; i += 1024) s_tab[i / E][i % E] = 0;
   __syncthreads();
   const int span = (((P + 15) / 16) + 63) & ~63;
   const int p_begin = min(P, wave * span), p_end = min(P, p_begin + span);
-  for (int p = p_begin + lane; p < p_end; p += 64) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&s_tab[wave][e], 1);
+  // the wave's pairs in batches of kMetaBatch per lane, every load of a batch in flight at once
+  for (int base = p_begin; base < p_end; base += 64 * kMetaBatch) {
+    int ev[kMetaBatch];
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i) {
+      const int p = base + lane + 64 * i;
+      ev[i] = p < p_end ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i)
+      if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&s_tab[wave][ev[i]], 1);
   }
   __syncthreads();
   int cnt = 0;
@@ -228,26 +238,35 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
   if (tid == 0) *n_tiles = n_routed + n_shared;
   __syncthreads();
   // pass 2: stable ranks
-  for (int base = p_begin; base < p_end; base += 64) {
-    const int p = base + lane;
-    const bool act = p < p_end;
-    int e = act ? ids[p] : 0;
-    const bool valid = act && (unsigned)e < (unsigned)E;
-    uint64_t peers = __ballot(valid);
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
+  for (int base = p_begin; base < p_end; base += 64 * kMetaBatch) {
+    int ev[kMetaBatch];
 #pragma unroll
-    for (int b = 0; b < 10; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(valid && bit);
-      peers &= bit ? bb : ~bb;
+    for (int i = 0; i < kMetaBatch; ++i) {
+      const int p = base + lane + 64 * i;
+      ev[i] = p < p_end ? ids[p] : -1;
     }
-    int pos = 0;
-    if (valid) pos = s_tab[wave][e] + __popcll(peers & lanemask_lt());
-    __builtin_amdgcn_wave_barrier();
-    if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      sorted_token[pos] = p / k;
-      inv_pos[p] = pos;
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i) {
+      if (base + 64 * i >= p_end) break;  // wave-uniform
+      const int p = base + lane + 64 * i;
+      const int e = ev[i];
+      const bool valid = (unsigned)e < (unsigned)E;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(valid && bit);
+        peers &= bit ? bb : ~bb;
+      }
+      int pos = 0;
+      if (valid) pos = s_tab[wave][e] + __popcll(peers & lanemask_lt());
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        sorted_token[pos] = p / k;
+        inv_pos[p] = pos;
+      }
     }
   }
 }
