@@ -44,11 +44,17 @@ DESCR = {
     "prefill": "prefill: T=512, d=2048, 256 experts top-8 + shared, I=I_s=512, int4 g64, 4 layers cycled",
     "long": "long: T=4096 as 4 chunks of 1024 (one layer each), Zipf logit bias, d=2048, 256 experts top-8 + shared, I=512",
     "diffusion": "diffusion: T=256 canvas x 30 layers, d=2048, 128 experts top-8, I=768, no shared expert",
+    "m2": "small-M: T=2, decode shapes, 40 layers cycled",
+    "m4": "small-M: T=4, decode shapes, 40 layers cycled",
+    "m8": "small-M: T=8, decode shapes, 40 layers cycled",
+    "m16": "small-M: T=16, decode shapes, 40 layers cycled",
 }
 # layers held on the GPU and calls per step
-PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "diffusion": (30, 30)}
+PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "diffusion": (30, 30),
+        "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40)}
 DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gateup_gemm", "long": "gateup_gemm",
-            "diffusion": "gateup_gemm"}
+            "diffusion": "gateup_gemm", "m2": "gemv_gateup_topk", "m4": "gemv_gateup_topk",
+            "m8": "gemv_gateup_topk", "m16": "gateup_gemm"}
 STAGE_SOURCE = {"router_decode": "route.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
                 "topk_prefill": "route.hip",
@@ -92,23 +98,25 @@ def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
     P = T * k
     act = int((counts > 0).sum())
     per_w = lambda out, inn: out * inn // 2 + 2 * 2 * out * inn // 64  # noqa: E731  codes + scales + biases
-    if name == "router_decode":  # router partials + the shared expert's gate/up rows
-        return 4 * d * E + 2 * T * d + 4 * (d // 64) * E + (2 * per_w(Is, d) + 2 * Is if Is else 0), \
-            2 * T * d * E + 4 * d * Is
+    if name == "router_decode":  # router partials (one plane per token) + the shared expert's gate/up rows
+        return 4 * d * E + 2 * T * d + 4 * T * (d // 64) * E + (2 * per_w(Is, d) + 2 * T * Is if Is else 0), \
+            2 * T * d * E + 4 * d * Is * T
     if name == "router_prefill":  # router weights, x, logits out
         return 4 * d * E + 2 * T * d + 4 * T * E, 2 * T * d * E
     if name == "topk_prefill":
         return 4 * T * E + 8 * P, 0
     if name == "decode_topk":
-        return 4 * (d // 64) * E + 8 * k, 0
+        return 4 * T * (d // 64) * E + 8 * P, 0
     if name == "gemv_gateup_topk":  # routed slots only; reads the router partials
-        return 2 * k * per_w(I, d) + 2 * d + 2 * k * I + 4 * (d // 64) * E, 4 * d * k * I
+        return 2 * act * per_w(I, d) + 2 * T * d + 2 * P * I + 4 * T * (d // 64) * E, 4 * d * P * I
     if name == "route_meta":
         return 4 * P * 3 + 4 * (2 * E + 1), 0
     if name == "gemv_gateup":
-        return 2 * (k * per_w(I, d) + (per_w(Is, d) if Is else 0)) + 2 * d + 2 * (k * I + Is), 4 * d * (k * I + Is)
+        return 2 * (act * per_w(I, d) + (per_w(Is, d) if Is else 0)) + 2 * T * d + 2 * (P * I + T * Is), \
+            4 * d * (P * I + T * Is)
     if name == "gemv_down_combine":
-        return (k * per_w(d, I) + (per_w(d, Is) if Is else 0)) + 2 * (k * I + Is) + 2 * d, 2 * d * (k * I + Is)
+        return (act * per_w(d, I) + (per_w(d, Is) if Is else 0)) + 2 * (P * I + T * Is) + 2 * T * d, \
+            2 * d * (P * I + T * Is)
     if name == "gateup_gemm":
         wb = 2 * (act * per_w(I, d) + (per_w(Is, d) if Is else 0))
         return wb + 2 * T * d + 2 * (P * I + T * Is), 4 * d * (P * I + T * Is)
@@ -300,6 +308,9 @@ def main() -> int:
 
     # ---- roofline of the dominant kernel
     dom = DOMINANT[args.workload]
+    if dom not in stages:
+        log(f"dominant stage {dom} is not on this call's path; stages: {list(stages)}")
+        return 1
     st = stages[dom]
     bound = "hbm"
     if args.workload == "long":

@@ -1,5 +1,7 @@
-// Batch-1 decode: bandwidth-bound grouped GEMV over the k selected experts plus the shared
-// expert, on the vector ALUs, with 128-bit loads of the 4-bit codes.
+// Decode and other small calls (T <= kGemvMaxT tokens): bandwidth-bound GEMV over each token's
+// k selected experts plus the shared expert, on the vector ALUs, with 128-bit loads of the
+// 4-bit codes. A wave works for one token; an expert chosen by several tokens is read once per
+// token (the repeats mostly hit L2), so no grouping step is needed.
 //
 // Decode has no weight reuse, so the aim is to move as few bytes per token as possible and to
 // keep the arithmetic below the memory time ("Perplexity's Lily Beats MLX-LM on MacBook M5.
@@ -152,11 +154,13 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode router: chunk partials of the logits (see route.hip for the fixed order) and, when the
-// shared expert's weights are given, its gate/up rows in the same launch (they do not depend on
-// the routing, so they overlap the router's reads). Blocks [0, n_part) hold one (chunk, 64
-// experts) item per wave; the blocks after them hold kGvRows shared h entries per wave.
-__global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int Is, int n_part_blocks,
+// Router of T <= kGemvMaxT tokens: chunk partials of the logits (see route.hip for the fixed
+// order) and, when the shared expert's weights are given, its gate/up rows in the same launch
+// (they do not depend on the routing, so they overlap the router's reads). Blocks
+// [0, n_part) hold one (chunk, 64 experts) item per wave: the wave loads the chunk's router
+// values once and runs one fma chain per token. The blocks after them hold kGvRows shared h
+// entries of one token per wave.
+__global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int Is, int T, int n_part_blocks,
                                                                  const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr,
                                                                  float* __restrict__ parts, GemvPtrs p,
@@ -170,39 +174,44 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, i
     const int e = (item / nchunks) * 64 + (threadIdx.x & 63);
     if (e >= E) return;
     const float* wp = wr + (size_t)c * kGroup * E + e;
-    const uint16_t* xp = x + c * kGroup;
     float v[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
-    float part = 0.0f;
+    for (int t = 0; t < T; ++t) {
+      const uint16_t* xp = x + (size_t)t * d + c * kGroup;
+      float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) part = fmaf(bf16_to_f32(xp[i]), v[i], part);
-    parts[(size_t)c * E + e] = part;
+      for (int i = 0; i < kGroup; ++i) part = fmaf(bf16_to_f32(xp[i]), v[i], part);
+      parts[((size_t)t * nchunks + c) * E + e] = part;
+    }
     return;
   }
-  const int i0 = uniform(((blockIdx.x - n_part_blocks) * kGvWaves + wave) * kGvRows);
-  if (i0 >= Is) return;
-  gateup_wave(d, (size_t)i0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x, hs + i0);
+  const int r0 = uniform(((blockIdx.x - n_part_blocks) * kGvWaves + wave) * kGvRows);
+  if (r0 >= T * Is) return;
+  const int t = r0 / Is, i0 = r0 - t * Is;
+  gateup_wave(d, (size_t)i0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x + (size_t)t * d, hs + (size_t)t * Is + i0);
 }
 
 hipError_t launch_router_decode(const Ctx& c) {
   const bool with_shared = c.Is > 0 && c.shared.gate.codes != nullptr;
   const int items = (c.d / kGroup) * ((c.E + 63) / 64);
   const int n_part = (items + kGvWaves - 1) / kGvWaves;
-  const int n_shared = with_shared ? (c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
+  const int n_shared = with_shared ? (c.T * c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
   hipLaunchKernelGGL(k_router_decode, dim3(n_part + n_shared), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E,
-                     with_shared ? c.Is : 0, n_part, c.x, c.w_router, c.router_parts, gemv_ptrs(c), c.hs);
+                     with_shared ? c.Is : 0, c.T, n_part, c.x, c.w_router, c.router_parts, gemv_ptrs(c), c.hs);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
-// h[j][i] for the k routed slots (e_j = topk_ids[j]) and, if include_shared, the shared slot.
-// FUSED_TOPK: every block first sums the router's chunk partials (in chunk order) and takes the
-// top-k itself, so no kernel boundary or atomic sits between the router and the experts' reads;
-// all blocks reach bit-identical choices, and block 0 publishes them for the down kernel.
+// h[t][j][i] for token t's k routed slots (e_j = topk_ids[t][j]) and, if include_shared, its
+// shared slot. Blocks are laid out token by token.
+// FUSED_TOPK: every block first sums its token's router chunk partials (in chunk order) and
+// takes the top-k itself, so no kernel boundary or atomic sits between the router and the
+// experts' reads; all blocks of a token reach bit-identical choices, and the token's first
+// block publishes them for the down kernel.
 template <bool FUSED_TOPK>
 __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int k, int I, int Is, int include_shared,
-                                                               const uint16_t* __restrict__ x,
+                                                               int blocks_per_token, const uint16_t* __restrict__ x,
                                                                const float* __restrict__ parts,
                                                                const float* __restrict__ bias, int32_t* __restrict__ ids,
                                                                float* __restrict__ wts, GemvPtrs p,
@@ -210,17 +219,19 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
   __shared__ int s_ids[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
   __shared__ float s_lg[FUSED_TOPK ? kMaxExperts : 1];
+  const int t = uniform(blockIdx.x / blocks_per_token), tb = uniform(blockIdx.x - t * blocks_per_token);
   if (FUSED_TOPK) {
-    sum_chunk_partials(parts, bias, d / kGroup, E, s_lg);
+    const int nchunks = d / kGroup;
+    sum_chunk_partials(parts + (size_t)t * nchunks * E, bias, nchunks, E, s_lg);
     __syncthreads();
     if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, s_ids, s_w);
     __syncthreads();
-    if (blockIdx.x == 0 && (int)threadIdx.x < k) {
-      ids[threadIdx.x] = s_ids[threadIdx.x];
-      wts[threadIdx.x] = s_w[threadIdx.x];
+    if (tb == 0 && (int)threadIdx.x < k) {
+      ids[(size_t)t * k + threadIdx.x] = s_ids[threadIdx.x];
+      wts[(size_t)t * k + threadIdx.x] = s_w[threadIdx.x];
     }
   }
-  const int r0 = uniform((blockIdx.x * kGvWaves + (threadIdx.x >> 6)) * kGvRows);
+  const int r0 = uniform((tb * kGvWaves + (threadIdx.x >> 6)) * kGvRows);
   const int total = k * I + (include_shared ? Is : 0);
   if (r0 >= total) return;
   const bool routed = r0 < k * I;
@@ -229,31 +240,33 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
   const int Ie = routed ? I : Is;
   int mat = 0;
   if (routed) {
-    mat = FUSED_TOPK ? s_ids[j] : ids[j];
+    mat = FUSED_TOPK ? s_ids[j] : ids[(size_t)t * k + j];
     if ((unsigned)mat >= (unsigned)E) mat = 0;  // a corrupt routing must not read out of bounds
   }
   gateup_wave(d, (size_t)mat * Ie + i0, routed ? p.gc : p.sgc, routed ? p.gs : p.sgs, routed ? p.gb : p.sgb,
-              routed ? p.uc : p.suc, routed ? p.us : p.sus, routed ? p.ub : p.sub, x,
-              routed ? h + (size_t)j * I + i0 : hs + i0);
+              routed ? p.uc : p.suc, routed ? p.us : p.sus, routed ? p.ub : p.sub, x + (size_t)t * d,
+              routed ? h + ((size_t)t * k + j) * I + i0 : hs + (size_t)t * Is + i0);
 }
 
 hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
   const int include_shared = fused_topk ? 0 : (c.Is > 0 ? 1 : 0);
   const int waves = (c.k * c.I + (include_shared ? c.Is : 0)) / kGvRows;
-  const int nblk = (waves + kGvWaves - 1) / kGvWaves;
+  const int bpt = (waves + kGvWaves - 1) / kGvWaves;  // blocks per token
+  const dim3 grid(bpt * c.T);
   if (fused_topk)
-    hipLaunchKernelGGL(k_gemv_gateup<true>, dim3(nblk), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
+    hipLaunchKernelGGL(k_gemv_gateup<true>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
+                       include_shared, bpt, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
                        c.h, c.hs);
   else
-    hipLaunchKernelGGL(k_gemv_gateup<false>, dim3(nblk), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
+    hipLaunchKernelGGL(k_gemv_gateup<false>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
+                       include_shared, bpt, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
                        c.h, c.hs);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
-// y[o] = bf16( sum_j w_j * (h_j . Wd[e_j][o]) + h_s . Wd_s[o] ). A block keeps every slot's h
+// y[t][o] = bf16( sum_j w_tj * (h_tj . Wd[e_tj][o]) + h_ts . Wd_s[o] ), token t = blockIdx.y.
+// A block keeps every slot's h
 // in LDS (re-paired) with per-segment sums. A wave owns 4 outputs (16 lanes each) and walks the
 // slots in step: at slot j every lane takes 16-byte pieces l16, l16 + 16, ... of row o of
 // expert e_j, so the slot, its expert and its weight are wave-uniform. Slots are taken in
@@ -270,6 +283,12 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
                                                            const uint16_t* __restrict__ h,
                                                            const uint16_t* __restrict__ hs, uint16_t* __restrict__ y) {
   extern __shared__ uint32_t s_h[];  // nseg * 16 dwords of re-paired h, then nseg sums
+  const int tok = blockIdx.y;        // this block's token
+  ids += (size_t)tok * k;
+  wts += (size_t)tok * k;
+  h += (size_t)tok * k * I;
+  hs += (size_t)tok * Is;
+  y += (size_t)tok * d;
   const int S = I / 32, Ss = Is / 32;
   const int nslot = k + (Is > 0 ? 1 : 0);
   const int nseg = k * S + Ss;
@@ -394,12 +413,12 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
 hipError_t launch_gemv_down_combine(const Ctx& c) {
   const int nseg = c.k * (c.I / 32) + c.Is / 32;
   const size_t lds = (size_t)nseg * 16 * 4 + (size_t)nseg * 4;
-  const int nblk = (c.d + kGdOut - 1) / kGdOut;
+  const dim3 grid((c.d + kGdOut - 1) / kGdOut, c.T);
   if (c.I <= 512 && c.Is <= 512)
-    hipLaunchKernelGGL(k_gemv_down_combine<1>, dim3(nblk), dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
+    hipLaunchKernelGGL(k_gemv_down_combine<1>, grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
                        c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
   else
-    hipLaunchKernelGGL(k_gemv_down_combine<2>, dim3(nblk), dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
+    hipLaunchKernelGGL(k_gemv_down_combine<2>, grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
                        c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
   return hipGetLastError();
 }

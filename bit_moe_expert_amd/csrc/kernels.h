@@ -18,7 +18,7 @@ struct Ctx {
   moe_ffn_q4 routed;
   moe_ffn_q4 shared;  // all-null when Is == 0
   moe_routing r;      // routing arrays (caller's or carved from the workspace)
-  float* router_parts;    // [d/64][E] decode router chunk partials
+  float* router_parts;    // [T][d/64][E] router chunk partials (GEMV path, T <= kGemvMaxT)
   float* logits;          // [T][E] router logits (T >= 2)
   uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1)
   uint16_t* hs;           // [T][Is] bf16
@@ -27,7 +27,8 @@ struct Ctx {
   hipStream_t stream;
 };
 
-// decode router chunk partials (+ the shared expert's gate/up rows when its weights are set)
+// router chunk partials of T <= kGemvMaxT tokens (+ the shared expert's gate/up rows when its
+// weights are set)
 hipError_t launch_router_decode(const Ctx& c);
 hipError_t launch_decode_topk(const Ctx& c);
 hipError_t launch_router_prefill(const Ctx& c);  // logits [T][E]
@@ -45,7 +46,9 @@ hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* o
 // Block-map tile height (rows of one expert group per tile).
 constexpr int kTileRows = 32;
 
-// The GEMV decode path keeps all selected experts' h in LDS: (k*I + Is) bf16 values.
+// Calls of up to kGemvMaxT tokens take the GEMV path (one token per wave, no grouping).
+constexpr int kGemvMaxT = 8;
+// The GEMV path's down kernel keeps a token's selected experts' h in LDS: (k*I + Is) bf16 values.
 constexpr int kGemvMaxH = 28672;
 // ... and its down kernel keeps two 16-lane rounds of 32-input pieces per row in registers.
 constexpr int kGemvMaxFF = 1024;

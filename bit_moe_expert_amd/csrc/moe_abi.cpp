@@ -53,13 +53,17 @@ int32_t max_tiles_of(const moe_dims& dm, int32_t T) {
   return (int32_t)t;
 }
 
+// Calls of up to kGemvMaxT tokens route through chunk partials (one per token) ...
+bool small_call(int32_t T) { return T >= 1 && T <= kGemvMaxT; }
+
+// ... and, when a token's h fits the down kernel, run the expert FFN on the GEMV path.
 bool gemv_path(const moe_dims& dm, int32_t T) {
-  return T == 1 && dm.top_k * dm.d_ff + dm.d_ff_shared <= kGemvMaxH && dm.d_ff <= kGemvMaxFF &&
+  return small_call(T) && dm.top_k * dm.d_ff + dm.d_ff_shared <= kGemvMaxH && dm.d_ff <= kGemvMaxFF &&
          dm.d_ff_shared <= kGemvMaxFF;
 }
 
 bool gemv_path_ctx(const Ctx& c) {
-  return c.T == 1 && c.k * c.I + c.Is <= kGemvMaxH && c.I <= kGemvMaxFF && c.Is <= kGemvMaxFF;
+  return small_call(c.T) && c.k * c.I + c.Is <= kGemvMaxH && c.I <= kGemvMaxFF && c.Is <= kGemvMaxFF;
 }
 
 struct Layout {
@@ -71,7 +75,7 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   const size_t P = (size_t)T * dm.top_k, E = dm.n_experts, d = dm.d_model;
   size_t o = 0;
   L.parts = o;
-  o += up(d / 64 * E * 4);
+  o += up((size_t)std::min<int32_t>(T, kGemvMaxT) * (d / 64) * E * 4);
   L.logits = o;
   o += up((size_t)T * E * 4);
   L.ids = o;
@@ -137,13 +141,13 @@ int check_ws(const moe_dims& dm, int32_t T, void* ws, size_t ws_bytes) {
 
 enum Stage {
   kRouterDecode,      // chunk partials of the logits (+ shared expert gate/up when its weights are set)
-  kDecodeTopk,        // partials -> top-k (moe_route at T == 1)
+  kDecodeTopk,        // partials -> top-k (moe_route at T <= kGemvMaxT)
   kRouterPrefill,     // logits for T >= 2
   kTopkPrefill,       // logits -> top-k for T >= 2
   kMeta,              // histogram, scan, scatter, block map
-  kGemvGateupTopk,    // decode gate/up of the routed slots, top-k fused in
-  kGemvGateup,        // decode gate/up from given routing, shared slot included
-  kGemvDown,          // decode down + weighted combine + shared
+  kGemvGateupTopk,    // GEMV gate/up of the routed slots, top-k fused in
+  kGemvGateup,        // GEMV gate/up from given routing, shared slot included
+  kGemvDown,          // GEMV down + weighted combine + shared
   kGemmGateup,
   kGemmDown,
   kCombine
@@ -159,7 +163,7 @@ int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
     out[n++] = kGemvDown;
     return n;
   }
-  if (T == 1) {
+  if (small_call(T)) {
     out[n++] = kRouterDecode;
     out[n++] = kDecodeTopk;
   } else {
@@ -294,7 +298,7 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
   c.w_router = w_router;
   c.logit_bias = logit_bias;
   c.r = *out;
-  if (T == 1) {
+  if (small_call(T)) {
     if (int rc = run_stage(kRouterDecode, c, false)) return rc;
     if (int rc = run_stage(kDecodeTopk, c, false)) return rc;
   } else {

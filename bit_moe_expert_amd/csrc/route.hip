@@ -14,19 +14,20 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// Decode (T == 1) top-k for moe_route: one block adds the decode router's chunk partials in
+// Top-k of T <= kGemvMaxT tokens for moe_route: block t adds token t's router chunk partials in
 // chunk order and takes the top-k. (moe_forward_layer fuses this step into its gate/up kernel.)
 __global__ __launch_bounds__(256) void k_decode_topk(int d, int E, int k, const float* __restrict__ parts,
                                                      const float* __restrict__ bias, int32_t* __restrict__ ids,
                                                      float* __restrict__ w) {
   __shared__ float s_lg[kMaxExperts];
-  sum_chunk_partials(parts, bias, d / kGroup, E, s_lg);
+  const int t = blockIdx.x, nchunks = d / kGroup;
+  sum_chunk_partials(parts + (size_t)t * nchunks * E, bias, nchunks, E, s_lg);
   __syncthreads();
-  if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, ids, w);
+  if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 hipError_t launch_decode_topk(const Ctx& c) {
-  hipLaunchKernelGGL(k_decode_topk, dim3(1), dim3(256), 0, c.stream, c.d, c.E, c.k, c.router_parts, c.logit_bias,
+  hipLaunchKernelGGL(k_decode_topk, dim3(c.T), dim3(256), 0, c.stream, c.d, c.E, c.k, c.router_parts, c.logit_bias,
                      c.r.topk_ids, c.r.topk_w);
   return hipGetLastError();
 }

@@ -144,24 +144,25 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
 /*
  * Expert FFN of routed tokens given their routing (as written by moe_route):
  *   y[t] = bf16( sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]) + FFN_shared(x[t]) ),
- *   FFN_e(x) = h Wd_e^T with h = bf16( silu(x Wg_e^T) * (x Wu_e^T) ), weights dequantised to
- *   bf16 on chip and never written out, fp32 accumulation.
- * T >= 2 runs the grouped GEMM path (uses every routing array); T == 1 runs the decode GEMV
- * path (uses topk_ids and topk_w only). `shared` must be NULL iff d_ff_shared == 0.
+ *   FFN_e(x) = h Wd_e^T with h = bf16( silu(x Wg_e^T) * (x Wu_e^T) ), each weight taken as
+ *   scale * code + bias inside the dot products (never expanded in memory), fp32 accumulation.
+ * Calls of 1..8 tokens run the GEMV path (uses topk_ids and topk_w only) when
+ * top_k * d_ff + d_ff_shared <= 28672 and d_ff, d_ff_shared <= 1024; other calls run the grouped
+ * GEMM path (uses every routing array). `shared` must be NULL iff d_ff_shared == 0.
  */
 int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_routing* routing,
                    const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y, void* ws,
                    size_t ws_bytes, void* stream);
 
-/* moe_route followed by moe_expert_ffn, with the routing arrays carved from `ws`. At T == 1
- * the block-map steps are skipped (the GEMV path does not read them), the top-k is taken
- * inside the gate/up kernel, and only topk_ids/topk_w of the carved routing are written. */
+/* moe_route followed by moe_expert_ffn, with the routing arrays carved from `ws`. On the GEMV
+ * path the block-map steps are skipped (it does not read them), the top-k is taken inside the
+ * gate/up kernel, and only topk_ids/topk_w of the carved routing are written. */
 int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
                       const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared,
                       uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Check export: dequantise `rows` rows of length in_dim (rows counts all matrices) to bf16
- * bits out_bf16 [rows][in_dim], with the same device routine the grouped GEMM uses. */
+ * bits out_bf16 [rows][in_dim]: w = bf16(fp32(scale * code + bias)), round to nearest even. */
 int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream);
 
 /* Profiling: moe_forward_layer runs moe_num_stages() kernels in sequence for this T; stage s

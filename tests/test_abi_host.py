@@ -44,6 +44,8 @@ def test_sizing_helpers():
     assert ws % 256 == 0 and ws >= (4096 + 512) * 2048 * 4 + 4096 * 512 * 2
     assert moe.workspace_bytes(d, 0) > 0
     assert moe.workspace_bytes(_dims(g=32), 8) == 0
+    # the router's chunk partials hold one [d/64][E] plane per token of a small call
+    assert moe.workspace_bytes(d, 8) - moe.workspace_bytes(d, 7) >= (2048 // 64) * 256 * 4
     assert moe.max_tiles(_dims(k=17), 8) == -1
 
 
@@ -60,6 +62,12 @@ def test_stage_lists():
     big = _dims(k=16, I=2048)  # too much h for the GEMV path: T = 1 runs the grouped GEMM
     assert [L.moe_stage_name(ctypes.byref(big), 1, s).decode() for s in range(L.moe_num_stages(ctypes.byref(big), 1))] \
         == ["router_decode", "decode_topk", "route_meta", "gateup_gemm", "down_gemm", "combine"]
+    # calls of up to 8 tokens take the GEMV path; 9 tokens and up the grouped GEMM
+    for T in (2, 5, 8):
+        assert [L.moe_stage_name(ctypes.byref(d), T, s).decode() for s in range(L.moe_num_stages(ctypes.byref(d), T))] \
+            == ["router_decode", "gemv_gateup_topk", "gemv_down_combine"], T
+    assert L.moe_stage_name(ctypes.byref(d), 9, 0).decode() == "router_prefill"
+    assert L.moe_num_stages(ctypes.byref(d), 9) == 6
 
 
 class _Fake:

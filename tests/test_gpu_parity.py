@@ -60,7 +60,8 @@ def test_dequant_bit_exact_workload_and_exhaustive_scales():
 
 # ------------------------------------------------------------------ routing (bit-exact)
 ROUTE_CASES = [("tiny", 0, 0), ("decode", 0, 0), ("decode", 17, 0), ("decode", 39, 0), ("prefill", 0, 0),
-               ("long", 0, 0), ("long", 0, 3), ("diffusion", 0, 0), ("diffusion", 29, 0)]
+               ("long", 0, 0), ("long", 0, 3), ("diffusion", 0, 0), ("diffusion", 29, 0), ("m2", 0, 0),
+               ("m8", 3, 0), ("m16", 39, 0)]
 
 
 @pytest.mark.parametrize("name,layer,chunk", ROUTE_CASES)
@@ -148,6 +149,12 @@ def test_forward_diffusion(layer):
     _forward_check(gen.WORKLOADS["diffusion"], layer=layer)
 
 
+@pytest.mark.parametrize("name,layer", [("m2", 0), ("m2", 39), ("m4", 7), ("m8", 0), ("m8", 39), ("m16", 11)])
+def test_forward_small_calls(name, layer):
+    """2..8 tokens run the GEMV path (a token per wave), 16 the grouped GEMM."""
+    _forward_check(gen.WORKLOADS[name], layer=layer)
+
+
 SHAPES = [
     # (T, d, E, k, I, Is): ragged T, K tails (d or I = 64 mod 128), shared size != routed, no shared
     (1, 256, 16, 4, 128, 128), (1, 192, 8, 2, 192, 64), (2, 256, 16, 4, 128, 128), (3, 192, 4, 2, 192, 0),
@@ -169,7 +176,7 @@ def test_decode_falls_back_to_grouped_gemm_when_h_is_large():
 
 
 # ------------------------------------------------------------------ composition and determinism
-@pytest.mark.parametrize("name", ["prefill", "decode"])
+@pytest.mark.parametrize("name", ["prefill", "decode", "m4", "m8"])
 def test_route_then_expert_ffn_equals_forward_and_is_deterministic(name):
     w = gen.WORKLOADS[name]
     L = gen.layer(w, 0)
