@@ -56,6 +56,12 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 // Stop the compiler from sinking the loads above below this point.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+// ... and from hoisting any arithmetic above it either: every load above is issued before the
+// first instruction below (the scheduler may otherwise interleave them to save registers).
+__device__ __forceinline__ void issue_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 struct GemvPtrs {
   const uint8_t *gc, *uc, *dc;       // routed gate/up/down codes
@@ -157,9 +163,10 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
 // Router of T <= kGemvMaxT tokens: chunk partials of the logits (see route.hip for the fixed
 // order) and, when the shared expert's weights are given, its gate/up rows in the same launch
 // (they do not depend on the routing, so they overlap the router's reads). Blocks
-// [0, n_part) hold one (chunk, 64 experts) item per wave: the wave loads the chunk's router
-// values once and runs one fma chain per token. The blocks after them hold kGvRows shared h
-// entries of one token per wave.
+// [0, n_part) hold one (chunk, 64 experts) item each: wave w loads the chunk's router values
+// and the inputs of tokens w and w + kGvWaves, all before the first use, and runs the two
+// tokens' fma chains interleaved. The blocks after them hold kGvRows shared h entries of one
+// token per wave.
 __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int Is, int T, int n_part_blocks,
                                                                  const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr,
@@ -167,23 +174,48 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, i
                                                                  uint16_t* __restrict__ hs) {
   const int wave = uniform(threadIdx.x >> 6);
   if ((int)blockIdx.x < n_part_blocks) {
+    // block = one (chunk, 64 experts) item; wave w takes tokens w and w + kGvWaves (lane = expert)
     const int nchunks = d / kGroup;
-    const int item = uniform(blockIdx.x * kGvWaves + wave);
-    if (item >= nchunks * ((E + 63) / 64)) return;
+    const int item = blockIdx.x;
     const int c = item % nchunks;
     const int e = (item / nchunks) * 64 + (threadIdx.x & 63);
-    if (e >= E) return;
+    const int ta = wave, tb = wave + kGvWaves;
+    if (ta >= T || e >= E) return;
+    const int tb2 = tb < T ? tb : ta;  // without a second token the second chain repeats the first
     const float* wp = wr + (size_t)c * kGroup * E + e;
     float v[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
-    for (int t = 0; t < T; ++t) {
-      const uint16_t* xp = x + (size_t)t * d + c * kGroup;
-      float part = 0.0f;
+    // the chunk's 64 inputs of both tokens (8 x 16 bytes each), all in flight with the weights;
+    // a zero the compiler cannot see through keeps them vector loads (scalar loads return out
+    // of order, so their uses would wait for all of them at once, in several rounds)
+    int vz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+    const uint4* xa = reinterpret_cast<const uint4*>(x + (size_t)ta * d + c * kGroup) + vz;
+    const uint4* xb = reinterpret_cast<const uint4*>(x + (size_t)tb2 * d + c * kGroup) + vz;
+    uint4 ua[kGroup / 8], ub[kGroup / 8];
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) part = fmaf(bf16_to_f32(xp[i]), v[i], part);
-      parts[((size_t)t * nchunks + c) * E + e] = part;
+    for (int q = 0; q < kGroup / 8; ++q) {
+      ua[q] = xa[q];
+      ub[q] = xb[q];
     }
+    issue_all();
+    // two independent chains, each over ascending inputs from +0
+    float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kGroup / 8; ++q) {
+      const uint32_t wa[4] = {ua[q].x, ua[q].y, ua[q].z, ua[q].w};
+      const uint32_t wb[4] = {ub[q].x, ub[q].y, ub[q].z, ub[q].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        pa = fmaf(bf16lo(wa[m]), v[8 * q + 2 * m], pa);
+        pb = fmaf(bf16lo(wb[m]), v[8 * q + 2 * m], pb);
+        pa = fmaf(bf16hi(wa[m]), v[8 * q + 2 * m + 1], pa);
+        pb = fmaf(bf16hi(wb[m]), v[8 * q + 2 * m + 1], pb);
+      }
+    }
+    parts[((size_t)ta * nchunks + c) * E + e] = pa;
+    parts[((size_t)tb2 * nchunks + c) * E + e] = pb;  // same value as pa when tb2 == ta
     return;
   }
   const int r0 = uniform(((blockIdx.x - n_part_blocks) * kGvWaves + wave) * kGvRows);
@@ -194,8 +226,8 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, i
 
 hipError_t launch_router_decode(const Ctx& c) {
   const bool with_shared = c.Is > 0 && c.shared.gate.codes != nullptr;
-  const int items = (c.d / kGroup) * ((c.E + 63) / 64);
-  const int n_part = (items + kGvWaves - 1) / kGvWaves;
+  static_assert(kGemvMaxT <= 2 * kGvWaves, "router partials: two tokens per wave");
+  const int n_part = (c.d / kGroup) * ((c.E + 63) / 64);  // one (chunk, 64 experts) item per block
   const int n_shared = with_shared ? (c.T * c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
   hipLaunchKernelGGL(k_router_decode, dim3(n_part + n_shared), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E,
                      with_shared ? c.Is : 0, c.T, n_part, c.x, c.w_router, c.router_parts, gemv_ptrs(c), c.hs);
