@@ -63,6 +63,19 @@ __device__ __forceinline__ uint32_t magic_pair(uint32_t w, int n) {
   return ((w >> (4 * n)) & 0x000F000Fu) | 0x43004300u;
 }
 
+// All four magic_pair(w, n), n = 0..3, in 7 operations: the low and high nibbles of every byte
+// (lo = inputs 0, 2, 4, 6 and hi = inputs 1, 3, 5, 7, one per byte), then byte permutes that
+// put each code under a 0x43 high byte: pair (n, n + 4) takes bytes (0, 2) of lo or hi for
+// n = 0, 1 and bytes (1, 3) for n = 2, 3.
+__device__ __forceinline__ void magic_pairs4(uint32_t w, uint32_t p[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  p[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04020400u);
+  p[1] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04020400u);
+  p[2] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030401u);
+  p[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u);
+}
+
 // Re-pair 8 bf16 values (4 dwords in natural order) to match magic_pair: pair n = (v[n], v[n+4]).
 __device__ __forceinline__ void repair8(const uint32_t v[4], uint32_t p[4]) {
   p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
@@ -183,21 +196,35 @@ __device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k,
     wave_topk_softmax_n<16>(lg, E, k, ids_out, w_out);
 }
 
-// Router logits of one token from its chunk partials parts[c][e] (c = 0 .. nchunks-1): the
-// partials are added in ascending chunk order to +0, then the bias. Threads of the block take
-// experts tid, tid + blockDim.x, ...; results go to lg[e]. Every load of a thread's 32-chunk
-// batch is issued before the adds.
+// Router logits of one token from its chunk partials parts[e][c] (c = 0 .. nchunks-1, each
+// expert's partials contiguous): the partials are added in ascending chunk order to +0, then the
+// bias. Threads of the block take experts tid, tid + blockDim.x, ...; results go to lg[e]. A
+// thread issues every load of a 32-chunk batch (16-byte loads when nchunks % 4 == 0) before
+// the adds.
 __device__ __forceinline__ void sum_chunk_partials(const float* __restrict__ parts, const float* __restrict__ bias,
                                                    int nchunks, int E, float* lg) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const float* pe = parts + (size_t)e * nchunks;
     float acc = 0.0f;
-    for (int cb = 0; cb < nchunks; cb += 32) {
-      float v[32];
+    if ((nchunks & 3) == 0) {
+      for (int cb = 0; cb < nchunks; cb += 32) {
+        f32x4_t v[8];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = cb + i < nchunks ? parts[(size_t)(cb + i) * E + e] : 0.0f;
+        for (int q = 0; q < 8; ++q)
+          v[q] = cb + 4 * q < nchunks ? reinterpret_cast<const f32x4_t*>(pe + cb)[q] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (cb + i < nchunks) acc = acc + v[i];
+        for (int q = 0; q < 8; ++q)
+          if (cb + 4 * q < nchunks) acc = (((acc + v[q].x) + v[q].y) + v[q].z) + v[q].w;
+      }
+    } else {
+      for (int cb = 0; cb < nchunks; cb += 32) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = cb + i < nchunks ? pe[cb + i] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (cb + i < nchunks) acc = acc + v[i];
+      }
     }
     if (bias) acc = acc + bias[e];
     lg[e] = acc;

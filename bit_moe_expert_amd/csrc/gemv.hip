@@ -46,9 +46,12 @@ __device__ __forceinline__ float seg_dot(const uint4& cw, const Seg32& a) {
   const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
   float acc = 0.0f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 4; ++m) {
+    uint32_t q[4];
+    magic_pairs4(w[m], q);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc = dot2_bf16(magic_pair(w[m], n), a.p[4 * m + n], acc);
+    for (int n = 0; n < 4; ++n) acc = dot2_bf16(q[n], a.p[4 * m + n], acc);
+  }
   return acc;
 }
 
@@ -214,8 +217,8 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, i
         pb = fmaf(bf16hi(wb[m]), v[8 * q + 2 * m + 1], pb);
       }
     }
-    parts[((size_t)ta * nchunks + c) * E + e] = pa;
-    parts[((size_t)tb2 * nchunks + c) * E + e] = pb;  // same value as pa when tb2 == ta
+    parts[((size_t)ta * E + e) * nchunks + c] = pa;
+    parts[((size_t)tb2 * E + e) * nchunks + c] = pb;  // same value as pa when tb2 == ta
     return;
   }
   const int r0 = uniform(((blockIdx.x - n_part_blocks) * kGvWaves + wave) * kGvRows);
@@ -235,6 +238,64 @@ hipError_t launch_router_decode(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Pipelined variant of gateup_wave for d <= 2048 (one 32-input segment per lane, lanes past the
+// segments idle): the caller holds the lane's x segment (re-paired once per token) and passes
+// the loads of the next rows while these rows are computed.
+struct GuLoads {
+  uint4 cw[2 * kGvRows];      // gate rows, then up rows: 16 bytes of codes each
+  uint32_t sb[2 * kGvRows];   // scale | bias << 16 of the segment's group
+};
+
+struct GuRows {
+  const uint8_t *gc, *uc;
+  const uint16_t *gs, *gb, *us, *ub;
+  size_t row0;
+  uint16_t* hout;
+};
+
+__device__ __forceinline__ void gu_load(const GuRows& g, int d, int seg, GuLoads& L) {
+  const size_t cstride = (size_t)d / 2, sstride = (size_t)d / kGroup;
+#pragma unroll
+  for (int r = 0; r < 2 * kGvRows; ++r) {
+    const size_t row = g.row0 + (r % kGvRows);
+    L.cw[r] = *reinterpret_cast<const uint4*>((r < kGvRows ? g.gc : g.uc) + row * cstride + (size_t)seg * 16);
+  }
+#pragma unroll
+  for (int r = 0; r < 2 * kGvRows; ++r) {
+    const size_t row = g.row0 + (r % kGvRows);
+    L.sb[r] = (uint32_t)(r < kGvRows ? g.gs : g.us)[row * sstride + seg / 2] |
+              ((uint32_t)(r < kGvRows ? g.gb : g.ub)[row * sstride + seg / 2] << 16);
+  }
+}
+
+__device__ __forceinline__ void gu_finish(const GuLoads& L, const Seg32& a, bool active, uint16_t* hout) {
+  const int lane = threadIdx.x & 63;
+  float acc[2 * kGvRows];
+#pragma unroll
+  for (int r = 0; r < 2 * kGvRows; ++r) {
+    const float s = bf16lo(L.sb[r]), b = bf16hi(L.sb[r]);
+    const float pd = seg_dot(L.cw[r], a);
+    // the same operations, in the same order, as one segment of gateup_wave
+    const float v = fmaf(fmaf(-128.0f, s, b), a.sum, fmaf(s, pd, 0.0f));
+    acc[r] = active ? v : 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < 2 * kGvRows; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane < kGvRows / 2) {
+    float hv[kGvRows];
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r) hv[r] = silu_mul(acc[r], acc[kGvRows + r]);
+    float a0 = hv[0], a1 = hv[1];
+#pragma unroll
+    for (int q = 1; q < kGvRows / 2; ++q)
+      if (lane == q) {
+        a0 = hv[2 * q];
+        a1 = hv[2 * q + 1];
+      }
+    reinterpret_cast<uint32_t*>(hout)[lane] = pack_bf16x2(a0, a1);
+  }
+}
+
 // h[t][j][i] for token t's k routed slots (e_j = topk_ids[t][j]) and, if include_shared, its
 // shared slot. Blocks are laid out token by token.
 // FUSED_TOPK: every block first sums its token's router chunk partials (in chunk order) and
@@ -243,7 +304,8 @@ hipError_t launch_router_decode(const Ctx& c) {
 // block publishes them for the down kernel.
 template <bool FUSED_TOPK>
 __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int k, int I, int Is, int include_shared,
-                                                               int blocks_per_token, const uint16_t* __restrict__ x,
+                                                               int groups_per_token, int reps,
+                                                               const uint16_t* __restrict__ x,
                                                                const float* __restrict__ parts,
                                                                const float* __restrict__ bias, int32_t* __restrict__ ids,
                                                                float* __restrict__ wts, GemvPtrs p,
@@ -251,48 +313,101 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
   __shared__ int s_ids[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
   __shared__ float s_lg[FUSED_TOPK ? kMaxExperts : 1];
-  const int t = uniform(blockIdx.x / blocks_per_token), tb = uniform(blockIdx.x - t * blocks_per_token);
+  const int bpt = (groups_per_token + reps - 1) / reps;  // blocks per token
+  const int t = uniform(blockIdx.x / bpt), tb0 = uniform(blockIdx.x - t * bpt);
   if (FUSED_TOPK) {
     const int nchunks = d / kGroup;
     sum_chunk_partials(parts + (size_t)t * nchunks * E, bias, nchunks, E, s_lg);
     __syncthreads();
     if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, s_ids, s_w);
     __syncthreads();
-    if (tb == 0 && (int)threadIdx.x < k) {
+    if (tb0 == 0 && (int)threadIdx.x < k) {
       ids[(size_t)t * k + threadIdx.x] = s_ids[threadIdx.x];
       wts[(size_t)t * k + threadIdx.x] = s_w[threadIdx.x];
     }
   }
-  const int r0 = uniform((tb * kGvWaves + (threadIdx.x >> 6)) * kGvRows);
   const int total = k * I + (include_shared ? Is : 0);
-  if (r0 >= total) return;
-  const bool routed = r0 < k * I;
-  const int j = routed ? r0 / I : k;
-  const int i0 = routed ? r0 - j * I : r0 - k * I;
-  const int Ie = routed ? I : Is;
-  int mat = 0;
-  if (routed) {
-    mat = FUSED_TOPK ? s_ids[j] : ids[(size_t)t * k + j];
-    if ((unsigned)mat >= (unsigned)E) mat = 0;  // a corrupt routing must not read out of bounds
+  const int wave = threadIdx.x >> 6;
+  // rows of pass `rep` of this wave; false past the end
+  auto rows_of = [&](int rep, GuRows& g) -> bool {
+    const int tb = tb0 * reps + rep;  // this pass's group of kGvWaves * kGvRows rows
+    const int r0 = uniform((tb * kGvWaves + wave) * kGvRows);
+    if (rep >= reps || r0 >= total) return false;
+    const bool routed = r0 < k * I;
+    const int j = routed ? r0 / I : k;
+    const int i0 = routed ? r0 - j * I : r0 - k * I;
+    int mat = 0;
+    if (routed) {
+      mat = FUSED_TOPK ? s_ids[j] : ids[(size_t)t * k + j];
+      if ((unsigned)mat >= (unsigned)E) mat = 0;  // a corrupt routing must not read out of bounds
+    }
+    g.gc = routed ? p.gc : p.sgc;
+    g.uc = routed ? p.uc : p.suc;
+    g.gs = routed ? p.gs : p.sgs;
+    g.gb = routed ? p.gb : p.sgb;
+    g.us = routed ? p.us : p.sus;
+    g.ub = routed ? p.ub : p.sub;
+    g.row0 = (size_t)mat * (routed ? I : Is) + i0;
+    g.hout = routed ? h + ((size_t)t * k + j) * I + i0 : hs + (size_t)t * Is + i0;
+    return true;
+  };
+  if (d > 64 * 32) {  // several segments per lane: one pass at a time
+    for (int rep = 0; rep < reps; ++rep) {
+      GuRows g;
+      if (!rows_of(rep, g)) break;
+      gateup_wave(d, g.row0, g.gc, g.gs, g.gb, g.uc, g.us, g.ub, x + (size_t)t * d, g.hout);
+    }
+    return;
   }
-  gateup_wave(d, (size_t)mat * Ie + i0, routed ? p.gc : p.sgc, routed ? p.gs : p.sgs, routed ? p.gb : p.sgb,
-              routed ? p.uc : p.suc, routed ? p.us : p.sus, routed ? p.ub : p.sub, x + (size_t)t * d,
-              routed ? h + ((size_t)t * k + j) * I + i0 : hs + (size_t)t * Is + i0);
+  const int lane = threadIdx.x & 63;
+  const bool active = lane < d / 32;
+  const int seg = active ? lane : 0;
+  GuRows g;
+  if (!rows_of(0, g)) return;
+  GuLoads cur;
+  gu_load(g, d, seg, cur);
+  uint32_t xv[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = reinterpret_cast<const uint4*>(x + (size_t)t * d + (size_t)seg * 32)[q];
+    xv[4 * q] = v.x;
+    xv[4 * q + 1] = v.y;
+    xv[4 * q + 2] = v.z;
+    xv[4 * q + 3] = v.w;
+  }
+  issue_fence();
+  Seg32 a;
+  make_seg(xv, a);
+  for (int rep = 0;; ++rep) {
+    GuRows gn;
+    const bool more = rows_of(rep + 1, gn);
+    GuLoads nxt;
+    if (more) gu_load(gn, d, seg, nxt);
+    issue_fence();
+    gu_finish(cur, a, active, g.hout);
+    if (!more) break;
+    cur = nxt;
+    g = gn;
+  }
 }
 
+// Blocks take reps consecutive row groups of one token, so that a call keeps about 512 blocks
+// whatever T, all resident at once: the top-k prologue is paid once per block rather than in
+// several rounds of blocks, and a wave's next rows load while its current rows are computed.
 hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
   const int include_shared = fused_topk ? 0 : (c.Is > 0 ? 1 : 0);
   const int waves = (c.k * c.I + (include_shared ? c.Is : 0)) / kGvRows;
-  const int bpt = (waves + kGvWaves - 1) / kGvWaves;  // blocks per token
-  const dim3 grid(bpt * c.T);
+  const int groups = (waves + kGvWaves - 1) / kGvWaves;  // row groups per token
+  const int reps = (groups * c.T + 511) / 512;
+  const dim3 grid(((groups + reps - 1) / reps) * c.T);
   if (fused_topk)
     hipLaunchKernelGGL(k_gemv_gateup<true>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, bpt, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
-                       c.h, c.hs);
+                       include_shared, groups, reps, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
+                       gemv_ptrs(c), c.h, c.hs);
   else
     hipLaunchKernelGGL(k_gemv_gateup<false>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, bpt, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
-                       c.h, c.hs);
+                       include_shared, groups, reps, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
+                       gemv_ptrs(c), c.h, c.hs);
   return hipGetLastError();
 }
 
@@ -303,13 +418,13 @@ hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
 // slots in step: at slot j every lane takes 16-byte pieces l16, l16 + 16, ... of row o of
 // expert e_j, so the slot, its expert and its weight are wave-uniform. Slots are taken in
 // batches of kGdBatch whose loads are all in flight together. Each output is reduced inside
-// its 16 lanes: no atomics.
-constexpr int kGdWaves = 2;  // waves per block
-constexpr int kGdOut = 4 * kGdWaves;  // outputs per block (4 per wave)
+// its 16 lanes: no atomics. WAVES waves per block (4 * WAVES outputs): two for a single token
+// (more blocks to spread one token's rows), four for more tokens (each block stages a token's h
+// in one round).
 constexpr int kGdBatch = 9;  // slots per batch (k = 8 routed + the shared expert in one batch)
 
-template <int PIECES>  // 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
-__global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
+template <int PIECES, int WAVES>  // PIECES: 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
                                                            const int32_t* __restrict__ ids,
                                                            const float* __restrict__ wts, GemvPtrs p,
                                                            const uint16_t* __restrict__ h,
@@ -326,7 +441,7 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
   const int nseg = k * S + Ss;
   float* s_sum = reinterpret_cast<float*>(s_h + (size_t)nseg * 16);
   const int lane = threadIdx.x & 63, l16 = lane & 15;
-  const int o = blockIdx.x * kGdOut + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  const int o = blockIdx.x * (4 * WAVES) + (threadIdx.x >> 6) * 4 + (lane >> 4);
   const bool ovalid = o < d;
   const int orow = ovalid ? o : 0;
   // every routed slot's expert and weight with one load per wave; slots read them by lane
@@ -341,7 +456,12 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
     const int gs0 = stage ? g0 : 0;
     const uint32_t* src0 = gs0 < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)gs0 * 16
                                        : reinterpret_cast<const uint32_t*>(hs) + (size_t)(gs0 - k * S) * 16;
-    uint32_t hv[16];
+    // ... and its second one (segments past 2 * blockDim.x are loaded in step 3)
+    const int g1 = g0 + (int)blockDim.x;
+    const int gs1 = (j0 == 0) && g1 < nseg ? g1 : 0;
+    const uint32_t* src1 = gs1 < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)gs1 * 16
+                                       : reinterpret_cast<const uint32_t*>(hs) + (size_t)(gs1 - k * S) * 16;
+    uint32_t hv[16], hv1[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 t = reinterpret_cast<const uint4*>(src0)[q];
@@ -349,6 +469,11 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
       hv[4 * q + 1] = t.y;
       hv[4 * q + 2] = t.z;
       hv[4 * q + 3] = t.w;
+      const uint4 t1 = reinterpret_cast<const uint4*>(src1)[q];
+      hv1[4 * q] = t1.x;
+      hv1[4 * q + 1] = t1.y;
+      hv1[4 * q + 2] = t1.z;
+      hv1[4 * q + 3] = t1.w;
     }
     // 2. the batch's code pieces, scales and biases: every load unconditional, addresses clamped
     uint4 cw[kGdBatch * PIECES];
@@ -381,8 +506,12 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
     issue_fence();
     // 3. stage h into LDS (first batch only)
     if (j0 == 0) {
-      for (int g = g0; g < nseg; g += blockDim.x) {
-        if (g != g0) {
+      for (int g = g0, r = 0; g < nseg; g += blockDim.x, ++r) {
+        if (r == 1) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) hv[q] = hv1[q];
+        }
+        if (r >= 2) {
           const uint32_t* src = g < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)g * 16
                                           : reinterpret_cast<const uint32_t*>(hs) + (size_t)(g - k * S) * 16;
 #pragma unroll
@@ -442,16 +571,28 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
   if (ovalid && l16 == 0) y[o] = f32_to_bf16(acc);
 }
 
+template <int PIECES, int WAVES>
+static void launch_down(const Ctx& c, size_t lds) {
+  const dim3 grid((c.d + 4 * WAVES - 1) / (4 * WAVES), c.T);
+  hipLaunchKernelGGL((k_gemv_down_combine<PIECES, WAVES>), grid, dim3(WAVES * 64), lds, c.stream, c.d, c.E, c.k, c.I,
+                     c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
+}
+
 hipError_t launch_gemv_down_combine(const Ctx& c) {
   const int nseg = c.k * (c.I / 32) + c.Is / 32;
   const size_t lds = (size_t)nseg * 16 * 4 + (size_t)nseg * 4;
-  const dim3 grid((c.d + kGdOut - 1) / kGdOut, c.T);
-  if (c.I <= 512 && c.Is <= 512)
-    hipLaunchKernelGGL(k_gemv_down_combine<1>, grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
-  else
-    hipLaunchKernelGGL(k_gemv_down_combine<2>, grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
+  const bool small = c.I <= 512 && c.Is <= 512;
+  if (c.T == 1) {
+    if (small)
+      launch_down<1, 2>(c, lds);
+    else
+      launch_down<2, 2>(c, lds);
+  } else {
+    if (small)
+      launch_down<1, 4>(c, lds);
+    else
+      launch_down<2, 4>(c, lds);
+  }
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ struct Ctx {
   moe_ffn_q4 routed;
   moe_ffn_q4 shared;  // all-null when Is == 0
   moe_routing r;      // routing arrays (caller's or carved from the workspace)
-  float* router_parts;    // [T][d/64][E] router chunk partials (GEMV path, T <= kGemvMaxT)
+  float* router_parts;    // [T][E][d/64] router chunk partials (GEMV path, T <= kGemvMaxT)
   float* logits;          // [T][E] router logits (T >= 2)
   uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1)
   uint16_t* hs;           // [T][Is] bf16
