@@ -98,17 +98,17 @@ def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
     P = T * k
     act = int((counts > 0).sum())
     per_w = lambda out, inn: out * inn // 2 + 2 * 2 * out * inn // 64  # noqa: E731  codes + scales + biases
-    if name == "router_decode":  # router partials (one plane per token) + the shared expert's gate/up rows
-        return 4 * d * E + 2 * T * d + 4 * T * (d // 64) * E + (2 * per_w(Is, d) + 2 * T * Is if Is else 0), \
-            2 * T * d * E + 4 * d * Is * T
+    if name == "router_decode":  # router weights, x, chunk partials out (one plane per token)
+        return 4 * d * E + 2 * T * d + 4 * T * (d // 64) * E, 2 * T * d * E
     if name == "router_prefill":  # router weights, x, logits out
         return 4 * d * E + 2 * T * d + 4 * T * E, 2 * T * d * E
     if name == "topk_prefill":
         return 4 * T * E + 8 * P, 0
     if name == "decode_topk":
         return 4 * T * (d // 64) * E + 8 * P, 0
-    if name == "gemv_gateup_topk":  # routed slots only; reads the router partials
-        return 2 * act * per_w(I, d) + 2 * T * d + 2 * P * I + 4 * T * (d // 64) * E, 4 * d * P * I
+    if name == "gemv_gateup_topk":  # reads the router partials; routed slots + the shared expert's rows
+        return 2 * act * per_w(I, d) + 2 * T * d + 2 * P * I + 4 * T * (d // 64) * E + \
+            (2 * per_w(Is, d) + 2 * T * Is if Is else 0), 4 * d * (P * I + T * Is)
     if name == "route_meta":
         return 4 * P * 3 + 4 * (2 * E + 1), 0
     if name == "gemv_gateup":

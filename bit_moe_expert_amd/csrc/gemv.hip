@@ -164,20 +164,14 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
 
 // ---------------------------------------------------------------------------------------------
 // Router of T <= kGemvMaxT tokens: chunk partials of the logits (see route.hip for the fixed
-// order) and, when the shared expert's weights are given, its gate/up rows in the same launch
-// (they do not depend on the routing, so they overlap the router's reads). Blocks
-// [0, n_part) hold one (chunk, 64 experts) item each: wave w loads the chunk's router values
-// and the inputs of tokens w and w + kGvWaves, all before the first use, and runs the two
-// tokens' fma chains interleaved. The blocks after them hold kGvRows shared h entries of one
-// token per wave.
-__global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int Is, int T, int n_part_blocks,
-                                                                 const uint16_t* __restrict__ x,
+// order), stored [T][E][d/64]. A block holds one (chunk, 64 experts) item: wave w loads the
+// chunk's router values and the inputs of tokens w and w + kGvWaves, all before the first use,
+// and runs the two tokens' fma chains interleaved (lane = expert).
+__global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int T, const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr,
-                                                                 float* __restrict__ parts, GemvPtrs p,
-                                                                 uint16_t* __restrict__ hs) {
+                                                                 float* __restrict__ parts) {
   const int wave = uniform(threadIdx.x >> 6);
-  if ((int)blockIdx.x < n_part_blocks) {
-    // block = one (chunk, 64 experts) item; wave w takes tokens w and w + kGvWaves (lane = expert)
+  {
     const int nchunks = d / kGroup;
     const int item = blockIdx.x;
     const int c = item % nchunks;
@@ -219,21 +213,14 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, i
     }
     parts[((size_t)ta * E + e) * nchunks + c] = pa;
     parts[((size_t)tb2 * E + e) * nchunks + c] = pb;  // same value as pa when tb2 == ta
-    return;
   }
-  const int r0 = uniform(((blockIdx.x - n_part_blocks) * kGvWaves + wave) * kGvRows);
-  if (r0 >= T * Is) return;
-  const int t = r0 / Is, i0 = r0 - t * Is;
-  gateup_wave(d, (size_t)i0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x + (size_t)t * d, hs + (size_t)t * Is + i0);
 }
 
 hipError_t launch_router_decode(const Ctx& c) {
-  const bool with_shared = c.Is > 0 && c.shared.gate.codes != nullptr;
   static_assert(kGemvMaxT <= 2 * kGvWaves, "router partials: two tokens per wave");
   const int n_part = (c.d / kGroup) * ((c.E + 63) / 64);  // one (chunk, 64 experts) item per block
-  const int n_shared = with_shared ? (c.T * c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
-  hipLaunchKernelGGL(k_router_decode, dim3(n_part + n_shared), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E,
-                     with_shared ? c.Is : 0, c.T, n_part, c.x, c.w_router, c.router_parts, gemv_ptrs(c), c.hs);
+  hipLaunchKernelGGL(k_router_decode, dim3(n_part), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.T, c.x, c.w_router,
+                     c.router_parts);
   return hipGetLastError();
 }
 
@@ -301,10 +288,12 @@ __device__ __forceinline__ void gu_finish(const GuLoads& L, const Seg32& a, bool
 // FUSED_TOPK: every block first sums its token's router chunk partials (in chunk order) and
 // takes the top-k itself, so no kernel boundary or atomic sits between the router and the
 // experts' reads; all blocks of a token reach bit-identical choices, and the token's first
-// block publishes them for the down kernel.
+// block publishes them for the down kernel. The launch starts with n_sh blocks of the shared
+// expert's rows (n_sh / T per token), which need no routing and start loading at once, while
+// the routed blocks take the top-k.
 template <bool FUSED_TOPK>
 __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int k, int I, int Is, int include_shared,
-                                                               int groups_per_token, int reps,
+                                                               int groups_per_token, int reps, int sh_bpt, int n_tok,
                                                                const uint16_t* __restrict__ x,
                                                                const float* __restrict__ parts,
                                                                const float* __restrict__ bias, int32_t* __restrict__ ids,
@@ -313,8 +302,18 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
   __shared__ int s_ids[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
   __shared__ float s_lg[FUSED_TOPK ? kMaxExperts : 1];
+  const int wave = threadIdx.x >> 6;
+  const int n_sh = FUSED_TOPK ? sh_bpt * n_tok : 0;
+  if ((int)blockIdx.x < n_sh) {  // shared expert rows: kGvRows per wave
+    const int t = uniform(blockIdx.x / sh_bpt), sb = uniform(blockIdx.x - t * sh_bpt);
+    const int r0 = uniform((sb * kGvWaves + wave) * kGvRows);
+    if (r0 >= Is) return;
+    gateup_wave(d, (size_t)r0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x + (size_t)t * d, hs + (size_t)t * Is + r0);
+    return;
+  }
+  const int bid = (int)blockIdx.x - (FUSED_TOPK ? n_sh : 0);
   const int bpt = (groups_per_token + reps - 1) / reps;  // blocks per token
-  const int t = uniform(blockIdx.x / bpt), tb0 = uniform(blockIdx.x - t * bpt);
+  const int t = uniform(bid / bpt), tb0 = uniform(bid - t * bpt);
   if (FUSED_TOPK) {
     const int nchunks = d / kGroup;
     sum_chunk_partials(parts + (size_t)t * nchunks * E, bias, nchunks, E, s_lg);
@@ -327,7 +326,6 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
     }
   }
   const int total = k * I + (include_shared ? Is : 0);
-  const int wave = threadIdx.x >> 6;
   // rows of pass `rep` of this wave; false past the end
   auto rows_of = [&](int rep, GuRows& g) -> bool {
     const int tb = tb0 * reps + rep;  // this pass's group of kGvWaves * kGvRows rows
@@ -399,14 +397,17 @@ hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
   const int waves = (c.k * c.I + (include_shared ? c.Is : 0)) / kGvRows;
   const int groups = (waves + kGvWaves - 1) / kGvWaves;  // row groups per token
   const int reps = (groups * c.T + 511) / 512;
-  const dim3 grid(((groups + reps - 1) / reps) * c.T);
+  // the fused launch also computes the shared expert's h (its own leading blocks)
+  const bool with_shared = fused_topk && c.Is > 0 && c.shared.gate.codes != nullptr;
+  const int sh_bpt = with_shared ? (c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
+  const dim3 grid(((groups + reps - 1) / reps) * c.T + (fused_topk ? sh_bpt * c.T : 0));
   if (fused_topk)
     hipLaunchKernelGGL(k_gemv_gateup<true>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, groups, reps, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
+                       include_shared, groups, reps, sh_bpt, c.T, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
                        gemv_ptrs(c), c.h, c.hs);
   else
     hipLaunchKernelGGL(k_gemv_gateup<false>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, groups, reps, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
+                       include_shared, groups, reps, 0, c.T, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
                        gemv_ptrs(c), c.h, c.hs);
   return hipGetLastError();
 }

@@ -27,15 +27,15 @@ struct Ctx {
   hipStream_t stream;
 };
 
-// router chunk partials of T <= kGemvMaxT tokens (+ the shared expert's gate/up rows when its
-// weights are set)
+// router chunk partials of T <= kGemvMaxT tokens
 hipError_t launch_router_decode(const Ctx& c);
 hipError_t launch_decode_topk(const Ctx& c);
 hipError_t launch_router_prefill(const Ctx& c);  // logits [T][E]
 hipError_t launch_topk_prefill(const Ctx& c);    // logits -> topk_ids, topk_w
 hipError_t launch_route_meta(const Ctx& c);
-// fused_topk: take the top-k from the router partials in every block (routed slots only);
-// otherwise read topk_ids and also compute the shared slot
+// fused_topk: take the top-k from the router partials in every block, plus the shared expert's
+// rows in blocks of their own when its weights are set; otherwise read topk_ids and compute the
+// shared slot after each token's routed slots
 hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk);
 hipError_t launch_gemv_down_combine(const Ctx& c);
 hipError_t launch_gateup_gemm(const Ctx& c);

@@ -177,15 +177,11 @@ int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
   return n;
 }
 
-int run_stage(Stage s, const Ctx& c0, bool layer_call) {
+int run_stage(Stage s, const Ctx& c0) {
   Ctx c = c0;
   hipError_t e = hipSuccess;
   switch (s) {
-    case kRouterDecode:
-      // the shared expert's gate/up rides along only where the GEMV path consumes it
-      if (!(layer_call && gemv_path_ctx(c))) memset(&c.shared, 0, sizeof(c.shared));
-      e = launch_router_decode(c);
-      break;
+    case kRouterDecode: e = launch_router_decode(c); break;
     case kDecodeTopk: e = launch_decode_topk(c); break;
     case kRouterPrefill: e = launch_router_prefill(c); break;
     case kTopkPrefill: e = launch_topk_prefill(c); break;
@@ -299,13 +295,13 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
   c.logit_bias = logit_bias;
   c.r = *out;
   if (small_call(T)) {
-    if (int rc = run_stage(kRouterDecode, c, false)) return rc;
-    if (int rc = run_stage(kDecodeTopk, c, false)) return rc;
+    if (int rc = run_stage(kRouterDecode, c)) return rc;
+    if (int rc = run_stage(kDecodeTopk, c)) return rc;
   } else {
-    if (int rc = run_stage(kRouterPrefill, c, false)) return rc;
-    if (int rc = run_stage(kTopkPrefill, c, false)) return rc;
+    if (int rc = run_stage(kRouterPrefill, c)) return rc;
+    if (int rc = run_stage(kTopkPrefill, c)) return rc;
   }
-  return run_stage(kMeta, c, false);
+  return run_stage(kMeta, c);
 }
 
 int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe_routing* routing,
@@ -320,12 +316,12 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe
   layer_ctx(c, dims, T, x, nullptr, nullptr, routed, shared, y, ws, stream);
   c.r = *routing;
   if (gemv_path(*dims, T)) {
-    if (int rc = run_stage(kGemvGateup, c, false)) return rc;
-    return run_stage(kGemvDown, c, false);
+    if (int rc = run_stage(kGemvGateup, c)) return rc;
+    return run_stage(kGemvDown, c);
   }
-  if (int rc = run_stage(kGemmGateup, c, false)) return rc;
-  if (int rc = run_stage(kGemmDown, c, false)) return rc;
-  return run_stage(kCombine, c, false);
+  if (int rc = run_stage(kGemmGateup, c)) return rc;
+  if (int rc = run_stage(kGemmDown, c)) return rc;
+  return run_stage(kCombine, c);
 }
 
 int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
@@ -339,7 +335,7 @@ int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const 
   Stage st[8];
   const int n = layer_stages(*dims, T, st);
   for (int i = 0; i < n; ++i)
-    if (int rc = run_stage(st[i], c, true)) return rc;
+    if (int rc = run_stage(st[i], c)) return rc;
   return MOE_OK;
 }
 
@@ -368,7 +364,7 @@ int moe_launch_stage(int32_t stage, const moe_dims* dims, int32_t T, const uint1
   if (stage < 0 || stage >= n) return fail(MOE_EINVAL, "stage %d out of range [0, %d)", stage, n);
   Ctx c;
   layer_ctx(c, dims, T, x, w_router, logit_bias, routed, shared, y, ws, stream);
-  return run_stage(st[stage], c, true);
+  return run_stage(st[stage], c);
 }
 
 int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream) {
