@@ -414,22 +414,23 @@ hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
 
 // ---------------------------------------------------------------------------------------------
 // y[t][o] = bf16( sum_j w_tj * (h_tj . Wd[e_tj][o]) + h_ts . Wd_s[o] ), token t = blockIdx.y.
-// A block keeps every slot's h
-// in LDS (re-paired) with per-segment sums. A wave owns 4 outputs (16 lanes each) and walks the
-// slots in step: at slot j every lane takes 16-byte pieces l16, l16 + 16, ... of row o of
-// expert e_j, so the slot, its expert and its weight are wave-uniform. Slots are taken in
-// batches of kGdBatch whose loads are all in flight together. Each output is reduced inside
-// its 16 lanes: no atomics. WAVES waves per block (4 * WAVES outputs): two for a single token
-// (more blocks to spread one token's rows), four for more tokens (each block stages a token's h
-// in one round).
-constexpr int kGdBatch = 9;  // slots per batch (k = 8 routed + the shared expert in one batch)
+// A block keeps every slot's h in LDS (re-paired) with per-segment sums. Slots v = 0 .. k-1 are
+// the routed ones, v = k the shared expert. An output takes HALVES groups of 16 lanes (a wave
+// owns 4 / HALVES outputs); with two, the halves take alternate slots (half 0: v = 0, 2, 4, ...;
+// half 1: v = 1, 3, ...). At each of its slots a lane takes 16-byte pieces l16, l16 + 16, ... of
+// row o of that slot's expert. A lane's slots are taken in batches of 9 / HALVES (rounded up)
+// whose loads are all in flight together. Each 16-lane group is reduced with DPP, then the
+// halves are added: no atomics. Two halves keep every SIMD busy for a single token; for more
+// tokens one group per output does less redundant staging per output.
+constexpr int kGdWaves = 4;  // waves per block
 
-template <int PIECES, int WAVES>  // PIECES: 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
-__global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
-                                                           const int32_t* __restrict__ ids,
-                                                           const float* __restrict__ wts, GemvPtrs p,
-                                                           const uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ hs, uint16_t* __restrict__ y) {
+template <int PIECES, int HALVES>  // PIECES: 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
+__global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
+                                                                     const int32_t* __restrict__ ids,
+                                                                     const float* __restrict__ wts, GemvPtrs p,
+                                                                     const uint16_t* __restrict__ h,
+                                                                     const uint16_t* __restrict__ hs,
+                                                                     uint16_t* __restrict__ y) {
   extern __shared__ uint32_t s_h[];  // nseg * 16 dwords of re-paired h, then nseg sums
   const int tok = blockIdx.y;        // this block's token
   ids += (size_t)tok * k;
@@ -441,8 +442,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
   const int nslot = k + (Is > 0 ? 1 : 0);
   const int nseg = k * S + Ss;
   float* s_sum = reinterpret_cast<float*>(s_h + (size_t)nseg * 16);
-  const int lane = threadIdx.x & 63, l16 = lane & 15;
-  const int o = blockIdx.x * (4 * WAVES) + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  constexpr int kGdBatch = (9 + HALVES - 1) / HALVES;  // slots per lane per batch
+  constexpr int kOutW = 4 / HALVES;                     // outputs per wave
+  const int lane = threadIdx.x & 63, l16 = lane & 15, half = HALVES == 2 ? (lane >> 4) & 1 : 0;
+  const int o = (blockIdx.x * kGdWaves + (threadIdx.x >> 6)) * kOutW + (lane >> 4) / HALVES;
   const bool ovalid = o < d;
   const int orow = ovalid ? o : 0;
   // every routed slot's expert and weight with one load per wave; slots read them by lane
@@ -450,16 +453,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
   const int id_lane = ids[lj];
   const float w_lane = wts[lj];
   float acc = 0.0f;
-  for (int j0 = 0; j0 < nslot; j0 += kGdBatch) {
-    // 1. this thread's h segment for the LDS staging (first batch only; clamped, never out of bounds)
-    const int g0 = threadIdx.x;
-    const bool stage = (j0 == 0) && g0 < nseg;
-    const int gs0 = stage ? g0 : 0;
+  for (int i0 = 0; HALVES * i0 < nslot; i0 += kGdBatch) {
+    // 1. this thread's h segments for the LDS staging (first batch only; clamped, never out of
+    //    bounds); segments past 2 * blockDim.x are loaded in step 3
+    const int g0 = threadIdx.x, g1 = g0 + (int)blockDim.x;
+    const int gs0 = (i0 == 0) && g0 < nseg ? g0 : 0;
+    const int gs1 = (i0 == 0) && g1 < nseg ? g1 : 0;
     const uint32_t* src0 = gs0 < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)gs0 * 16
                                        : reinterpret_cast<const uint32_t*>(hs) + (size_t)(gs0 - k * S) * 16;
-    // ... and its second one (segments past 2 * blockDim.x are loaded in step 3)
-    const int g1 = g0 + (int)blockDim.x;
-    const int gs1 = (j0 == 0) && g1 < nseg ? g1 : 0;
     const uint32_t* src1 = gs1 < k * S ? reinterpret_cast<const uint32_t*>(h) + (size_t)gs1 * 16
                                        : reinterpret_cast<const uint32_t*>(hs) + (size_t)(gs1 - k * S) * 16;
     uint32_t hv[16], hv1[16];
@@ -482,15 +483,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
     float wj[kGdBatch];
 #pragma unroll
     for (int b = 0; b < kGdBatch; ++b) {
-      const int jj = j0 + b;  // wave-uniform
-      const bool valid = jj < nslot;
-      const bool sh = valid && jj >= k;
+      const int v0 = HALVES * (i0 + b);  // half 0's slot; half 1 takes v0 + 1
+      const int v = v0 + half;
+      const bool valid = v < nslot;
+      const bool sh = valid && v >= k;
       const int Ie = sh ? Is : I;
-      const int jl = (valid && !sh) ? jj : 0;
-      int mat = __builtin_amdgcn_readlane(id_lane, jl);
+      const int m0 = __builtin_amdgcn_readlane(id_lane, v0 < k ? v0 : 0);
+      const int m1 = __builtin_amdgcn_readlane(id_lane, v0 + 1 < k ? v0 + 1 : 0);
+      const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), v0 < k ? v0 : 0));
+      const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), v0 + 1 < k ? v0 + 1 : 0));
+      int mat = half ? m1 : m0;
       if (!valid || sh || (unsigned)mat >= (unsigned)E) mat = 0;
-      const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), jl));
-      wj[b] = !valid ? 0.0f : (sh ? 1.0f : wr);
+      wj[b] = !valid ? 0.0f : (sh ? 1.0f : (half ? w1 : w0));
       const uint8_t* dc = sh ? p.sdc : p.dc;
       const uint16_t* ds = sh ? p.sds : p.ds;
       const uint16_t* db = sh ? p.sdb : p.db;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
     }
     issue_fence();
     // 3. stage h into LDS (first batch only)
-    if (j0 == 0) {
+    if (i0 == 0) {
       for (int g = g0, r = 0; g < nseg; g += blockDim.x, ++r) {
         if (r == 1) {
 #pragma unroll
@@ -535,11 +539,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
     // 4. arithmetic
 #pragma unroll
     for (int b = 0; b < kGdBatch; ++b) {
-      const int jj = j0 + b;
-      const bool valid = jj < nslot;
-      const bool sh = valid && jj >= k;
+      const int v = HALVES * (i0 + b) + half;
+      const bool valid = v < nslot;
+      const bool sh = valid && v >= k;
       const int Sj = sh ? Ss : S;
-      const int gbase = sh ? k * S : (valid ? jj * S : 0);
+      const int gbase = sh ? k * S : (valid ? v * S : 0);
 #pragma unroll
       for (int q = 0; q < PIECES; ++q) {
         const int seg = l16 + 16 * q;
@@ -549,11 +553,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
         const uint4* hp = reinterpret_cast<const uint4*>(s_h + (size_t)gi * 16);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint4 v = hp[t];
-          a.p[4 * t] = v.x;
-          a.p[4 * t + 1] = v.y;
-          a.p[4 * t + 2] = v.z;
-          a.p[4 * t + 3] = v.w;
+          const uint4 vv = hp[t];
+          a.p[4 * t] = vv.x;
+          a.p[4 * t + 1] = vv.y;
+          a.p[4 * t + 2] = vv.z;
+          a.p[4 * t + 3] = vv.w;
         }
         a.sum = s_sum[gi];
         const uint32_t w2 = sb[b * PIECES + q];
@@ -564,35 +568,49 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_down_combine(int d, int E, 
       }
     }
   }
-  // sum over the output's 16 lanes (a DPP row); lane 0 of the row holds it after the rotations
+  // sum over each group's 16 lanes (a DPP row; every lane of the row ends with the row sum)
   acc += dpp_f32<0xB1>(acc);
   acc += dpp_f32<0x4E>(acc);
   acc += dpp_f32<0x124>(acc);
   acc += dpp_f32<0x128>(acc);
-  if (ovalid && l16 == 0) y[o] = f32_to_bf16(acc);
-}
-
-template <int PIECES, int WAVES>
-static void launch_down(const Ctx& c, size_t lds) {
-  const dim3 grid((c.d + 4 * WAVES - 1) / (4 * WAVES), c.T);
-  hipLaunchKernelGGL((k_gemv_down_combine<PIECES, WAVES>), grid, dim3(WAVES * 64), lds, c.stream, c.d, c.E, c.k, c.I,
-                     c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
+  if (HALVES == 1) {
+    if (ovalid && l16 == 0) y[o] = f32_to_bf16(acc);
+    return;
+  }
+  // the two halves of each output: outputs o0 = rows 0 + 1, o0 + 1 = rows 2 + 3 of the wave
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
+  const int o0 = o - (lane >> 5);  // the wave's first output (even)
+  if (lane == 0) {
+    if (o0 + 1 < d)
+      reinterpret_cast<uint32_t*>(y)[o0 >> 1] = pack_bf16x2(r0 + r1, r2 + r3);
+    else if (o0 < d)
+      y[o0] = f32_to_bf16(r0 + r1);
+  }
 }
 
 hipError_t launch_gemv_down_combine(const Ctx& c) {
   const int nseg = c.k * (c.I / 32) + c.Is / 32;
   const size_t lds = (size_t)nseg * 16 * 4 + (size_t)nseg * 4;
   const bool small = c.I <= 512 && c.Is <= 512;
-  if (c.T == 1) {
+  if (c.T == 1) {  // two 16-lane halves per output, 2 outputs per wave
+    const dim3 grid((c.d + 2 * kGdWaves - 1) / (2 * kGdWaves), c.T);
     if (small)
-      launch_down<1, 2>(c, lds);
+      hipLaunchKernelGGL((k_gemv_down_combine<1, 2>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
+                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
     else
-      launch_down<2, 2>(c, lds);
-  } else {
+      hipLaunchKernelGGL((k_gemv_down_combine<2, 2>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
+                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
+  } else {  // 16 lanes per output, 4 outputs per wave
+    const dim3 grid((c.d + 4 * kGdWaves - 1) / (4 * kGdWaves), c.T);
     if (small)
-      launch_down<1, 4>(c, lds);
+      hipLaunchKernelGGL((k_gemv_down_combine<1, 1>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
+                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
     else
-      launch_down<2, 4>(c, lds);
+      hipLaunchKernelGGL((k_gemv_down_combine<2, 1>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
+                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
   }
   return hipGetLastError();
 }
