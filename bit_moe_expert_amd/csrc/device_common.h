@@ -185,6 +185,85 @@ __device__ __forceinline__ void wave_topk_softmax_n(const float* lg, int E, int 
   }
 }
 
+// Top-k keys of experts [e0, e1) of lg (e1 - e0 <= 64 * SLOTS) by one wave, in order (key
+// desc, index asc): lane j < k writes the j-th key and its expert to ckey[j], cidx[j] (key 0 and
+// expert 0 when the range has fewer than j + 1 experts). Lane l holds experts e0 + l + 64 s.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_keys(const float* lg, int e0, int e1, int k, uint32_t* ckey, int32_t* cidx) {
+  const int lane = (int)lane_id();
+  uint32_t key[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int e = e0 + lane + 64 * s;
+    key[s] = e < e1 ? topk_key(lg[e]) : 0u;
+  }
+  uint32_t my_key = 0u;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t loc = key[0];
+#pragma unroll
+    for (int s = 1; s < SLOTS; ++s) loc = max(loc, key[s]);
+    const uint32_t best = wave_max_u32(loc);
+    int win = -1;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const uint64_t m = __ballot(key[s] == best);
+      if (win < 0 && m != 0) win = 64 * s + (int)__builtin_ctzll(m);
+    }
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+      if (lane + 64 * s == win) key[s] = 0u;
+    if (lane == j) {
+      my_key = best;
+      my_e = best != 0u ? e0 + win : 0;
+    }
+  }
+  if (lane < k) {
+    ckey[lane] = my_key;
+    cidx[lane] = my_e;
+  }
+}
+
+// Top-k and softmax of one token's logits lg[0..E) by a whole block of 4 waves (E <= 1024,
+// k <= 16), with the same result as wave_topk_softmax: wave w first takes the top-k of experts
+// [w * Ew, (w + 1) * Ew), Ew = ceil(E / 4), with rounds over few keys per lane; wave 0 then
+// merges the 4 sorted lists, one candidate per lane. Equal keys resolve to the lower expert:
+// within a list they come in index order, and a lower list (lower lane) holds lower experts.
+// Lanes j < k of wave 0 write slot j. Call with every thread of a 256-thread block.
+__device__ __forceinline__ void block_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
+  __shared__ uint32_t c_key[4 * kMaxTopK];
+  __shared__ int32_t c_idx[4 * kMaxTopK];
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)lane_id();
+  const int Ew = (E + 3) / 4;
+  const int e0 = min(E, wave * Ew), e1 = min(E, e0 + Ew);
+  if (Ew <= 64)
+    wave_topk_keys<1>(lg, e0, e1, k, c_key + wave * k, c_idx + wave * k);
+  else if (Ew <= 128)
+    wave_topk_keys<2>(lg, e0, e1, k, c_key + wave * k, c_idx + wave * k);
+  else
+    wave_topk_keys<4>(lg, e0, e1, k, c_key + wave * k, c_idx + wave * k);
+  __syncthreads();
+  if (wave != 0) return;
+  uint32_t key = lane < 4 * k ? c_key[lane] : 0u;
+  const int idx = lane < 4 * k ? c_idx[lane] : 0;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t best = wave_max_u32(key);
+    const int wl = (int)__builtin_ctzll(__ballot(key == best));
+    const int e = __builtin_amdgcn_readlane(idx, wl);
+    if (lane == wl) key = 0u;
+    if (lane == j) my_e = e;
+  }
+  const float my_l = lane < k ? lg[my_e] : 0.0f;
+  const float top = __shfl(my_l, 0, 64);
+  const float ex = lane < k ? expf(my_l - top) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    ids_out[lane] = my_e;
+    w_out[lane] = ex / sum;
+  }
+}
+
 __device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
   if (E <= 64)
     wave_topk_softmax_n<1>(lg, E, k, ids_out, w_out);
@@ -206,7 +285,15 @@ __device__ __forceinline__ void sum_chunk_partials(const float* __restrict__ par
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const float* pe = parts + (size_t)e * nchunks;
     float acc = 0.0f;
-    if ((nchunks & 3) == 0) {
+    if ((nchunks & 31) == 0) {  // whole batches: straight-line loads, then the adds
+      for (int cb = 0; cb < nchunks; cb += 32) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = reinterpret_cast<const f32x4_t*>(pe + cb)[q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc = (((acc + v[q].x) + v[q].y) + v[q].z) + v[q].w;
+      }
+    } else if ((nchunks & 3) == 0) {
       for (int cb = 0; cb < nchunks; cb += 32) {
         f32x4_t v[8];
 #pragma unroll
