@@ -185,73 +185,66 @@ __device__ __forceinline__ void wave_topk_softmax_n(const float* lg, int E, int 
   }
 }
 
-// Top-k keys of experts [e0, e1) of lg (e1 - e0 <= 64 * SLOTS) by one wave, in order (key
-// desc, index asc): lane j < k writes the j-th key and its expert to ckey[j], cidx[j] (key 0 and
-// expert 0 when the range has fewer than j + 1 experts). Lane l holds experts e0 + l + 64 s.
-template <int SLOTS>
-__device__ __forceinline__ void wave_topk_keys(const float* lg, int e0, int e1, int k, uint32_t* ckey, int32_t* cidx) {
-  const int lane = (int)lane_id();
-  uint32_t key[SLOTS];
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int e = e0 + lane + 64 * s;
-    key[s] = e < e1 ? topk_key(lg[e]) : 0u;
-  }
-  uint32_t my_key = 0u;
-  int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    uint32_t loc = key[0];
-#pragma unroll
-    for (int s = 1; s < SLOTS; ++s) loc = max(loc, key[s]);
-    const uint32_t best = wave_max_u32(loc);
-    int win = -1;
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const uint64_t m = __ballot(key[s] == best);
-      if (win < 0 && m != 0) win = 64 * s + (int)__builtin_ctzll(m);
-    }
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
-      if (lane + 64 * s == win) key[s] = 0u;
-    if (lane == j) {
-      my_key = best;
-      my_e = best != 0u ? e0 + win : 0;
-    }
-  }
-  if (lane < k) {
-    ckey[lane] = my_key;
-    cidx[lane] = my_e;
-  }
+// Min of a 32-bit value over the wave, returned uniform (as wave_max_u32).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));
+  v = min(v, dpp_u32<0x4E>(v));
+  v = min(v, dpp_u32<0x124>(v));
+  v = min(v, dpp_u32<0x128>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(r0, r1), min(r2, r3));
 }
 
-// Top-k and softmax of one token's logits lg[0..E) by a whole block of 4 waves (E <= 1024,
-// k <= 16), with the same result as wave_topk_softmax: wave w first takes the top-k of experts
-// [w * Ew, (w + 1) * Ew), Ew = ceil(E / 4), with rounds over few keys per lane; wave 0 then
-// merges the 4 sorted lists, one candidate per lane. Equal keys resolve to the lower expert:
-// within a list they come in index order, and a lower list (lower lane) holds lower experts.
-// Lanes j < k of wave 0 write slot j. Call with every thread of a 256-thread block.
-__device__ __forceinline__ void block_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
-  __shared__ uint32_t c_key[4 * kMaxTopK];
-  __shared__ int32_t c_idx[4 * kMaxTopK];
-  const int wave = (int)(threadIdx.x >> 6), lane = (int)lane_id();
-  const int Ew = (E + 3) / 4;
-  const int e0 = min(E, wave * Ew), e1 = min(E, e0 + Ew);
-  if (Ew <= 64)
-    wave_topk_keys<1>(lg, e0, e1, k, c_key + wave * k, c_idx + wave * k);
-  else if (Ew <= 128)
-    wave_topk_keys<2>(lg, e0, e1, k, c_key + wave * k, c_idx + wave * k);
-  else
-    wave_topk_keys<4>(lg, e0, e1, k, c_key + wave * k, c_idx + wave * k);
-  __syncthreads();
-  if (wave != 0) return;
-  uint32_t key = lane < 4 * k ? c_key[lane] : 0u;
-  const int idx = lane < 4 * k ? c_idx[lane] : 0;
+// wave_topk_softmax with each lane's keys sorted first: a lane's SLOTS experts are ordered by
+// (key desc, index asc) once, and every round reduces only the lanes' heads. The largest head
+// is the next pick; when several lanes' heads hold it (an exact tie), the lowest expert among
+// them wins. The winning lane then moves to its next key.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_softmax_sorted(const float* lg, int E, int k, int32_t* ids_out,
+                                                         float* w_out) {
+  const int lane = (int)lane_id();
+  uint32_t key[SLOTS];
+  int idx[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    idx[s] = lane + 64 * s;
+    key[s] = idx[s] < E ? topk_key(lg[idx[s]]) : 0u;
+  }
+  // insertion sort by key desc; idx ascends with s, so a strict comparison keeps equal keys
+  // in index order
+#pragma unroll
+  for (int a = 1; a < SLOTS; ++a)
+#pragma unroll
+    for (int b = a; b > 0; --b) {
+      const bool sw = key[b] > key[b - 1];
+      const uint32_t tk = key[b];
+      const int ti = idx[b];
+      key[b] = sw ? key[b - 1] : key[b];
+      idx[b] = sw ? idx[b - 1] : idx[b];
+      key[b - 1] = sw ? tk : key[b - 1];
+      idx[b - 1] = sw ? ti : idx[b - 1];
+    }
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    const uint32_t best = wave_max_u32(key);
-    const int wl = (int)__builtin_ctzll(__ballot(key == best));
-    const int e = __builtin_amdgcn_readlane(idx, wl);
-    if (lane == wl) key = 0u;
+    const uint32_t best = wave_max_u32(key[0]);
+    const uint64_t m = __ballot(key[0] == best);
+    int wl;
+    if (__builtin_popcountll(m) == 1) {
+      wl = (int)__builtin_ctzll(m);
+    } else {
+      const uint32_t lo = wave_min_u32(key[0] == best ? (uint32_t)idx[0] : 0xFFFFFFFFu);
+      wl = (int)__builtin_ctzll(__ballot(key[0] == best && (uint32_t)idx[0] == lo));
+    }
+    const int e = __builtin_amdgcn_readlane(idx[0], wl);
+    if (lane == wl) {
+#pragma unroll
+      for (int s = 0; s + 1 < SLOTS; ++s) {
+        key[s] = key[s + 1];
+        idx[s] = idx[s + 1];
+      }
+      key[SLOTS - 1] = 0u;
+    }
     if (lane == j) my_e = e;
   }
   const float my_l = lane < k ? lg[my_e] : 0.0f;
@@ -266,11 +259,11 @@ __device__ __forceinline__ void block_topk_softmax(const float* lg, int E, int k
 
 __device__ __forceinline__ void wave_topk_softmax(const float* lg, int E, int k, int32_t* ids_out, float* w_out) {
   if (E <= 64)
-    wave_topk_softmax_n<1>(lg, E, k, ids_out, w_out);
+    wave_topk_softmax_sorted<1>(lg, E, k, ids_out, w_out);
   else if (E <= 128)
-    wave_topk_softmax_n<2>(lg, E, k, ids_out, w_out);
+    wave_topk_softmax_sorted<2>(lg, E, k, ids_out, w_out);
   else if (E <= 256)
-    wave_topk_softmax_n<4>(lg, E, k, ids_out, w_out);
+    wave_topk_softmax_sorted<4>(lg, E, k, ids_out, w_out);
   else
     wave_topk_softmax_n<16>(lg, E, k, ids_out, w_out);
 }

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
     const int nchunks = d / kGroup;
     sum_chunk_partials(parts + (size_t)t * nchunks * E, bias, nchunks, E, s_lg);
     __syncthreads();
-    block_topk_softmax(s_lg, E, k, s_ids, s_w);
+    if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, s_ids, s_w);
     __syncthreads();
     if (tb0 == 0 && (int)threadIdx.x < k) {
       ids[(size_t)t * k + threadIdx.x] = s_ids[threadIdx.x];

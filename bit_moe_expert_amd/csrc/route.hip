@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void k_decode_topk(int d, int E, int k, const 
   const int t = blockIdx.x, nchunks = d / kGroup;
   sum_chunk_partials(parts + (size_t)t * nchunks * E, bias, nchunks, E, s_lg);
   __syncthreads();
-  block_topk_softmax(s_lg, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  if (threadIdx.x < 64) wave_topk_softmax(s_lg, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 hipError_t launch_decode_topk(const Ctx& c) {
