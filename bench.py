@@ -54,7 +54,7 @@ PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "
         "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40)}
 DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gateup_gemm", "long": "gateup_gemm",
             "diffusion": "gateup_gemm", "m2": "gemv_gateup_topk", "m4": "gemv_gateup_topk",
-            "m8": "gemv_gateup_topk", "m16": "gateup_gemm"}
+            "m8": "gemv_gateup_topk", "m16": "gemv_gateup_topk"}
 STAGE_SOURCE = {"router_decode": "gemv.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
                 "topk_prefill": "route.hip",

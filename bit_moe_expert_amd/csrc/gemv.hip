@@ -165,24 +165,25 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
 // ---------------------------------------------------------------------------------------------
 // Router of T <= kGemvMaxT tokens: chunk partials of the logits (see route.hip for the fixed
 // order), stored [T][E][d/64]. A block holds one (chunk, 64 experts) item: wave w loads the
-// chunk's router values and the inputs of tokens w and w + kGvWaves, all before the first use,
-// and runs the two tokens' fma chains interleaved (lane = expert).
+// chunk's router values once, then takes tokens (w, w + kGvWaves), (w + 2 kGvWaves, ...), ...
+// in pairs: each pair's inputs are loaded before the first use and the two tokens' fma chains
+// run interleaved (lane = expert).
 __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, int T, const uint16_t* __restrict__ x,
                                                                  const float* __restrict__ wr,
                                                                  float* __restrict__ parts) {
   const int wave = uniform(threadIdx.x >> 6);
-  {
-    const int nchunks = d / kGroup;
-    const int item = blockIdx.x;
-    const int c = item % nchunks;
-    const int e = (item / nchunks) * 64 + (threadIdx.x & 63);
-    const int ta = wave, tb = wave + kGvWaves;
-    if (ta >= T || e >= E) return;
-    const int tb2 = tb < T ? tb : ta;  // without a second token the second chain repeats the first
-    const float* wp = wr + (size_t)c * kGroup * E + e;
-    float v[kGroup];
+  const int nchunks = d / kGroup;
+  const int item = blockIdx.x;
+  const int c = item % nchunks;
+  const int e = (item / nchunks) * 64 + (threadIdx.x & 63);
+  if (wave >= T || e >= E) return;
+  const float* wp = wr + (size_t)c * kGroup * E + e;
+  float v[kGroup];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
+  for (int i = 0; i < kGroup; ++i) v[i] = wp[(size_t)i * E];
+  for (int ta = wave; ta < T; ta += 2 * kGvWaves) {
+    const int tb = ta + kGvWaves;
+    const int tb2 = tb < T ? tb : ta;  // without a second token the second chain repeats the first
     // the chunk's 64 inputs of both tokens (8 x 16 bytes each), all in flight with the weights;
     // a zero the compiler cannot see through keeps them vector loads (scalar loads return out
     // of order, so their uses would wait for all of them at once, in several rounds)
@@ -217,7 +218,6 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_router_decode(int d, int E, i
 }
 
 hipError_t launch_router_decode(const Ctx& c) {
-  static_assert(kGemvMaxT <= 2 * kGvWaves, "router partials: two tokens per wave");
   const int n_part = (c.d / kGroup) * ((c.E + 63) / 64);  // one (chunk, 64 experts) item per block
   hipLaunchKernelGGL(k_router_decode, dim3(n_part), dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.T, c.x, c.w_router,
                      c.router_parts);

@@ -151,7 +151,7 @@ def test_forward_diffusion(layer):
 
 @pytest.mark.parametrize("name,layer", [("m2", 0), ("m2", 39), ("m4", 7), ("m8", 0), ("m8", 39), ("m16", 11)])
 def test_forward_small_calls(name, layer):
-    """2..8 tokens run the GEMV path (a token per wave), 16 the grouped GEMM."""
+    """2..16 tokens run the GEMV path (a token per wave)."""
     _forward_check(gen.WORKLOADS[name], layer=layer)
 
 
@@ -159,7 +159,7 @@ SHAPES = [
     # (T, d, E, k, I, Is): ragged T, K tails (d or I = 64 mod 128), shared size != routed, no shared
     (1, 256, 16, 4, 128, 128), (1, 192, 8, 2, 192, 64), (2, 256, 16, 4, 128, 128), (3, 192, 4, 2, 192, 0),
     (33, 256, 8, 3, 64, 128), (257, 128, 16, 2, 128, 64), (130, 320, 2, 2, 64, 192), (5, 64, 1, 1, 64, 64),
-    (40, 128, 4, 4, 256, 0), (1, 128, 1, 1, 64, 0),
+    (40, 128, 4, 4, 256, 0), (1, 128, 1, 1, 64, 0), (13, 256, 16, 4, 128, 128), (16, 192, 8, 3, 64, 64),
 ]
 
 
