@@ -48,13 +48,16 @@ DESCR = {
     "m4": "small-M: T=4, decode shapes, 40 layers cycled",
     "m8": "small-M: T=8, decode shapes, 40 layers cycled",
     "m16": "small-M: T=16, decode shapes, 40 layers cycled",
+    "m32": "small-M: T=32, decode shapes, 40 layers cycled",
+    "m64": "small-M: T=64, decode shapes, 40 layers cycled",
 }
 # layers held on the GPU and calls per step
 PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "diffusion": (30, 30),
-        "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40)}
+        "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40), "m32": (40, 40), "m64": (40, 40)}
 DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gateup_gemm", "long": "gateup_gemm",
             "diffusion": "gateup_gemm", "m2": "gemv_gateup_topk", "m4": "gemv_gateup_topk",
-            "m8": "gemv_gateup_topk", "m16": "gemv_gateup_topk"}
+            "m8": "gemv_gateup_topk", "m16": "gemv_gateup_topk", "m32": "gemv_gateup_topk",
+            "m64": "gateup_gemm"}
 STAGE_SOURCE = {"router_decode": "gemv.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
                 "topk_prefill": "route.hip",
@@ -307,9 +310,10 @@ def main() -> int:
         torch.cuda.synchronize()
 
     # ---- roofline of the dominant kernel
-    dom = DOMINANT[args.workload]
-    if dom not in stages:
-        log(f"dominant stage {dom} is not on this call's path; stages: {list(stages)}")
+    # the gate/up stage of whichever path this call takes (the GEMV tier's bound is a build choice)
+    dom = next((s for s in (DOMINANT[args.workload], "gemv_gateup_topk", "gateup_gemm") if s in stages), None)
+    if dom is None:
+        log(f"no gate/up stage on this call's path; stages: {list(stages)}")
         return 1
     st = stages[dom]
     bound = "hbm"

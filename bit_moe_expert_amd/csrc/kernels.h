@@ -47,7 +47,7 @@ hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* o
 constexpr int kTileRows = 32;
 
 // Calls of up to kGemvMaxT tokens take the GEMV path (one token per wave, no grouping).
-constexpr int kGemvMaxT = 16;
+constexpr int kGemvMaxT = 32;
 // The GEMV path's down kernel keeps a token's selected experts' h in LDS: (k*I + Is) bf16 values.
 constexpr int kGemvMaxH = 28672;
 // ... and its down kernel keeps two 16-lane rounds of 32-input pieces per row in registers.

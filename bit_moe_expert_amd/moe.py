@@ -194,7 +194,7 @@ def route(x: torch.Tensor, w_router: torch.Tensor, k: int, d_ff: int, d_ff_share
 
 def expert_ffn(x: torch.Tensor, routing: Dict[str, torch.Tensor], routed: QuantFFN, shared: Optional[QuantFFN],
                ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """moe_expert_ffn: the expert FFN of routed tokens (GEMV path for calls of up to 16 tokens, grouped GEMM above)."""
+    """moe_expert_ffn: the expert FFN of routed tokens (GEMV path for calls of up to 32 tokens, grouped GEMM above)."""
     T, d = x.shape
     k = routing["topk_ids"].shape[1]
     dims = _dims_for(x, routed, shared, k)

@@ -146,7 +146,7 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
  *   y[t] = bf16( sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]) + FFN_shared(x[t]) ),
  *   FFN_e(x) = h Wd_e^T with h = bf16( silu(x Wg_e^T) * (x Wu_e^T) ), each weight taken as
  *   scale * code + bias inside the dot products (never expanded in memory), fp32 accumulation.
- * Calls of 1..16 tokens run the GEMV path (uses topk_ids and topk_w only) when
+ * Calls of 1..32 tokens run the GEMV path (uses topk_ids and topk_w only) when
  * top_k * d_ff + d_ff_shared <= 28672 and d_ff, d_ff_shared <= 1024; other calls run the grouped
  * GEMM path (uses every routing array). `shared` must be NULL iff d_ff_shared == 0.
  */

@@ -62,12 +62,12 @@ def test_stage_lists():
     big = _dims(k=16, I=2048)  # too much h for the GEMV path: T = 1 runs the grouped GEMM
     assert [L.moe_stage_name(ctypes.byref(big), 1, s).decode() for s in range(L.moe_num_stages(ctypes.byref(big), 1))] \
         == ["router_decode", "decode_topk", "route_meta", "gateup_gemm", "down_gemm", "combine"]
-    # calls of up to 16 tokens take the GEMV path; 17 tokens and up the grouped GEMM
-    for T in (2, 5, 8, 16):
+    # calls of up to 32 tokens take the GEMV path; 33 tokens and up the grouped GEMM
+    for T in (2, 5, 8, 16, 32):
         assert [L.moe_stage_name(ctypes.byref(d), T, s).decode() for s in range(L.moe_num_stages(ctypes.byref(d), T))] \
             == ["router_decode", "gemv_gateup_topk", "gemv_down_combine"], T
-    assert L.moe_stage_name(ctypes.byref(d), 17, 0).decode() == "router_prefill"
-    assert L.moe_num_stages(ctypes.byref(d), 17) == 6
+    assert L.moe_stage_name(ctypes.byref(d), 33, 0).decode() == "router_prefill"
+    assert L.moe_num_stages(ctypes.byref(d), 33) == 6
 
 
 class _Fake:

@@ -149,9 +149,10 @@ def test_forward_diffusion(layer):
     _forward_check(gen.WORKLOADS["diffusion"], layer=layer)
 
 
-@pytest.mark.parametrize("name,layer", [("m2", 0), ("m2", 39), ("m4", 7), ("m8", 0), ("m8", 39), ("m16", 11)])
+@pytest.mark.parametrize("name,layer", [("m2", 0), ("m2", 39), ("m4", 7), ("m8", 0), ("m8", 39), ("m16", 11),
+                                        ("m32", 5), ("m64", 2)])
 def test_forward_small_calls(name, layer):
-    """2..16 tokens run the GEMV path (a token per wave)."""
+    """2..32 tokens run the GEMV path (a token per wave), 64 the grouped GEMM."""
     _forward_check(gen.WORKLOADS[name], layer=layer)
 
 
@@ -160,6 +161,7 @@ SHAPES = [
     (1, 256, 16, 4, 128, 128), (1, 192, 8, 2, 192, 64), (2, 256, 16, 4, 128, 128), (3, 192, 4, 2, 192, 0),
     (33, 256, 8, 3, 64, 128), (257, 128, 16, 2, 128, 64), (130, 320, 2, 2, 64, 192), (5, 64, 1, 1, 64, 64),
     (40, 128, 4, 4, 256, 0), (1, 128, 1, 1, 64, 0), (13, 256, 16, 4, 128, 128), (16, 192, 8, 3, 64, 64),
+    (31, 192, 8, 3, 64, 0), (32, 256, 16, 4, 128, 128),
 ]
 
 

@@ -171,12 +171,14 @@ WORKLOADS: Dict[str, Workload] = {
     "long": Workload("long", 4096, 2048, 256, 8, 512, 512, 0.02, 1, 1024, zipf=True),
     # diffusion canvas: 256 positions x 30 layers, 128 experts top-8, I = 768, no shared expert
     "diffusion": Workload("diffusion", 256, 2048, 128, 8, 768, 0, 0.02, 30, 256),
-    # small-M calls (2..16 tokens, e.g. a few decode streams or speculative rows) at the decode
+    # small-M calls (2..64 tokens, e.g. a few decode streams or speculative rows) at the decode
     # shapes, over the same 40 layers
     "m2": Workload("m2", 2, 2048, 256, 8, 512, 512, 0.02, 40, 2),
     "m4": Workload("m4", 4, 2048, 256, 8, 512, 512, 0.02, 40, 4),
     "m8": Workload("m8", 8, 2048, 256, 8, 512, 512, 0.02, 40, 8),
     "m16": Workload("m16", 16, 2048, 256, 8, 512, 512, 0.02, 40, 16),
+    "m32": Workload("m32", 32, 2048, 256, 8, 512, 512, 0.02, 40, 32),
+    "m64": Workload("m64", 64, 2048, 256, 8, 512, 512, 0.02, 40, 64),
 }
 
 
