@@ -38,6 +38,11 @@
  *      rounded to bf16 -- [LILY-BLOG "Decode: minimize bytes per token"] (expert output
  *      projection fused with the routing scores and the shared expert).
  *
+ *   8. (separate workload) the exact top-K of each row of a logit matrix, by (value descending,
+ *      index ascending) -- [DIFFGEMMA "The optimizations that worked"], whose hierarchical
+ *      chunk-max selection reaches exactly this set; the oracle is the plain definition, a full
+ *      sort of the row.
+ *
  * Parity pins: every function here is checked by the CPU tests against closed forms,
  * exhaustive identities or brute force (see the tests named test_oracle_*.py).
  */
@@ -446,4 +451,39 @@ int oracle_forward_tokens(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I,
     free(yr);
   }
   return rc;
+}
+
+/* ---------------------------------------------------------------- 8. exact top-K of logit rows
+ * [DIFFGEMMA "The optimizations that worked"]: a sampler needs only the K largest logits of a
+ * position; the pages reach them through chunk maxima and state that the result is exactly
+ * the global top-K. Definition used here: sort the row by (value descending, index ascending)
+ * and keep the first K; ids[r][j] and vals[r][j] are the j-th entry. -0 and +0 compare equal
+ * (so the lower index comes first). Rows must hold no NaN (reading: the pages' logits are
+ * finite). */
+static const float* orc_sort_row;
+static int orc_cmp_desc(const void* a, const void* b) {
+  const int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+  const float x = orc_sort_row[i], y = orc_sort_row[j];
+  if (x > y) return -1;
+  if (x < y) return 1;
+  return (i > j) - (i < j);
+}
+
+int oracle_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids, float* vals) {
+  if (R < 0 || V < 1 || K < 1 || K > V) return 1;
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)V);
+  if (!idx) return 2;
+  /* qsort takes no context argument, so rows are sorted one after another */
+  for (int32_t r = 0; r < R; ++r) {
+    const float* row = logits + (int64_t)r * V;
+    for (int32_t i = 0; i < V; ++i) idx[i] = i;
+    orc_sort_row = row;
+    qsort(idx, (size_t)V, sizeof(int32_t), orc_cmp_desc);
+    for (int32_t j = 0; j < K; ++j) {
+      ids[(int64_t)r * K + j] = idx[j];
+      vals[(int64_t)r * K + j] = row[idx[j]];
+    }
+  }
+  free(idx);
+  return 0;
 }

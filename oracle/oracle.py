@@ -55,8 +55,9 @@ def lib():
                                            ctypes.POINTER(_FFN), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.oracle_forward_tokens.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(_FFN),
                                             ctypes.POINTER(_FFN), i32, vp, vp, vp, vp]
+        L.oracle_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp]
         for f in ("oracle_router_logits", "oracle_topk_softmax", "oracle_route_meta", "oracle_dequant",
-                  "oracle_forward_layer", "oracle_forward_tokens"):
+                  "oracle_forward_layer", "oracle_forward_tokens", "oracle_vocab_topk"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,3 +228,15 @@ def forward_tokens(x, w_router, routed: dict, shared: Optional[dict], k: int, se
     if rc:
         raise ValueError(f"oracle_forward_tokens rc={rc}")
     return {"y": y, "topk_ids": ids, "topk_w": w}
+
+
+def vocab_topk(logits, K: int):
+    """Exact top-K of each row by (value desc, index asc): (ids [R][K] int32, vals [R][K] fp32)."""
+    logits = _c(logits, np.float32)
+    R, V = logits.shape
+    ids = np.empty((R, K), np.int32)
+    vals = np.empty((R, K), np.float32)
+    rc = lib().oracle_vocab_topk(R, V, K, _p(logits), _p(ids), _p(vals))
+    if rc:
+        raise ValueError(f"oracle_vocab_topk rc={rc}")
+    return ids, vals

@@ -521,3 +521,82 @@ def test_oracle_is_thread_count_invariant():
         outs.append(subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                                    check=True).stdout.strip())
     assert outs[0] == outs[1] and len(outs[0]) == 64
+
+
+# ------------------------------------------------------------------ exact top-K of logit rows
+def _brute_topk(row, K):
+    order = sorted(range(len(row)), key=lambda i: (-float(row[i]), i))[:K]
+    return np.array(order, np.int32), row[order]
+
+
+def _chunk_max_topk(row, K, C, lower_chunk_first=True):
+    """The pages' hierarchical selection, written from their description: chunk maxima, the K
+    chunks with the largest maxima, then the top K inside the chosen chunks."""
+    V = len(row)
+    nch = (V + C - 1) // C
+    cmax = [max(float(v) for v in row[c * C:(c + 1) * C]) for c in range(nch)]
+    tie = (lambda c: c) if lower_chunk_first else (lambda c: -c)
+    chosen = sorted(range(nch), key=lambda c: (-cmax[c], tie(c)))[:K]
+    cand = [i for c in chosen for i in range(c * C, min(V, (c + 1) * C))]
+    cand.sort(key=lambda i: (-float(row[i]), i))
+    return np.array(cand[:K], np.int32)
+
+
+def test_vocab_topk_closed_forms():
+    V, K = 1000, 16
+    ids, vals = oracle.vocab_topk(np.zeros((1, V), np.float32), K)           # all equal: lowest indices
+    assert (ids[0] == np.arange(K)).all() and (vals == 0).all()
+    ids, _ = oracle.vocab_topk(-np.arange(V, dtype=np.float32)[None], K)      # decreasing ramp
+    assert (ids[0] == np.arange(K)).all()
+    ids, vals = oracle.vocab_topk(np.arange(V, dtype=np.float32)[None], K)    # increasing ramp
+    assert (ids[0] == np.arange(V - 1, V - 1 - K, -1)).all() and (vals[0] == ids[0]).all()
+    ids, _ = oracle.vocab_topk(np.array([[-0.0, 0.0, -1.0]], np.float32), 2)  # -0 == +0: index order
+    assert ids.tolist() == [[0, 1]]
+    ids, vals = oracle.vocab_topk(np.array([[1.0, np.inf, -np.inf, 2.0]], np.float32), 4)
+    assert ids.tolist() == [[1, 3, 0, 2]]
+
+
+def test_vocab_topk_matches_brute_force_with_ties():
+    rng = np.random.default_rng(11)
+    for V, K in ((1, 1), (7, 7), (300, 1), (513, 64), (2000, 100)):
+        x = rng.integers(-6, 6, size=(3, V)).astype(np.float32) * 0.5  # heavy ties
+        x[1] = rng.normal(size=V).astype(np.float32)
+        ids, vals = oracle.vocab_topk(x, K)
+        for r in range(3):
+            bi, bv = _brute_topk(x[r], K)
+            assert (ids[r] == bi).all() and (vals[r] == bv).all(), (V, K, r)
+
+
+def test_chunk_max_selection_is_exact_as_the_pages_state():
+    """[DIFFGEMMA "The optimizations that worked"]: a value in the global top-K has fewer than K
+    chunk maxima above it, so its chunk is among the K chosen. With equal maxima the lower chunk
+    must win (the values tied with it that it displaces come first); adversarial rows check both."""
+    rng = np.random.default_rng(12)
+    V = 1000
+    rows = [rng.normal(size=V).astype(np.float32)]
+    r = rng.normal(size=V).astype(np.float32) - 10.0
+    r[200:264] = 5.0 + rng.random(64).astype(np.float32)  # the whole top-K inside one chunk
+    rows.append(r)
+    rows.append(np.repeat(rng.integers(0, 4, V // 8 + 1), 8)[:V].astype(np.float32))  # ties across chunks
+    r = np.zeros(V, np.float32)
+    r[::50] = 1.0  # one maximum per chunk of 50, equal everywhere
+    rows.append(r)
+    for row in rows:
+        for K in (1, 5, 16, 64):
+            want, _ = oracle.vocab_topk(row[None], K)
+            for C in (50, 64, 128, 333):
+                assert (_chunk_max_topk(row, K, C) == want[0]).all(), (K, C)
+    # the tie rule matters: taking the higher chunk among equal maxima loses lower-index entries
+    row = np.zeros(V, np.float32)
+    assert not (_chunk_max_topk(row, 4, 100, lower_chunk_first=False) == oracle.vocab_topk(row[None], 4)[0][0]).all()
+
+
+def test_vocab_topk_full_size_row_against_lexsort():
+    """One row of the pages' size (262,144 logits, K = 64) against numpy's lexsort."""
+    rng = np.random.default_rng(13)
+    x = (rng.normal(size=(2, 262144)) * 3).astype(np.float32)
+    x[1, 1000:1100] = x[0].max() + 1.0  # a tied block at the top
+    ids, vals = oracle.vocab_topk(x, 64)
+    for r in range(2):
+        order = np.lexsort((np.arange(x.shape[1]), -x[r].astype(np.float64)))[:64]
+        assert (ids[r] == order).all() and (vals[r] == x[r][order]).all()

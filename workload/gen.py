@@ -35,6 +35,7 @@ T_SH_UP_CODES, T_SH_UP_SB = 10, 11
 T_SH_DOWN_CODES, T_SH_DOWN_SB = 12, 13
 T_PERM = 14
 T_X = 100  # + chunk index
+T_LOGITS = 1000  # + step index (logit rows of the top-K workload)
 
 QUANT_SIGMA = 0.02
 GROUP = 64
@@ -228,6 +229,35 @@ def logit_bias(w: Workload, permuted: bool = False) -> Optional[np.ndarray]:
 def tokens(w: Workload, layer: int, chunk: int, T: Optional[int] = None) -> np.ndarray:
     T = w.chunk if T is None else T
     return normal_bf16(key(w.seed, layer, T_X + chunk), T * w.d, 1.0).reshape(T, w.d)
+
+
+@dataclasses.dataclass(frozen=True)
+class VocabWorkload:
+    """Rows of logits whose exact top-K a sampler needs: R positions over a V-entry vocabulary."""
+    name: str
+    R: int
+    V: int
+    K: int
+    sigma: float    # spread of the raw logits
+    softcap: float  # logits are softcap * tanh(z / softcap), z ~ N(0, sigma^2), as a softcapped head gives
+    steps: int = 1  # distinct logit matrices the benchmark cycles
+    seed: int = 0
+
+
+VOCAB_WORKLOADS: Dict[str, VocabWorkload] = {
+    "vocab_tiny": VocabWorkload("vocab_tiny", 5, 3000, 16, 3.0, 30.0),
+    # a 256-position canvas over a 262,144-entry vocabulary, top-64 per position
+    "vocab": VocabWorkload("vocab", 256, 262144, 64, 3.0, 30.0, steps=4),
+}
+
+
+def vocab_logits(w: VocabWorkload, step: int = 0, rows: Optional[int] = None) -> np.ndarray:
+    """fp32 logits [R][V] of one step (the first `rows` rows when given)."""
+    R = w.R if rows is None else rows
+    z = normal_f32(key(w.seed, 0, T_LOGITS + step), R * w.V, w.sigma)
+    np.tanh(z * np.float32(1.0 / w.softcap), out=z)
+    z *= np.float32(w.softcap)
+    return z.reshape(R, w.V)
 
 
 def layer(w: Workload, layer_idx: int = 0) -> dict:
