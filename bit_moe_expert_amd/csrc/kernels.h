@@ -41,6 +41,13 @@ hipError_t launch_gemv_down_combine(const Ctx& c);
 hipError_t launch_gateup_gemm(const Ctx& c);
 hipError_t launch_down_gemm(const Ctx& c);
 hipError_t launch_combine(const Ctx& c);
+// Exact top-K of logit rows (vocab_topk.hip): chunk size C for a given K (K * C = 32768 keys at
+// most in LDS), the largest K and V supported, and the launch (cmax: [R][ceil(V / C)] keys).
+constexpr int kVocabMaxK = 128;
+constexpr int kVocabMaxChunks = 8192;
+inline int vocab_chunk(int K) { return K <= 32 ? 1024 : K <= 64 ? 512 : 256; }
+hipError_t launch_vocab_topk(int R, int V, int K, const float* logits, uint32_t* cmax, int32_t* ids, float* vals,
+                             hipStream_t stream);
 hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* out, hipStream_t stream);
 
 // Block-map tile height (rows of one expert group per tile).

@@ -1,6 +1,6 @@
 // C ABI of libmoe_int4.so: argument validation (before any HIP call), workspace layout and the
-// stage sequence of each entry point. The kernels live in route.hip, gemv.hip, gemm.hip and
-// dequant.hip.
+// stage sequence of each entry point. The kernels live in route.hip, gemv.hip, gemm.hip,
+// dequant.hip and vocab_topk.hip.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -377,6 +377,34 @@ int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* o
   if (rows * (in_dim / 64) > (int64_t)1 << 38) return fail(MOE_EUNSUPPORTED, "too many rows");
   hipError_t e = launch_dequant(*w, rows, in_dim, out_bf16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EHIP, "launch of dequant failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+size_t moe_vocab_topk_workspace_bytes(int32_t R, int32_t V, int32_t K) {
+  if (R < 0 || V < 1 || K < 1 || K > kVocabMaxK || K > V) return 0;
+  const int64_t nch = ((int64_t)V + vocab_chunk(K) - 1) / vocab_chunk(K);
+  if (nch > kVocabMaxChunks) return 0;
+  return up((size_t)std::max<int32_t>(R, 1) * (size_t)nch * 4);
+}
+
+int moe_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids, float* vals, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (R < 0) return fail(MOE_EINVAL, "R = %d is negative", R);
+  if (V < 1 || K < 1 || K > V) return fail(MOE_EUNSUPPORTED, "need 1 <= K <= V (K = %d, V = %d)", K, V);
+  if (K > kVocabMaxK) return fail(MOE_EUNSUPPORTED, "K = %d exceeds %d", K, kVocabMaxK);
+  const size_t need = moe_vocab_topk_workspace_bytes(R, V, K);
+  if (need == 0)
+    return fail(MOE_EUNSUPPORTED, "V = %d exceeds %d chunks of %d", V, kVocabMaxChunks, vocab_chunk(K));
+  if (R == 0) return MOE_OK;
+  if (!logits || !aligned(logits, 4)) return fail(MOE_EINVAL, "logits NULL or not 4-byte aligned");
+  if (!ids || !aligned(ids, 4) || !vals || !aligned(vals, 4))
+    return fail(MOE_EINVAL, "ids/vals NULL or not 4-byte aligned");
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_EINVAL, "workspace not 256-byte aligned");
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  const hipError_t e = launch_vocab_topk(R, V, K, logits, static_cast<uint32_t*>(ws), ids, vals,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "launch of the top-K kernels failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
 

@@ -73,7 +73,11 @@ def lib():
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
-        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_launch_stage"):
+        L.moe_vocab_topk_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_vocab_topk_workspace_bytes.restype = sz
+        L.moe_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_launch_stage",
+                  "moe_vocab_topk"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -273,3 +277,28 @@ def debug_dequant(p: QProj) -> torch.Tensor:
     rc = lib().moe_debug_dequant(ctypes.byref(q), rows, in_dim, _ptr(out, torch.bfloat16, "out", dev), _stream(dev))
     _check(rc, "moe_debug_dequant")
     return out
+
+
+def vocab_topk_workspace_bytes(R: int, V: int, K: int) -> int:
+    return lib().moe_vocab_topk_workspace_bytes(R, V, K)
+
+
+def vocab_topk(logits: torch.Tensor, K: int, ws: Optional[torch.Tensor] = None, ids: Optional[torch.Tensor] = None,
+               vals: Optional[torch.Tensor] = None):
+    """moe_vocab_topk: exact top-K of each row of fp32 logits [R][V] by (value desc, index asc).
+    Returns (ids [R][K] int32, vals [R][K] fp32)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R][V]")
+    R, V = logits.shape
+    dev = logits.device
+    n = vocab_topk_workspace_bytes(R, V, K)
+    if n == 0:
+        raise MoeError(MOE_EUNSUPPORTED, "moe_vocab_topk_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    ids = torch.empty((R, K), dtype=torch.int32, device=dev) if ids is None else ids
+    vals = torch.empty((R, K), dtype=torch.float32, device=dev) if vals is None else vals
+    rc = lib().moe_vocab_topk(R, V, K, _ptr(logits, torch.float32, "logits", dev), _ptr(ids, torch.int32, "ids", dev),
+                              _ptr(vals, torch.float32, "vals", dev), _ptr(ws, torch.uint8, "ws", dev), ws.numel(),
+                              _stream(dev))
+    _check(rc, "moe_vocab_topk")
+    return ids, vals

@@ -175,6 +175,26 @@ int moe_launch_stage(int32_t stage, const moe_dims* dims, int32_t T, const uint1
                      const float* w_router, const float* logit_bias, const moe_ffn_q4* routed,
                      const moe_ffn_q4* shared, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Exact top-K of each row of a logit matrix, the candidates a sampler over a large vocabulary
+ * needs ("Squeezing a 26B diffusion LLM onto a Mac", section "The optimizations that worked",
+ * the hierarchical exact top-K): for every row r < R of logits [R][V] (fp32, row-major),
+ *   ids[r][j], vals[r][j] = index and value of the j-th entry of the row in the order
+ *   (value descending, index ascending), j < K.
+ * The row is reduced to chunk maxima, the K chunks with the largest maxima are kept, and the
+ * top K is taken among their entries; the result equals the full sort's (no approximation).
+ * -0 and +0 compare equal; rows must hold no NaN.
+ * Limits: 1 <= K <= 128, K <= V, and V <= 8192 * C with C = 1024 for K <= 32, 512 for K <= 64,
+ * 256 above (so V <= 4,194,304 at K = 64); otherwise MOE_EUNSUPPORTED. R = 0 is a no-op.
+ * Pointers are device pointers, 4-byte aligned (logits 16-byte aligned with V % 4 == 0 gives
+ * the fastest loads); ids [R][K] int32 and vals [R][K] fp32 must not overlap logits. ws holds
+ * moe_vocab_topk_workspace_bytes(R, V, K) bytes, 256-byte aligned, contents irrelevant.
+ * Enqueues two kernels on `stream`; no host synchronisation.
+ */
+size_t moe_vocab_topk_workspace_bytes(int32_t R, int32_t V, int32_t K);  /* 0 if unsupported */
+int moe_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids, float* vals, void* ws,
+                   size_t ws_bytes, void* stream);
+
 const char* moe_status_str(int status);
 const char* moe_last_error(void);
 

@@ -153,3 +153,26 @@ def test_binding_refuses_cpu_tensors_and_has_no_fallback():
     src = "".join(open(os.path.join(ROOT, "bit_moe_expert_amd", n)).read() for n in ("moe.py", "__init__.py"))
     assert "oracle" not in src.replace("oracle_", "")
     assert pkg.moe.LIB_PATH.endswith("libmoe_int4.so")
+
+
+def test_vocab_topk_sizing_and_validation():
+    L = moe.lib()
+    assert L.moe_vocab_topk_workspace_bytes(256, 262144, 64) == 256 * 512 * 4
+    assert L.moe_vocab_topk_workspace_bytes(1, 100, 16) == 256            # one chunk, rounded up
+    assert L.moe_vocab_topk_workspace_bytes(3, 1 << 22, 64) == 3 * 8192 * 4
+    assert L.moe_vocab_topk_workspace_bytes(3, (1 << 22) + 1, 64) == 0     # more than 8192 chunks
+    assert L.moe_vocab_topk_workspace_bytes(3, 1000, 129) == 0
+    assert L.moe_vocab_topk_workspace_bytes(3, 10, 11) == 0
+    f = _Fake()
+    call = lambda R, V, K, **o: L.moe_vocab_topk(R, V, K, o.get("logits", f()), o.get("ids", f()),  # noqa: E731
+                                                 o.get("vals", f()), o.get("ws", f()), o.get("ws_bytes", 1 << 30),
+                                                 None)
+    assert call(0, 1000, 8) == moe.MOE_OK
+    assert call(-1, 1000, 8) == moe.MOE_EINVAL
+    assert call(2, 1000, 0) == moe.MOE_EUNSUPPORTED
+    assert call(2, 1000, 129) == moe.MOE_EUNSUPPORTED
+    assert call(2, 8, 9) == moe.MOE_EUNSUPPORTED
+    assert call(2, 1000, 8, logits=None) == moe.MOE_EINVAL
+    assert call(2, 1000, 8, ids=f() + 2) == moe.MOE_EINVAL
+    assert call(2, 1000, 8, ws=f() + 128) == moe.MOE_EINVAL
+    assert call(2, 1000, 8, ws_bytes=16) == moe.MOE_EWORKSPACE
