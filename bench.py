@@ -62,7 +62,8 @@ STAGE_SOURCE = {"router_decode": "gemv.hip", "router_prefill": "route.hip", "rou
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
                 "topk_prefill": "route.hip",
                 "gemv_down_combine": "gemv.hip", "gateup_gemm": "gemm.hip",
-                "down_gemm": "gemm.hip", "combine": "gemm.hip"}
+                "down_gemm": "gemm.hip", "combine": "gemm.hip", "chunk_max": "vocab_topk.hip",
+                "topk_rows": "vocab_topk.hip"}
 
 
 def log(msg: str) -> None:
@@ -169,13 +170,124 @@ def cpu_baseline(w: gen.Workload, host_layers, seconds: float):
                       f"{len(host_layers)} layers cycled), {el:.1f} s"}
 
 
+# ------------------------------------------------------------------------- exact top-K of logit rows
+def vocab_work(w: gen.VocabWorkload, stage: int):
+    """(bytes) one launch of a top-K kernel must move: stage 0 reads every logit once and writes the
+    chunk maxima; stage 1 reads the chunk maxima and the K chosen chunks and writes K ids and values."""
+    C = 1024 if w.K <= 32 else 512 if w.K <= 64 else 256  # the library's chunk size for this K
+    nch = (w.V + C - 1) // C
+    if stage == 0:
+        return 4 * w.R * w.V + 4 * w.R * nch
+    return w.R * (4 * nch + 4 * min(w.K, nch) * C + 8 * w.K)
+
+
+def main_vocab(args) -> int:
+    dev = torch.device("cuda:0")
+    w = gen.VOCAB_WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    host = [gen.vocab_logits(w, s) for s in range(w.steps)]
+    xs = [torch.from_numpy(h).to(dev) for h in host]
+    ws = torch.empty(moe.vocab_topk_workspace_bytes(w.R, w.V, w.K), dtype=torch.uint8, device=dev)
+    ids = [torch.empty((w.R, w.K), dtype=torch.int32, device=dev) for _ in xs]
+    vals = [torch.empty((w.R, w.K), dtype=torch.float32, device=dev) for _ in xs]
+    torch.cuda.synchronize()
+    log(f"{w.steps} logit matrices [{w.R}][{w.V}] resident in {time.perf_counter() - t0:.1f} s")
+    # eager pass + parity gate (bit-exact on sampled rows of every matrix)
+    for s in range(w.steps):
+        moe.vocab_topk(xs[s], w.K, ws, ids[s], vals[s])
+    torch.cuda.synchronize()
+    eager = [(i.clone(), v.clone()) for i, v in zip(ids, vals)]
+    from oracle import oracle
+    rows = np.linspace(0, w.R - 1, min(w.R, 8)).astype(np.int64)
+    for s in range(w.steps):
+        ri, rv = oracle.vocab_topk(host[s][rows], w.K)
+        gi, gv = ids[s].cpu().numpy()[rows], vals[s].cpu().numpy()[rows]
+        if not ((gi == ri).all() and (gv.view(np.uint32) == rv.view(np.uint32)).all()):
+            log(f"PARITY FAILED on matrix {s}; no throughput reported")
+            return 1
+    log("parity vs oracle ok (bit-exact ids and values on sampled rows)")
+    # one step = the top-K of every matrix, captured as a HIP graph
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(w.steps):
+            moe.vocab_topk(xs[s], w.K, ws, ids[s], vals[s])
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    for s in range(w.steps):
+        if not (torch.equal(ids[s], eager[s][0]) and torch.equal(vals[s].view(torch.int32), eager[s][1].view(torch.int32))):
+            log(f"graph replay differs from eager on matrix {s}; no throughput reported")
+            return 1
+    rows_per_step = w.steps * w.R
+    value = rows_per_step / (ms_step / 1e3)
+    log(f"step {ms_step * 1e3:.1f} us for {w.steps} matrices of {w.R} rows -> {value:,.0f} rows/s")
+    # each kernel alone: graphs of back-to-back launches cycling the matrices
+    stages = {}
+    for st, name in ((0, "chunk_max"), (1, "topk_rows")):
+        gs = torch.cuda.CUDAGraph()
+        per = 4 * w.steps
+        with torch.cuda.graph(gs):
+            for i in range(per):
+                moe.vocab_topk(xs[i % w.steps], w.K, ws, ids[i % w.steps], vals[i % w.steps], stage=st)
+        gs.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.stage_reps // per)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            gs.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * per)
+        wb = vocab_work(w, st)
+        stages[name] = {"us": round(us, 3), "bytes": int(wb), "flops": 0, "GBps": round(wb / us / 1e3, 1), "TFLOPs": 0.0}
+        log(f"  {name:18s} {us:8.2f} us  {wb / 1e6:9.3f} MB  {wb / us / 1e3:8.1f} GB/s")
+        del gs
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    st = stages["chunk_max"]
+    roof = {"bound": "hbm", "achieved": st["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(st["GBps"] / HBM_PEAK_GBS, 4), "kernel": "chunk_max", "bytes_per_launch": st["bytes"],
+            "flops_per_launch": 0, "avg_us": st["us"], "traffic": traffic_from_profiles(args.workload, "chunk_max")}
+    out = {
+        "metric": "top-K rows/s", "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded generator)",
+        "config": {"workload": f"exact top-{w.K} of {w.R} rows x {w.V} fp32 logits (softcapped normal), "
+                               f"{w.steps} matrices cycled", "parallelism": "single GPU"},
+        "roofline": roof, "stages": stages,
+    }
+    if not args.no_cpu:
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            oracle.vocab_topk(host[0][n % w.R:n % w.R + 1], w.K)
+            n += 1
+        el = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": n / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} rows of the first matrix, one full sort each, {el:.1f} s"}
+        log(f"cpu oracle: {n / el:.1f} rows/s")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # ------------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=sorted(PLAN))
+    ap.add_argument("--workload", default="decode", choices=sorted(PLAN) + sorted(gen.VOCAB_WORKLOADS))
     ap.add_argument("--stage-reps", type=int, default=200, help="timed launches per stage")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -186,6 +298,8 @@ def main() -> int:
               "in DESIGN.md); run with --gpus 1", file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.workload in gen.VOCAB_WORKLOADS:
+        return main_vocab(args)
     dev = torch.device("cuda:0")
     w = gen.WORKLOADS[args.workload]
     n_layers, calls = PLAN[args.workload]

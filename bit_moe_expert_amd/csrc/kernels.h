@@ -46,8 +46,9 @@ hipError_t launch_combine(const Ctx& c);
 constexpr int kVocabMaxK = 128;
 constexpr int kVocabMaxChunks = 8192;
 inline int vocab_chunk(int K) { return K <= 32 ? 1024 : K <= 64 ? 512 : 256; }
+// stage: -1 both kernels, 0 the chunk maxima only, 1 the selection only
 hipError_t launch_vocab_topk(int R, int V, int K, const float* logits, uint32_t* cmax, int32_t* ids, float* vals,
-                             hipStream_t stream);
+                             hipStream_t stream, int stage);
 hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* out, hipStream_t stream);
 
 // Block-map tile height (rows of one expert group per tile).

@@ -387,8 +387,9 @@ size_t moe_vocab_topk_workspace_bytes(int32_t R, int32_t V, int32_t K) {
   return up((size_t)std::max<int32_t>(R, 1) * (size_t)nch * 4);
 }
 
-int moe_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids, float* vals, void* ws,
-                   size_t ws_bytes, void* stream) {
+int moe_vocab_topk_stage(int32_t stage, int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids,
+                         float* vals, void* ws, size_t ws_bytes, void* stream) {
+  if (stage < -1 || stage > 1) return fail(MOE_EINVAL, "stage %d is not 0 or 1", stage);
   if (R < 0) return fail(MOE_EINVAL, "R = %d is negative", R);
   if (V < 1 || K < 1 || K > V) return fail(MOE_EUNSUPPORTED, "need 1 <= K <= V (K = %d, V = %d)", K, V);
   if (K > kVocabMaxK) return fail(MOE_EUNSUPPORTED, "K = %d exceeds %d", K, kVocabMaxK);
@@ -403,9 +404,14 @@ int moe_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t
   if (!aligned(ws, 256)) return fail(MOE_EINVAL, "workspace not 256-byte aligned");
   if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   const hipError_t e = launch_vocab_topk(R, V, K, logits, static_cast<uint32_t*>(ws), ids, vals,
-                                         static_cast<hipStream_t>(stream));
+                                         static_cast<hipStream_t>(stream), stage);
   if (e != hipSuccess) return fail(MOE_EHIP, "launch of the top-K kernels failed: %s", hipGetErrorString(e));
   return MOE_OK;
+}
+
+int moe_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids, float* vals, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return moe_vocab_topk_stage(-1, R, V, K, logits, ids, vals, ws, ws_bytes, stream);
 }
 
 const char* moe_status_str(int status) {

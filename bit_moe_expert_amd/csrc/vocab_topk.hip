@@ -10,11 +10,13 @@
 //   k_chunk_max   streams the logits once (the HBM-bound part): one wave per chunk of C entries,
 //                 16-byte loads, writing each chunk's largest order-preserving key.
 //   k_topk_rows   one 1024-thread block per row: a radix select over the row's chunk keys picks
-//                 K chunks; their K * C entries are loaded into LDS as keys and a second radix
-//                 select picks the K entries; a rank count orders them. Only K / (V / C) of the
-//                 row is read a second time.
+//                 K chunks; their entries are read once more and reduced to sub-chunk maxima, a
+//                 second select picks K sub-chunks, and a third picks the K entries among those
+//                 sub-chunks' entries; a rank count orders them. Only K / (V / C) of the row is
+//                 read a second time.
 // Radix select: four passes over 8-bit digits from the top, each a histogram of the entries that
-// still match the chosen prefix (per-wave LDS histograms, then summed), which leaves the K-th
+// still match the chosen prefix (per-wave LDS histograms that one wave then reads and sums in
+// registers), which leaves the K-th
 // largest key tau, how many entries lie above it, and how many equal it. When more entries equal
 // tau than are still needed, the needed ones are those of lowest index, found by a radix select
 // over the inverted indices of the tied entries.
@@ -81,6 +83,23 @@ struct Sel {
   int above, eq;
 };
 
+// Inclusive prefix sum over the wave's lanes: Hillis-Steele steps of 1, 2, 4, 8 lanes inside each
+// row of 16 (DPP row shifts, zero from outside the row), then the earlier rows' totals.
+template <int CTRL>
+__device__ __forceinline__ int dpp_shr0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += dpp_shr0<0x111>(v);  // row_shr:1
+  v += dpp_shr0<0x112>(v);  // row_shr:2
+  v += dpp_shr0<0x114>(v);  // row_shr:4
+  v += dpp_shr0<0x118>(v);  // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  return v + (row == 0 ? 0 : row == 1 ? t0 : row == 2 ? t0 + t1 : t0 + t1 + t2);
+}
+
 template <class Part, class Val>
 __device__ __forceinline__ Sel radix_select(int n, int K, Part part, Val val, uint32_t* s_hist /* kTkWaves x 256 */,
                                             int* s_ctl /* 4 ints */) {
@@ -88,42 +107,40 @@ __device__ __forceinline__ Sel radix_select(int n, int K, Part part, Val val, ui
   uint32_t prefix = 0u, mask = 0u;
   int rem = K;  // how many are still to be taken at or below the current prefix
   int eq = 0;
+  uint32_t* h = s_hist + wave * 256;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kTkWaves * 256; i += kTkThreads) s_hist[i] = 0u;
-    __syncthreads();
-    uint32_t* h = s_hist + wave * 256;
+    // this wave's histogram: cleared and filled by the wave itself (a wave's LDS accesses
+    // complete in order, so no barrier is needed between the two)
+    *reinterpret_cast<uint4*>(h + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tid; i < n; i += kTkThreads)
       if (part(i)) {
         const uint32_t v = val(i);
         if ((v & mask) == prefix) atomicAdd(&h[(v >> shift) & 255u], 1u);
       }
     __syncthreads();
-    // the per-wave histograms summed into wave 0's
-    for (int b = tid; b < 256; b += kTkThreads) {
-      uint32_t t = 0u;
-      for (int w = 0; w < kTkWaves; ++w) t += s_hist[w * 256 + b];
-      s_hist[b] = t;
-    }
-    __syncthreads();
     if (wave == 0) {
-      // lane l holds digits 4l .. 4l + 3; find the digit where the count from the top reaches rem
-      uint32_t hb[4];
+      // lane l sums digits 255 - 4l .. 252 - 4l (hb[0] the highest) over every wave's
+      // histogram; a prefix sum over the lanes then counts from the top digit down, and the lane
+      // holding the digit where that count reaches rem reports it
+      const int hi = 252 - 4 * lane;
+      uint32_t hb[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hb[q] = s_hist[4 * lane + q];
-      const int mine = (int)(hb[0] + hb[1] + hb[2] + hb[3]);
-      int incl = mine;  // sum over lanes >= this one
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_down(incl, off, 64);
-        if (lane + off < 64) incl += t;
+      for (int w = 0; w < kTkWaves; ++w) {
+        const uint4 t = *reinterpret_cast<const uint4*>(s_hist + w * 256 + hi);
+        hb[0] += t.w;
+        hb[1] += t.z;
+        hb[2] += t.y;
+        hb[3] += t.x;
       }
+      const int mine = (int)(hb[0] + hb[1] + hb[2] + hb[3]);
+      const int incl = wave_prefix_sum(mine);  // over lanes <= this one, i.e. digits >= hi
       const int excl = incl - mine;
       if (excl < rem && rem <= incl) {
         int cum = excl;
 #pragma unroll
-        for (int q = 3; q >= 0; --q) {
+        for (int q = 0; q < 4; ++q) {
           if (cum + (int)hb[q] >= rem) {
-            s_ctl[0] = 4 * lane + q;
+            s_ctl[0] = hi + 3 - q;
             s_ctl[1] = cum;  // participants above this digit
             s_ctl[2] = (int)hb[q];
             break;
@@ -138,8 +155,8 @@ __device__ __forceinline__ Sel radix_select(int n, int K, Part part, Val val, ui
     eq = s_ctl[2];
     prefix |= digit << shift;
     mask |= 255u << shift;
-    __syncthreads();
   }
+  __syncthreads();  // every thread has read s_ctl before anyone writes it again
   Sel s;
   s.tau = prefix;
   s.above = K - rem;
@@ -182,28 +199,128 @@ __device__ __forceinline__ void select_k(int n, int K, Part part, Val val, Idx i
   __syncthreads();
 }
 
-// One block per row. LDS (static, about 146 KB of gfx950's 160 KB): the keys, first of the
-// row's chunk maxima and then of the chosen chunks' entries (max(nch, K * C) <= kTkMaxKeys);
-// the K chosen chunks; the K chosen positions; per-wave histograms; control words.
-constexpr int kTkMaxKeys = 32768;
+// One block per row. A fast path (step 0 below) ranks the entries >= the K-th largest chunk
+// maximum directly; when ties make those too many, three exact reductions in a row:
+//   1. the K chunks with the largest maxima among the row's nch chunk maxima;
+//   2. the chosen chunks' entries are read once (every wave issues all of its loads first) and
+//      cut into sub-chunks of S = C / 64 consecutive entries, one per lane; the K sub-chunks with
+//      the largest maxima are chosen among the K * 64 (the chunk argument again: the chosen
+//      chunks hold the global top K, so the top K of their entries is the global top K);
+//   3. the K entries among the K * S entries of the chosen sub-chunks, re-read from memory.
+// Ties between equal maxima go to the lower range, ranges being ordered by their first entry.
+// LDS: up to kTkMaxKeys keys, the chosen chunks, sub-chunks and entries, per-wave histograms.
+constexpr int kTkMaxKeys = 8192;  // >= nch and >= K * 64
 constexpr int kTkMaxK = 128;
+constexpr int kTkMaxS = 16;       // C / 64 for C <= 1024
+constexpr int kTkCap = 1024;      // candidates of the fast path (one per thread for the rank)
 
+template <bool VEC>
 __global__ __launch_bounds__(kTkThreads) void k_topk_rows(int V, int K, int C, int nch, const float* __restrict__ logits,
                                                           const uint32_t* __restrict__ cmax, int32_t* __restrict__ ids,
                                                           float* __restrict__ vals) {
   __shared__ uint32_t s_key[kTkMaxKeys];
+  __shared__ uint32_t s_fin[kTkMaxK * kTkMaxS];  // keys of the chosen sub-chunks' entries
   __shared__ int s_chunk[kTkMaxK];
+  __shared__ int s_sub[kTkMaxK];
   __shared__ int s_pos[kTkMaxK];
   __shared__ uint32_t s_hist[kTkWaves * 256];
   __shared__ int s_ctl[4];
-  const int tid = threadIdx.x, r = blockIdx.x;
+  __shared__ uint32_t s_ck[kTkCap];  // fast path: candidate keys
+  __shared__ int s_ci[kTkCap];       // ... and their indices
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = blockIdx.x;
   const float* row = logits + (size_t)r * V;
-
-  // 1. the K chunks with the largest maxima (lower chunk first on equal maxima); all of them
-  //    when there are no more than K
-  const int nsel = min(K, nch);
+  const int S = C / 64;
   for (int i = tid; i < nch; i += kTkThreads) s_key[i] = cmax[(size_t)r * nch + i];
   __syncthreads();
+
+  // 0. Fast path. tau1 = the K-th largest chunk maximum (0 when there are no more than K
+  //    chunks). Those K maxima are K entries >= tau1, so every entry of the top K is >= tau1 and
+  //    the entries >= tau1 (all in chunks whose maximum is >= tau1) hold the answer. When there
+  //    are at most kTkMaxK such chunks and kTkCap such entries (the usual case; ties at the top
+  //    of many chunks are not), they are gathered and ranked directly.
+  {
+    uint32_t tau1 = 0u;
+    if (nch > K) {
+      auto all = [](int) { return true; };
+      auto ck = [&](int i) { return s_key[i]; };
+      tau1 = radix_select(nch, K, all, ck, s_hist, s_ctl).tau;
+    }
+    if (tid == 0) s_ctl[3] = 0;
+    __syncthreads();
+    for (int i = tid; i < nch; i += kTkThreads)
+      if (s_key[i] >= tau1) append(s_chunk, kTkMaxK, s_ctl, i);
+    __syncthreads();
+    const int nc = s_ctl[3];
+    __syncthreads();
+    if (nc <= kTkMaxK) {
+      if (tid == 0) s_ctl[3] = 0;
+      __syncthreads();
+      for (int q0 = wave; q0 < nc; q0 += 4 * kTkWaves) {
+        float v[4][kTkMaxS];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u * kTkWaves;
+          const int e0 = (q < nc ? min(max(s_chunk[q], 0), nch - 1) : 0) * C + lane * S;
+#pragma unroll
+          for (int j = 0; j < kTkMaxS; j += 4) {
+            if (j >= S) break;
+            if (VEC) {
+              const float4 t =
+                  e0 + j < V ? *reinterpret_cast<const float4*>(row + e0 + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+              v[u][j] = t.x;
+              v[u][j + 1] = t.y;
+              v[u][j + 2] = t.z;
+              v[u][j + 3] = t.w;
+            } else {
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) v[u][j + jj] = e0 + j + jj < V ? row[e0 + j + jj] : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u * kTkWaves;
+          if (q >= nc) break;
+          const int e0 = min(max(s_chunk[q], 0), nch - 1) * C + lane * S;
+#pragma unroll
+          for (int j = 0; j < kTkMaxS; ++j)
+            if (j < S && e0 + j < V) {
+              const uint32_t kk = logit_key(v[u][j]);
+              if (kk >= tau1) {
+                const int slot = atomicAdd(&s_ctl[3], 1);
+                if (slot < kTkCap) {
+                  s_ck[slot] = kk;
+                  s_ci[slot] = e0 + j;
+                }
+              }
+            }
+        }
+      }
+      __syncthreads();
+      const int M = s_ctl[3];
+      if (M <= kTkCap) {
+        // rank of each candidate by (key desc, index asc); the first K go out
+        if (tid < M) {
+          const uint32_t kp = s_ck[tid];
+          const int ip = s_ci[tid];
+          int rank = 0;
+          for (int j = 0; j < M; ++j) {
+            const uint32_t kj = s_ck[j];
+            rank += (kj > kp || (kj == kp && s_ci[j] < ip)) ? 1 : 0;
+          }
+          if (rank < K) {
+            ids[(size_t)r * K + rank] = ip;
+            vals[(size_t)r * K + rank] = row[min(max(ip, 0), V - 1)];
+          }
+        }
+        return;
+      }
+    }
+    __syncthreads();  // the general path below starts from the chunk keys, still in s_key
+  }
+
+  // 1. chunks: all of them when there are no more than K
+  const int nsel = min(K, nch);
   if (nch <= K) {
     for (int i = tid; i < nch; i += kTkThreads) s_chunk[i] = i;
     __syncthreads();
@@ -213,35 +330,86 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(int V, int K, int C, i
     auto cid = [](int i) { return i; };
     select_k(nch, K, all, ck, cid, s_chunk, s_hist, s_ctl);
   }
-  // 2. their entries as keys: slot q holds chunk s_chunk[q]; entries past V are empty (key 0)
-  const int ncand = nsel * C;
-  for (int p = tid; p < ncand; p += kTkThreads) {
-    const int q = p / C, o = p - q * C;
-    const int i = min(max(s_chunk[q], 0), nch - 1) * C + o;
-    s_key[p] = i < V ? logit_key(row[i]) : 0u;
+  // 2. sub-chunk maxima of the chosen chunks: slot q's lane l covers entries
+  //    chunk * C + l * S .. + S - 1; key 0 when the sub-chunk lies past V
+  auto chunk_of = [&](int q) { return min(max(s_chunk[q], 0), nch - 1); };
+  for (int q0 = wave; q0 < nsel; q0 += 4 * kTkWaves) {
+    float v[4][kTkMaxS];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * kTkWaves;
+      const int e0 = (q < nsel ? chunk_of(q) : 0) * C + lane * S;
+#pragma unroll
+      for (int j = 0; j < kTkMaxS; j += 4) {
+        if (j >= S) break;
+        if (VEC) {
+          const float4 t = e0 + j < V ? *reinterpret_cast<const float4*>(row + e0 + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+          v[u][j] = t.x;
+          v[u][j + 1] = t.y;
+          v[u][j + 2] = t.z;
+          v[u][j + 3] = t.w;
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v[u][j + jj] = e0 + j + jj < V ? row[e0 + j + jj] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * kTkWaves;
+      if (q >= nsel) break;
+      const int e0 = chunk_of(q) * C + lane * S;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int j = 0; j < kTkMaxS; ++j)
+        if (j < S && e0 + j < V) m = max(m, logit_key(v[u][j]));
+      s_key[q * 64 + lane] = m;
+    }
   }
   __syncthreads();
-  // 3. the K entries among them (empty slots never take part)
-  auto live = [&](int p) { return s_key[p] != 0u; };
-  auto key = [&](int p) { return s_key[p]; };
-  auto idx = [&](int p) {
-    const int q = p / C;
-    return min(max(s_chunk[q], 0), nch - 1) * C + (p - q * C);
+  const int nsub = nsel * 64;
+  auto sub_first = [&](int i) { return chunk_of(i >> 6) * C + (i & 63) * S; };  // first entry of sub-chunk i
+  // When every chunk was kept the live sub-chunks are 0 .. ceil(V / S) - 1, and there may be no
+  // more than K of them: then all are kept. Otherwise K chosen chunks hold at least K live ones.
+  const int nlive = nch <= K ? (V + S - 1) / S : nsub;
+  const int nsubsel = min(K, nlive);
+  if (nlive <= K) {
+    for (int i = tid; i < nlive; i += kTkThreads) s_sub[i] = i;
+    __syncthreads();
+  } else {
+    auto live = [&](int i) { return s_key[i] != 0u; };
+    auto sk = [&](int i) { return s_key[i]; };
+    select_k(nsub, K, live, sk, sub_first, s_sub, s_hist, s_ctl);
+  }
+  // 3. the chosen sub-chunks' entries (position p = slot * S + offset), and the K among them
+  auto elem = [&](int p) {
+    const int u = p / S;
+    return sub_first(min(max(s_sub[u], 0), nsub - 1)) + (p - u * S);
   };
-  select_k(ncand, K, live, key, idx, s_pos, s_hist, s_ctl);
-  // 4. order: rank of each chosen entry among the K by (key desc, index asc)
-  // (positions and indices are clamped to their ranges, so a selection that went wrong could
-  // only give wrong answers, never an access outside the buffers)
-  auto pos = [&](int j) { return min(max(s_pos[j], 0), ncand - 1); };
+  const int nfin = nsubsel * S;
+  for (int p = tid; p < nfin; p += kTkThreads) {
+    const int i = elem(p);
+    s_fin[p] = i < V ? logit_key(row[i]) : 0u;
+  }
+  __syncthreads();
+  {
+    auto live = [&](int p) { return s_fin[p] != 0u; };
+    auto fk = [&](int p) { return s_fin[p]; };
+    select_k(nfin, K, live, fk, elem, s_pos, s_hist, s_ctl);
+  }
+  // 4. order: rank of each chosen entry among the K by (key desc, index asc). Positions and
+  //    indices are clamped to their ranges, so a selection gone wrong could give wrong answers
+  //    but never an access outside the buffers.
+  auto pos = [&](int j) { return min(max(s_pos[j], 0), nfin - 1); };
   if (tid < K) {
     const int p = pos(tid);
-    const uint32_t kp = s_key[p];
-    const int ip = idx(p);
+    const uint32_t kp = s_fin[p];
+    const int ip = elem(p);
     int rank = 0;
     for (int j = 0; j < K; ++j) {
       const int pj = pos(j);
-      const uint32_t kj = s_key[pj];
-      const int ij = idx(pj);
+      const uint32_t kj = s_fin[pj];
+      const int ij = elem(pj);
       rank += (kj > kp || (kj == kp && ij < ip)) ? 1 : 0;
     }
     rank = min(rank, K - 1);
@@ -252,19 +420,25 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(int V, int K, int C, i
 
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_vocab_topk(int R, int V, int K, const float* logits, uint32_t* cmax, int32_t* ids, float* vals,
-                             hipStream_t stream) {
+                             hipStream_t stream, int stage) {
   const int C = vocab_chunk(K), nch = (V + C - 1) / C;
-  static_assert(kVocabMaxK <= kTkMaxK && kVocabMaxK * 256 <= kTkMaxKeys && 1024 * 32 <= kTkMaxKeys,
-                "K * C and the chunk count fit the LDS key buffer");
+  static_assert(kVocabMaxK <= kTkMaxK && kVocabMaxK * 64 <= kTkMaxKeys && kVocabMaxChunks <= kTkMaxKeys,
+                "the chunk keys and the sub-chunk keys fit the LDS key buffer");
   const dim3 g1((nch + 3) / 4, R);
   const bool vec = (V % 4 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
+  if (stage != 1) {
+    if (vec)
+      hipLaunchKernelGGL(k_chunk_max<true>, g1, dim3(256), 0, stream, V, C, nch, logits, cmax);
+    else
+      hipLaunchKernelGGL(k_chunk_max<false>, g1, dim3(256), 0, stream, V, C, nch, logits, cmax);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || stage == 0) return e;
+  }
   if (vec)
-    hipLaunchKernelGGL(k_chunk_max<true>, g1, dim3(256), 0, stream, V, C, nch, logits, cmax);
+    hipLaunchKernelGGL(k_topk_rows<true>, dim3(R), dim3(kTkThreads), 0, stream, V, K, C, nch, logits, cmax, ids, vals);
   else
-    hipLaunchKernelGGL(k_chunk_max<false>, g1, dim3(256), 0, stream, V, C, nch, logits, cmax);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk_rows, dim3(R), dim3(kTkThreads), 0, stream, V, K, C, nch, logits, cmax, ids, vals);
+    hipLaunchKernelGGL(k_topk_rows<false>, dim3(R), dim3(kTkThreads), 0, stream, V, K, C, nch, logits, cmax, ids,
+                       vals);
   return hipGetLastError();
 }
 

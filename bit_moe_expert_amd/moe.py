@@ -76,8 +76,9 @@ def lib():
         L.moe_vocab_topk_workspace_bytes.argtypes = [i32, i32, i32]
         L.moe_vocab_topk_workspace_bytes.restype = sz
         L.moe_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_vocab_topk_stage.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_launch_stage",
-                  "moe_vocab_topk"):
+                  "moe_vocab_topk", "moe_vocab_topk_stage"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -284,9 +285,10 @@ def vocab_topk_workspace_bytes(R: int, V: int, K: int) -> int:
 
 
 def vocab_topk(logits: torch.Tensor, K: int, ws: Optional[torch.Tensor] = None, ids: Optional[torch.Tensor] = None,
-               vals: Optional[torch.Tensor] = None):
+               vals: Optional[torch.Tensor] = None, stage: int = -1):
     """moe_vocab_topk: exact top-K of each row of fp32 logits [R][V] by (value desc, index asc).
-    Returns (ids [R][K] int32, vals [R][K] fp32)."""
+    Returns (ids [R][K] int32, vals [R][K] fp32). stage 0 / 1 runs one of its two kernels alone
+    (moe_vocab_topk_stage, for timing)."""
     if logits.dim() != 2:
         raise ValueError("logits must be [R][V]")
     R, V = logits.shape
@@ -297,8 +299,8 @@ def vocab_topk(logits: torch.Tensor, K: int, ws: Optional[torch.Tensor] = None, 
     ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
     ids = torch.empty((R, K), dtype=torch.int32, device=dev) if ids is None else ids
     vals = torch.empty((R, K), dtype=torch.float32, device=dev) if vals is None else vals
-    rc = lib().moe_vocab_topk(R, V, K, _ptr(logits, torch.float32, "logits", dev), _ptr(ids, torch.int32, "ids", dev),
-                              _ptr(vals, torch.float32, "vals", dev), _ptr(ws, torch.uint8, "ws", dev), ws.numel(),
-                              _stream(dev))
-    _check(rc, "moe_vocab_topk")
+    rc = lib().moe_vocab_topk_stage(stage, R, V, K, _ptr(logits, torch.float32, "logits", dev),
+                                    _ptr(ids, torch.int32, "ids", dev), _ptr(vals, torch.float32, "vals", dev),
+                                    _ptr(ws, torch.uint8, "ws", dev), ws.numel(), _stream(dev))
+    _check(rc, "moe_vocab_topk" if stage < 0 else f"moe_vocab_topk_stage({stage})")
     return ids, vals

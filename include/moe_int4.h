@@ -194,6 +194,11 @@ int moe_launch_stage(int32_t stage, const moe_dims* dims, int32_t T, const uint1
 size_t moe_vocab_topk_workspace_bytes(int32_t R, int32_t V, int32_t K);  /* 0 if unsupported */
 int moe_vocab_topk(int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids, float* vals, void* ws,
                    size_t ws_bytes, void* stream);
+/* Profiling: moe_vocab_topk's kernels one at a time, with its arguments and checks. Stage 0
+ * writes the chunk maxima into ws; stage 1 selects from the chunk maxima ws already holds (run
+ * stage 0 or moe_vocab_topk on that ws first). For per-kernel timing only. */
+int moe_vocab_topk_stage(int32_t stage, int32_t R, int32_t V, int32_t K, const float* logits, int32_t* ids,
+                         float* vals, void* ws, size_t ws_bytes, void* stream);
 
 const char* moe_status_str(int status);
 const char* moe_last_error(void);
