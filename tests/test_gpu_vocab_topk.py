@@ -84,3 +84,14 @@ def test_vocab_topk_zero_rows_and_repeat():
     b = moe.vocab_topk(xt, 64)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_vocab_topk_full_width_ties_take_the_general_path():
+    """Rows of the pages' width whose maximum is shared by every chunk (zeros; four values): more
+    than 128 chunks reach the K-th largest chunk maximum, so the three-level path runs."""
+    rng = np.random.default_rng(21)
+    V = 262144
+    x = np.stack([np.zeros(V, np.float32), rng.integers(0, 4, V).astype(np.float32),
+                  np.repeat(rng.integers(0, 3, V // 1000 + 1), 1000)[:V].astype(np.float32)])
+    for K in (64, 128):
+        _check(x, K, f"full-width ties K={K}")
