@@ -58,9 +58,10 @@
 #define ORC_TILE_ROWS 32
 
 typedef struct {
-  const uint8_t* codes;    /* [n_mat][out][in/2], low nibble = even input index */
+  const uint8_t* codes;    /* [n_mat][out][in * bits / 8]: each row a little-endian bit stream */
   const uint16_t* scales;  /* [n_mat][out][in/64] bf16 bits */
   const uint16_t* biases;  /* [n_mat][out][in/64] bf16 bits */
+  int32_t bits;            /* bits per code: 4 (also when 0), 3 or 2 */
 } orc_q4;
 
 typedef struct {
@@ -214,13 +215,22 @@ int oracle_route_meta(int32_t T, int32_t E, int32_t k, int32_t has_shared, const
 
 /* ---------------------------------------------------------------- 4. dequantisation
  * Group g of row r covers inputs 64g .. 64g+63 and has one bf16 scale s and one bf16 bias b.
- * Input c of row r has code q = (byte >> (4 * (c & 1))) & 15 of byte c/2 (two codes per byte,
- * the even input in the low nibble -- reading). The weight is w = s * q + b evaluated in fp32
- * (s * q is exact in fp32, so this is one rounding) and then rounded to bf16, the operand type
- * of the matrix units. */
+ * With 4-bit codes, input c of row r has code q = (byte >> (4 * (c & 1))) & 15 of byte c/2 (two
+ * codes per byte, the even input in the low nibble -- reading). In general a row's codes form a
+ * little-endian bit stream: code c occupies bits [bits * c, bits * c + bits) of the row's bytes
+ * (bit j of the stream is bit j % 8 of byte j / 8), which for 4 bits is the nibble order above
+ * (reading for 2- and 3-bit codes, a variant [DIFFGEMMA "The physics ceiling: why 300+ tok/s is
+ * blocked"] names but does not define). The weight is w = s * q + b evaluated in fp32 (s * q is
+ * exact in fp32, so this is one rounding) and then rounded to bf16, the operand type of the
+ * matrix units. */
 static uint16_t orc_dequant_one(const orc_q4* m, int64_t row, int32_t in_dim, int32_t c) {
-  uint8_t byte = m->codes[row * (in_dim / 2) + c / 2];
-  uint32_t q = (c & 1) ? (uint32_t)(byte >> 4) : (uint32_t)(byte & 15u);
+  const int32_t bits = m->bits ? m->bits : 4;
+  const int64_t row_bytes = (int64_t)in_dim * bits / 8;
+  const uint8_t* rp = m->codes + row * row_bytes;
+  const int64_t bit = (int64_t)c * bits;
+  uint32_t two = rp[bit / 8];
+  if (bit / 8 + 1 < row_bytes) two |= (uint32_t)rp[bit / 8 + 1] << 8;
+  const uint32_t q = (two >> (bit % 8)) & ((1u << bits) - 1u);
   int64_t gi = row * (in_dim / ORC_GROUP) + c / ORC_GROUP;
   float s = (float)orc_bf16_value(m->scales[gi]);
   float b = (float)orc_bf16_value(m->biases[gi]);
@@ -229,14 +239,19 @@ static uint16_t orc_dequant_one(const orc_q4* m, int64_t row, int32_t in_dim, in
 }
 
 /* rows counts rows over all matrices (n_mat * out); out_bf16 is [rows][in_dim]. */
-int oracle_dequant(int64_t rows, int32_t in_dim, const uint8_t* codes, const uint16_t* scales,
-                   const uint16_t* biases, uint16_t* out_bf16) {
-  if (in_dim % ORC_GROUP) return 1;
-  orc_q4 m = {codes, scales, biases};
+int oracle_dequant_bits(int64_t rows, int32_t in_dim, int32_t bits, const uint8_t* codes, const uint16_t* scales,
+                        const uint16_t* biases, uint16_t* out_bf16) {
+  if (in_dim % ORC_GROUP || (bits != 2 && bits != 3 && bits != 4)) return 1;
+  orc_q4 m = {codes, scales, biases, bits};
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int32_t c = 0; c < in_dim; ++c) out_bf16[r * in_dim + c] = orc_dequant_one(&m, r, in_dim, c);
   return 0;
+}
+
+int oracle_dequant(int64_t rows, int32_t in_dim, const uint8_t* codes, const uint16_t* scales,
+                   const uint16_t* biases, uint16_t* out_bf16) {
+  return oracle_dequant_bits(rows, in_dim, 4, codes, scales, biases, out_bf16);
 }
 
 /* Dequantise matrix `mat` ([out][in]) of a projection into doubles (values are bf16). */

@@ -31,7 +31,8 @@ def build(verbose: bool = False) -> str:
 
 
 class _Q4(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("bits", ctypes.c_int32)]
 
 
 class _FFN(ctypes.Structure):
@@ -51,13 +52,14 @@ def lib():
         L.oracle_topk_softmax.argtypes = [i32, i32, i32, vp, vp, vp]
         L.oracle_route_meta.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
         L.oracle_dequant.argtypes = [i64, i32, vp, vp, vp, vp]
+        L.oracle_dequant_bits.argtypes = [i64, i32, i32, vp, vp, vp, vp]
         L.oracle_forward_layer.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(_FFN),
                                            ctypes.POINTER(_FFN), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.oracle_forward_tokens.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(_FFN),
                                             ctypes.POINTER(_FFN), i32, vp, vp, vp, vp]
         L.oracle_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp]
         for f in ("oracle_router_logits", "oracle_topk_softmax", "oracle_route_meta", "oracle_dequant",
-                  "oracle_forward_layer", "oracle_forward_tokens", "oracle_vocab_topk"):
+                  "oracle_forward_layer", "oracle_forward_tokens", "oracle_vocab_topk", "oracle_dequant_bits"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -89,7 +91,7 @@ def _ffn(w: Optional[dict]):
         s = _c(w[name]["scales"], np.uint16)
         b = _c(w[name]["biases"], np.uint16)
         keep += [c, s, b]
-        q[name] = _Q4(_p(c), _p(s), _p(b))
+        q[name] = _Q4(_p(c), _p(s), _p(b), int(w[name].get("bits", 4)))
     return _FFN(q["gate"], q["up"], q["down"]), keep
 
 
@@ -153,15 +155,15 @@ def route_meta(ids, E: int, has_shared: bool):
             "tiles": tiles[: n[0]].copy(), "n_tiles": int(n[0])}
 
 
-def dequant(codes, scales, biases) -> np.ndarray:
-    """codes [..., out, in/2] -> bf16 bits [..., out, in]."""
+def dequant(codes, scales, biases, bits: int = 4) -> np.ndarray:
+    """codes [..., out, in * bits / 8] -> bf16 bits [..., out, in]."""
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint16)
     biases = _c(biases, np.uint16)
-    in_dim = codes.shape[-1] * 2
+    in_dim = codes.shape[-1] * 8 // bits
     rows = codes.size // codes.shape[-1]
     out = np.empty(codes.shape[:-1] + (in_dim,), np.uint16)
-    rc = lib().oracle_dequant(rows, in_dim, _p(codes), _p(scales), _p(biases), _p(out))
+    rc = lib().oracle_dequant_bits(rows, in_dim, bits, _p(codes), _p(scales), _p(biases), _p(out))
     if rc:
         raise ValueError(f"oracle_dequant rc={rc}")
     return out

@@ -406,11 +406,14 @@ def test_expert_selection_uses_the_routed_experts_weights():
         assert (out["y"] == _bf16(want)).all()
 
 
-def _random_layer(rng, T, d, E, k, I, Is):
+def _random_layer(rng, T, d, E, k, I, Is, bits=4):
     def proj(n, o, i):
-        return {"codes": rng.integers(0, 256, (n, o, i // 2), dtype=np.uint8),
-                "scales": _bf16(np.abs(rng.standard_normal((n, o, i // 64))) * 0.02),
-                "biases": _bf16(rng.standard_normal((n, o, i // 64)) * 0.1)}
+        p = {"codes": rng.integers(0, 256, (n, o, i * bits // 8), dtype=np.uint8),
+             "scales": _bf16(np.abs(rng.standard_normal((n, o, i // 64))) * 0.02),
+             "biases": _bf16(rng.standard_normal((n, o, i // 64)) * 0.1)}
+        if bits != 4:
+            p["bits"] = bits
+        return p
     routed = {"gate": proj(E, I, d), "up": proj(E, I, d), "down": proj(E, d, I)}
     shared = {"gate": proj(1, Is, d), "up": proj(1, Is, d), "down": proj(1, d, Is)} if Is else None
     x = _bf16(rng.standard_normal((T, d)))
@@ -425,8 +428,12 @@ def _python_dense_forward(x, routed, shared, ids, w):
     xf = oracle.bf16_to_f32(x).astype(np.float64)
 
     def deq(m, mat, row, c, in_dim):
-        byte = int(m["codes"][mat, row, c // 2])
-        q = (byte >> 4) if (c & 1) else (byte & 15)
+        bits = m.get("bits", 4)
+        if bits == 4:
+            byte = int(m["codes"][mat, row, c // 2])
+            q = (byte >> 4) if (c & 1) else (byte & 15)
+        else:  # the row's bytes as one little-endian integer, code c at bits [bits*c, bits*c + bits)
+            q = (int.from_bytes(bytes(m["codes"][mat, row]), "little") >> (bits * c)) & ((1 << bits) - 1)
         s = np.float32(_bits_to_f(int(m["scales"][mat, row, c // 64])))
         b = np.float32(_bits_to_f(int(m["biases"][mat, row, c // 64])))
         return _bits_to_f(int(_bf16([np.float32(s * np.float32(q)) + b])[0]))
@@ -470,6 +477,56 @@ def test_grouped_forward_equals_dense_brute_force():
     ids, w = oracle.topk_softmax(oracle.router_logits(x, wr), k)
     assert (out["topk_ids"] == ids).all() and (out["topk_w"] == w).all()
     assert (out["y"] == _python_dense_forward(x, routed, shared, ids, w)).all()
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_lowbit_grouped_forward_equals_dense_brute_force(bits):
+    rng = np.random.default_rng(50 + bits)
+    T, d, E, k, I, Is = 3, 64, 4, 2, 64, 64
+    x, wr, routed, shared = _random_layer(rng, T, d, E, k, I, Is, bits=bits)
+    out = oracle.forward_layer(x, wr, routed, shared, k)
+    ids, w = oracle.topk_softmax(oracle.router_logits(x, wr), k)
+    assert (out["y"] == _python_dense_forward(x, routed, shared, ids, w)).all()
+
+
+def _pack_codes(codes, bits):
+    """Independent packer: codes [rows][n] -> bytes [rows][n * bits / 8], code i at bits
+    [bits * i, bits * i + bits) of the row read as a little-endian integer."""
+    rows, n = codes.shape
+    out = np.zeros((rows, n * bits // 8), np.uint8)
+    for r in range(rows):
+        v = 0
+        for i in range(n - 1, -1, -1):
+            v = (v << bits) | int(codes[r, i])
+        out[r] = np.frombuffer(v.to_bytes(n * bits // 8, "little"), np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lowbit_unpack_round_trip(bits):
+    rng = np.random.default_rng(60 + bits)
+    codes = rng.integers(0, 1 << bits, (5, 192))
+    ones = np.full((5, 3), 0x3F80, np.uint16)  # scale 1.0
+    zeros = np.zeros((5, 3), np.uint16)
+    w = oracle.bf16_to_f32(oracle.dequant(_pack_codes(codes, bits), ones, zeros, bits))
+    assert (w == codes).all()
+    if bits == 4:  # the bit-stream reading is the nibble order of the 4-bit format
+        assert (_pack_codes(codes, 4)[:, 0] == (codes[:, 0] | (codes[:, 1] << 4))).all()
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_lowbit_affine_identities(bits):
+    """bias = -2^(bits-1) * scale, as the generator draws it: w32 = s * (q - 2^(bits-1)) exactly,
+    and the bf16 result is the round-to-nearest-even of that exact product."""
+    rng = np.random.default_rng(70 + bits)
+    rows = 64
+    codes = rng.integers(0, 1 << bits, (rows, 64))
+    s = _bf16(np.abs(rng.standard_normal(rows)) * 0.05).reshape(rows, 1)
+    b = _bf16(-(2.0 ** (bits - 1)) * oracle.bf16_to_f32(s).astype(np.float64)).reshape(rows, 1)
+    assert (oracle.bf16_to_f32(b) == -(2.0 ** (bits - 1)) * oracle.bf16_to_f32(s)).all()  # exact
+    w = oracle.bf16_to_f32(oracle.dequant(_pack_codes(codes, bits), s, b, bits)).astype(np.float64)
+    exact = oracle.bf16_to_f32(s).astype(np.float64) * (codes - 2 ** (bits - 1))
+    assert (w == oracle.bf16_to_f32(_bf16(exact))).all()
 
 
 def test_sampled_tokens_equal_grouped_rows():

@@ -146,6 +146,7 @@ class Workload:
     chunk: int        # tokens per call (T is processed in T // chunk sequential calls)
     zipf: bool = False
     seed: int = 0
+    bits: int = 4     # bits per expert weight code (4, or the 3- and 2-bit variants)
 
     @property
     def calls(self) -> int:
@@ -154,7 +155,7 @@ class Workload:
     @property
     def expert_bytes(self) -> int:
         """Packed bytes of one routed expert (codes + bf16 scales + bf16 biases, 3 matrices)."""
-        return 3 * self.d * self.I // 2 + 3 * 2 * 2 * self.d * self.I // GROUP
+        return 3 * self.d * self.I * self.bits // 8 + 3 * 2 * 2 * self.d * self.I // GROUP
 
     @property
     def shared_bytes(self) -> int:
@@ -180,21 +181,37 @@ WORKLOADS: Dict[str, Workload] = {
     "m16": Workload("m16", 16, 2048, 256, 8, 512, 512, 0.02, 40, 16),
     "m32": Workload("m32", 32, 2048, 256, 8, 512, 512, 0.02, 40, 32),
     "m64": Workload("m64", 64, 2048, 256, 8, 512, 512, 0.02, 40, 64),
+    # the 3- and 2-bit expert variants at the decode shapes (same layers, fewer bits per weight)
+    "decode3": Workload("decode3", 1, 2048, 256, 8, 512, 512, 0.02, 40, 1, bits=3),
+    "decode2": Workload("decode2", 1, 2048, 256, 8, 512, 512, 0.02, 40, 1, bits=2),
+    "m32_3": Workload("m32_3", 32, 2048, 256, 8, 512, 512, 0.02, 40, 32, bits=3),
+    "m32_2": Workload("m32_2", 32, 2048, 256, 8, 512, 512, 0.02, 40, 32, bits=2),
+    "tiny3": Workload("tiny3", 8, 256, 16, 4, 128, 128, 0.05, 1, 8, bits=3),
+    "tiny2": Workload("tiny2", 8, 256, 16, 4, 128, 128, 0.05, 1, 8, bits=2),
 }
 
 
 def _proj(seed: int, layer: int, t_codes: int, t_sb: int, n_mat: int, out_dim: int, in_dim: int,
-          out: Optional[dict] = None) -> dict:
-    n_codes = n_mat * out_dim * in_dim // 2
+          out: Optional[dict] = None, bits: int = 4) -> dict:
+    """Codes are uniform random bits (so every b-bit code is uniform in [0, 2^b)); a row's codes
+    are a little-endian bit stream. scale = |N(0, 0.02^2)| * 2^(4 - b) and bias = -2^(b-1) * scale,
+    so the weights s * (q - 2^(b-1)) cover the same range at every b; the bias is then -8 times the
+    4-bit scale, the same bits as for 4-bit codes."""
+    n_codes = n_mat * out_dim * in_dim * bits // 8
     n_sb = n_mat * out_dim * in_dim // GROUP
     if out is None:
         out = {"codes": np.empty(n_codes, np.uint8), "scales": np.empty(n_sb, np.uint16),
                "biases": np.empty(n_sb, np.uint16)}
     rand_bytes(key(seed, layer, t_codes), n_codes, out=out["codes"].reshape(-1))
     scale_bias(key(seed, layer, t_sb), n_sb, out_s=out["scales"].reshape(-1), out_b=out["biases"].reshape(-1))
-    out["codes"] = out["codes"].reshape(n_mat, out_dim, in_dim // 2)
+    if bits != 4:  # times 2^(4 - b): an exact exponent step for these normal bf16 values
+        sc = out["scales"].reshape(-1)
+        sc += np.uint16((4 - bits) << 7)
+    out["codes"] = out["codes"].reshape(n_mat, out_dim, in_dim * bits // 8)
     out["scales"] = out["scales"].reshape(n_mat, out_dim, in_dim // GROUP)
     out["biases"] = out["biases"].reshape(n_mat, out_dim, in_dim // GROUP)
+    if bits != 4:  # (absent: 4-bit codes)
+        out["bits"] = bits
     return out
 
 
@@ -207,9 +224,9 @@ def expert_weights(w: Workload, layer: int, shared: bool = False, out: Optional[
         n, I, ids = w.E, w.I, (T_GATE_CODES, T_GATE_SB, T_UP_CODES, T_UP_SB, T_DOWN_CODES, T_DOWN_SB)
     out = out or {}
     return {
-        "gate": _proj(seed, layer, ids[0], ids[1], n, I, w.d, out.get("gate")),
-        "up": _proj(seed, layer, ids[2], ids[3], n, I, w.d, out.get("up")),
-        "down": _proj(seed, layer, ids[4], ids[5], n, w.d, I, out.get("down")),
+        "gate": _proj(seed, layer, ids[0], ids[1], n, I, w.d, out.get("gate"), w.bits),
+        "up": _proj(seed, layer, ids[2], ids[3], n, I, w.d, out.get("up"), w.bits),
+        "down": _proj(seed, layer, ids[4], ids[5], n, w.d, I, out.get("down"), w.bits),
     }
 
 
