@@ -50,14 +50,23 @@ DESCR = {
     "m16": "small-M: T=16, decode shapes, 40 layers cycled",
     "m32": "small-M: T=32, decode shapes, 40 layers cycled",
     "m64": "small-M: T=64, decode shapes, 40 layers cycled",
+    "decode3": "decode with 3-bit expert codes: T=1, d=2048, 256 experts top-8 + shared, I=I_s=512, g64, 40 layers",
+    "decode2": "decode with 2-bit expert codes: T=1, d=2048, 256 experts top-8 + shared, I=I_s=512, g64, 40 layers",
+    "m32_3": "small-M with 3-bit expert codes: T=32, decode shapes, 40 layers cycled",
+    "m32_2": "small-M with 2-bit expert codes: T=32, decode shapes, 40 layers cycled",
+    "tiny3": "tiny with 3-bit expert codes: T=8, d=256, 16 experts top-4 + shared (I=I_s=128), g64",
+    "tiny2": "tiny with 2-bit expert codes: T=8, d=256, 16 experts top-4 + shared (I=I_s=128), g64",
 }
 # layers held on the GPU and calls per step
 PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "diffusion": (30, 30),
-        "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40), "m32": (40, 40), "m64": (40, 40)}
+        "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40), "m32": (40, 40), "m64": (40, 40),
+        "decode3": (40, 40), "decode2": (40, 40), "m32_3": (40, 40), "m32_2": (40, 40), "tiny3": (1, 1), "tiny2": (1, 1)}
 DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gateup_gemm", "long": "gateup_gemm",
             "diffusion": "gateup_gemm", "m2": "gemv_gateup_topk", "m4": "gemv_gateup_topk",
             "m8": "gemv_gateup_topk", "m16": "gemv_gateup_topk", "m32": "gemv_gateup_topk",
-            "m64": "gateup_gemm"}
+            "m64": "gateup_gemm", "decode3": "gemv_gateup_topk", "decode2": "gemv_gateup_topk",
+            "m32_3": "gemv_gateup_topk", "m32_2": "gemv_gateup_topk", "tiny3": "gemv_gateup_topk",
+            "tiny2": "gemv_gateup_topk"}
 STAGE_SOURCE = {"router_decode": "gemv.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
                 "topk_prefill": "route.hip",
@@ -76,7 +85,8 @@ def bf16_dev(a, dev):
 
 def to_layer(L: dict, k: int, dev) -> moe.Layer:
     def proj(p):
-        return moe.QProj(torch.from_numpy(p["codes"]).to(dev), bf16_dev(p["scales"], dev), bf16_dev(p["biases"], dev))
+        return moe.QProj(torch.from_numpy(p["codes"]).to(dev), bf16_dev(p["scales"], dev), bf16_dev(p["biases"], dev),
+                         p.get("bits", 4))
 
     def ffn(f):
         return None if f is None else moe.QuantFFN(proj(f["gate"]), proj(f["up"]), proj(f["down"]))
@@ -101,7 +111,7 @@ def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
     d, E, k, I, Is, T = w.d, w.E, w.k, w.I, w.Is, w.chunk
     P = T * k
     act = int((counts > 0).sum())
-    per_w = lambda out, inn: out * inn // 2 + 2 * 2 * out * inn // 64  # noqa: E731  codes + scales + biases
+    per_w = lambda out, inn: out * inn * w.bits // 8 + 2 * 2 * out * inn // 64  # noqa: E731  codes + scales + biases
     if name == "router_decode":  # router weights, x, chunk partials out (one plane per token)
         return 4 * d * E + 2 * T * d + 4 * T * (d // 64) * E, 2 * T * d * E
     if name == "router_prefill":  # router weights, x, logits out

@@ -76,6 +76,46 @@ __device__ __forceinline__ void magic_pairs4(uint32_t w, uint32_t p[4]) {
   p[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u);
 }
 
+// The 32 weight codes of one 32-input segment as 16 bytes of nibbles, code i in nibble i (the
+// 4-bit layout): a row's codes are a little-endian bit stream of BITS bits per code, so the
+// segment occupies 4 * BITS bytes at p (16-, 12- or 8-byte loads). 2-bit codes are spread to
+// nibbles by three shift-or-mask steps per 8 codes; 3-bit codes are first cut into four 24-bit
+// windows (funnel shifts across the three words) and spread the same way.
+__device__ __forceinline__ uint32_t spread2(uint32_t u) {  // 8 codes in bits 0..15
+  u = (u | (u << 8)) & 0x00FF00FFu;
+  u = (u | (u << 4)) & 0x0F0F0F0Fu;
+  return (u | (u << 2)) & 0x33333333u;
+}
+__device__ __forceinline__ uint32_t spread3(uint32_t u) {  // 8 codes in bits 0..23
+  u = (u & 0xFFFu) | ((u & 0xFFF000u) << 4);
+  u = (u & 0x003F003Fu) | ((u & 0x0FC00FC0u) << 2);
+  return (u & 0x07070707u) | ((u & 0x38383838u) << 1);
+}
+// The load (load_code_words: the segment's raw words, unused ones zero) and the spread
+// (codes_to_nibbles) are separate so that the spread can wait until the codes are used.
+template <int BITS>
+__device__ __forceinline__ uint4 load_code_words(const uint8_t* p) {
+  if (BITS == 4) return *reinterpret_cast<const uint4*>(p);
+  if (BITS == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_uint4(w.x, w.y, 0u, 0u);
+  }
+  const uint3 w = *reinterpret_cast<const uint3*>(p);
+  return make_uint4(w.x, w.y, w.z, 0u);
+}
+template <int BITS>
+__device__ __forceinline__ uint4 codes_to_nibbles(const uint4& w) {
+  if (BITS == 4) return w;
+  if (BITS == 2)
+    return make_uint4(spread2(w.x & 0xFFFFu), spread2(w.x >> 16), spread2(w.y & 0xFFFFu), spread2(w.y >> 16));
+  return make_uint4(spread3(w.x & 0xFFFFFFu), spread3(__builtin_amdgcn_alignbit(w.y, w.x, 24) & 0xFFFFFFu),
+                    spread3(__builtin_amdgcn_alignbit(w.z, w.y, 16) & 0xFFFFFFu), spread3(w.z >> 8));
+}
+template <int BITS>
+__device__ __forceinline__ uint4 load_codes32(const uint8_t* p) {
+  return codes_to_nibbles<BITS>(load_code_words<BITS>(p));
+}
+
 // Re-pair 8 bf16 values (4 dwords in natural order) to match magic_pair: pair n = (v[n], v[n+4]).
 __device__ __forceinline__ void repair8(const uint32_t v[4], uint32_t p[4]) {
   p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);

@@ -100,12 +100,13 @@ static GemvPtrs gemv_ptrs(const Ctx& c) {
 // One wave computes h[i0 .. i0 + kGvRows) = bf16(silu(x . Wg[row]) * (x . Wu[row])) for the
 // weight rows row0 .. row0 + kGvRows of one expert's gate and up matrices; lane l takes the
 // 16-byte code pieces l, l+64, ... of each row.
+template <int BITS>
 __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* gc, const uint16_t* gs,
                                             const uint16_t* gb, const uint8_t* uc, const uint16_t* us,
                                             const uint16_t* ub, const uint16_t* __restrict__ x, uint16_t* hout) {
   const int lane = threadIdx.x & 63;
   const int nseg = d / 32;
-  const size_t cstride = (size_t)d / 2, sstride = (size_t)d / kGroup;
+  const size_t cstride = (size_t)d * BITS / 8, sstride = (size_t)d / kGroup;
   float acc[2 * kGvRows];
 #pragma unroll
   for (int r = 0; r < 2 * kGvRows; ++r) acc[r] = 0.0f;
@@ -116,7 +117,7 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
     for (int r = 0; r < 2 * kGvRows; ++r) {
       const size_t row = row0 + (r % kGvRows);
       const uint8_t* cp = r < kGvRows ? gc : uc;
-      cw[r] = *reinterpret_cast<const uint4*>(cp + row * cstride + (size_t)seg * 16);
+      cw[r] = load_code_words<BITS>(cp + row * cstride + (size_t)seg * 4 * BITS);
     }
 #pragma unroll
     for (int r = 0; r < 2 * kGvRows; ++r) {
@@ -139,7 +140,7 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
 #pragma unroll
     for (int r = 0; r < 2 * kGvRows; ++r) {
       const float s = bf16_to_f32(sr[r]), b = bf16_to_f32(br[r]);
-      const float pd = seg_dot(cw[r], a);
+      const float pd = seg_dot(codes_to_nibbles<BITS>(cw[r]), a);
       acc[r] = fmaf(s, pd, acc[r]);
       acc[r] = fmaf(fmaf(-128.0f, s, b), a.sum, acc[r]);
     }
@@ -229,7 +230,7 @@ hipError_t launch_router_decode(const Ctx& c) {
 // segments idle): the caller holds the lane's x segment (re-paired once per token) and passes
 // the loads of the next rows while these rows are computed.
 struct GuLoads {
-  uint4 cw[2 * kGvRows];      // gate rows, then up rows: 16 bytes of codes each
+  uint4 cw[2 * kGvRows];      // gate rows, then up rows: the segment's code words each
   uint32_t sb[2 * kGvRows];   // scale | bias << 16 of the segment's group
 };
 
@@ -240,12 +241,13 @@ struct GuRows {
   uint16_t* hout;
 };
 
+template <int BITS>
 __device__ __forceinline__ void gu_load(const GuRows& g, int d, int seg, GuLoads& L) {
-  const size_t cstride = (size_t)d / 2, sstride = (size_t)d / kGroup;
+  const size_t cstride = (size_t)d * BITS / 8, sstride = (size_t)d / kGroup;
 #pragma unroll
   for (int r = 0; r < 2 * kGvRows; ++r) {
     const size_t row = g.row0 + (r % kGvRows);
-    L.cw[r] = *reinterpret_cast<const uint4*>((r < kGvRows ? g.gc : g.uc) + row * cstride + (size_t)seg * 16);
+    L.cw[r] = load_code_words<BITS>((r < kGvRows ? g.gc : g.uc) + row * cstride + (size_t)seg * 4 * BITS);
   }
 #pragma unroll
   for (int r = 0; r < 2 * kGvRows; ++r) {
@@ -255,13 +257,14 @@ __device__ __forceinline__ void gu_load(const GuRows& g, int d, int seg, GuLoads
   }
 }
 
+template <int BITS>
 __device__ __forceinline__ void gu_finish(const GuLoads& L, const Seg32& a, bool active, uint16_t* hout) {
   const int lane = threadIdx.x & 63;
   float acc[2 * kGvRows];
 #pragma unroll
   for (int r = 0; r < 2 * kGvRows; ++r) {
     const float s = bf16lo(L.sb[r]), b = bf16hi(L.sb[r]);
-    const float pd = seg_dot(L.cw[r], a);
+    const float pd = seg_dot(codes_to_nibbles<BITS>(L.cw[r]), a);
     // the same operations, in the same order, as one segment of gateup_wave
     const float v = fmaf(fmaf(-128.0f, s, b), a.sum, fmaf(s, pd, 0.0f));
     acc[r] = active ? v : 0.0f;
@@ -291,7 +294,7 @@ __device__ __forceinline__ void gu_finish(const GuLoads& L, const Seg32& a, bool
 // block publishes them for the down kernel. The launch starts with n_sh blocks of the shared
 // expert's rows (n_sh / T per token), which need no routing and start loading at once, while
 // the routed blocks take the top-k.
-template <bool FUSED_TOPK>
+template <bool FUSED_TOPK, int BITS>
 __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int k, int I, int Is, int include_shared,
                                                                int groups_per_token, int reps, int sh_bpt, int n_tok,
                                                                const uint16_t* __restrict__ x,
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
     const int t = uniform(blockIdx.x / sh_bpt), sb = uniform(blockIdx.x - t * sh_bpt);
     const int r0 = uniform((sb * kGvWaves + wave) * kGvRows);
     if (r0 >= Is) return;
-    gateup_wave(d, (size_t)r0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x + (size_t)t * d, hs + (size_t)t * Is + r0);
+    gateup_wave<BITS>(d, (size_t)r0, p.sgc, p.sgs, p.sgb, p.suc, p.sus, p.sub, x + (size_t)t * d, hs + (size_t)t * Is + r0);
     return;
   }
   const int bid = (int)blockIdx.x - (FUSED_TOPK ? n_sh : 0);
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
     for (int rep = 0; rep < reps; ++rep) {
       GuRows g;
       if (!rows_of(rep, g)) break;
-      gateup_wave(d, g.row0, g.gc, g.gs, g.gb, g.uc, g.us, g.ub, x + (size_t)t * d, g.hout);
+      gateup_wave<BITS>(d, g.row0, g.gc, g.gs, g.gb, g.uc, g.us, g.ub, x + (size_t)t * d, g.hout);
     }
     return;
   }
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
   GuRows g;
   if (!rows_of(0, g)) return;
   GuLoads cur;
-  gu_load(g, d, seg, cur);
+  gu_load<BITS>(g, d, seg, cur);
   uint32_t xv[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -380,9 +383,9 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
     GuRows gn;
     const bool more = rows_of(rep + 1, gn);
     GuLoads nxt;
-    if (more) gu_load(gn, d, seg, nxt);
+    if (more) gu_load<BITS>(gn, d, seg, nxt);
     issue_fence();
-    gu_finish(cur, a, active, g.hout);
+    gu_finish<BITS>(cur, a, active, g.hout);
     if (!more) break;
     cur = nxt;
     g = gn;
@@ -401,14 +404,26 @@ hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
   const bool with_shared = fused_topk && c.Is > 0 && c.shared.gate.codes != nullptr;
   const int sh_bpt = with_shared ? (c.Is / kGvRows + kGvWaves - 1) / kGvWaves : 0;
   const dim3 grid(((groups + reps - 1) / reps) * c.T + (fused_topk ? sh_bpt * c.T : 0));
-  if (fused_topk)
-    hipLaunchKernelGGL(k_gemv_gateup<true>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, groups, reps, sh_bpt, c.T, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
-                       gemv_ptrs(c), c.h, c.hs);
-  else
-    hipLaunchKernelGGL(k_gemv_gateup<false>, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is,
-                       include_shared, groups, reps, 0, c.T, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w,
-                       gemv_ptrs(c), c.h, c.hs);
+  const auto go = [&](auto kernel, int shb) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kGvWaves * 64), 0, c.stream, c.d, c.E, c.k, c.I, c.Is, include_shared,
+                       groups, reps, shb, c.T, c.x, c.router_parts, c.logit_bias, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c),
+                       c.h, c.hs);
+  };
+  if (fused_topk) {
+    if (c.bits == 3)
+      go(k_gemv_gateup<true, 3>, sh_bpt);
+    else if (c.bits == 2)
+      go(k_gemv_gateup<true, 2>, sh_bpt);
+    else
+      go(k_gemv_gateup<true, 4>, sh_bpt);
+  } else {
+    if (c.bits == 3)
+      go(k_gemv_gateup<false, 3>, 0);
+    else if (c.bits == 2)
+      go(k_gemv_gateup<false, 2>, 0);
+    else
+      go(k_gemv_gateup<false, 4>, 0);
+  }
   return hipGetLastError();
 }
 
@@ -424,7 +439,7 @@ hipError_t launch_gemv_gateup(const Ctx& c, bool fused_topk) {
 // tokens one group per output does less redundant staging per output.
 constexpr int kGdWaves = 4;  // waves per block
 
-template <int PIECES, int HALVES>  // PIECES: 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
+template <int PIECES, int HALVES, int BITS>  // PIECES: 16-lane rounds of 32-input pieces per row: I, Is <= 512 * PIECES
 __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int E, int k, int I, int Is,
                                                                      const int32_t* __restrict__ ids,
                                                                      const float* __restrict__ wts, GemvPtrs p,
@@ -503,7 +518,7 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
       for (int q = 0; q < PIECES; ++q) {
         int seg = l16 + 16 * q;
         seg = seg < Ie / 32 ? seg : 0;
-        cw[b * PIECES + q] = *reinterpret_cast<const uint4*>(dc + row * (size_t)(Ie / 2) + (size_t)seg * 16);
+        cw[b * PIECES + q] = load_code_words<BITS>(dc + row * (size_t)(Ie * BITS / 8) + (size_t)seg * 4 * BITS);
         sb[b * PIECES + q] = (uint32_t)ds[row * (size_t)(Ie / kGroup) + seg / 2] |
                              ((uint32_t)db[row * (size_t)(Ie / kGroup) + seg / 2] << 16);
       }
@@ -562,7 +577,7 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
         a.sum = s_sum[gi];
         const uint32_t w2 = sb[b * PIECES + q];
         const float s = bf16lo(w2), bb = bf16hi(w2);
-        const float pd = seg_dot(cw[b * PIECES + q], a);
+        const float pd = seg_dot(codes_to_nibbles<BITS>(cw[b * PIECES + q]), a);
         const float c = fmaf(s, pd, fmaf(-128.0f, s, bb) * a.sum);
         acc = fmaf(use ? wj[b] : 0.0f, c, acc);
       }
@@ -591,27 +606,36 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
   }
 }
 
+template <int BITS>
+static void launch_down(const Ctx& c, size_t lds) {
+  const bool small = c.I <= 512 && c.Is <= 512;
+  const auto go = [&](auto kernel, int outs_per_block) {
+    const dim3 grid((c.d + outs_per_block - 1) / outs_per_block, c.T);
+    hipLaunchKernelGGL(kernel, grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I, c.Is, c.r.topk_ids,
+                       c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
+  };
+  if (c.T == 1) {  // two 16-lane halves per output, 2 outputs per wave
+    if (small)
+      go(k_gemv_down_combine<1, 2, BITS>, 2 * kGdWaves);
+    else
+      go(k_gemv_down_combine<2, 2, BITS>, 2 * kGdWaves);
+  } else {  // 16 lanes per output, 4 outputs per wave
+    if (small)
+      go(k_gemv_down_combine<1, 1, BITS>, 4 * kGdWaves);
+    else
+      go(k_gemv_down_combine<2, 1, BITS>, 4 * kGdWaves);
+  }
+}
+
 hipError_t launch_gemv_down_combine(const Ctx& c) {
   const int nseg = c.k * (c.I / 32) + c.Is / 32;
   const size_t lds = (size_t)nseg * 16 * 4 + (size_t)nseg * 4;
-  const bool small = c.I <= 512 && c.Is <= 512;
-  if (c.T == 1) {  // two 16-lane halves per output, 2 outputs per wave
-    const dim3 grid((c.d + 2 * kGdWaves - 1) / (2 * kGdWaves), c.T);
-    if (small)
-      hipLaunchKernelGGL((k_gemv_down_combine<1, 2>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
-                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
-    else
-      hipLaunchKernelGGL((k_gemv_down_combine<2, 2>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
-                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
-  } else {  // 16 lanes per output, 4 outputs per wave
-    const dim3 grid((c.d + 4 * kGdWaves - 1) / (4 * kGdWaves), c.T);
-    if (small)
-      hipLaunchKernelGGL((k_gemv_down_combine<1, 1>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
-                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
-    else
-      hipLaunchKernelGGL((k_gemv_down_combine<2, 1>), grid, dim3(kGdWaves * 64), lds, c.stream, c.d, c.E, c.k, c.I,
-                         c.Is, c.r.topk_ids, c.r.topk_w, gemv_ptrs(c), c.h, c.hs, c.y);
-  }
+  if (c.bits == 3)
+    launch_down<3>(c, lds);
+  else if (c.bits == 2)
+    launch_down<2>(c, lds);
+  else
+    launch_down<4>(c, lds);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ namespace moe {
 // Everything one layer call needs, resolved to device pointers by the C-ABI layer.
 struct Ctx {
   int d, E, k, I, Is, T, P, max_tiles;
+  int bits;  // bits per expert weight code: 4, 3 or 2 (3 and 2 on the GEMV path only)
   const uint16_t* x;
   const float* w_router;
   const float* logit_bias;
@@ -49,7 +50,7 @@ inline int vocab_chunk(int K) { return K <= 32 ? 1024 : K <= 64 ? 512 : 256; }
 // stage: -1 both kernels, 0 the chunk maxima only, 1 the selection only
 hipError_t launch_vocab_topk(int R, int V, int K, const float* logits, uint32_t* cmax, int32_t* ids, float* vals,
                              hipStream_t stream, int stage);
-hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, uint16_t* out, hipStream_t stream);
+hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, int bits, uint16_t* out, hipStream_t stream);
 
 // Block-map tile height (rows of one expert group per tile).
 constexpr int kTileRows = 32;

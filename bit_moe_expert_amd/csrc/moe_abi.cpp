@@ -44,8 +44,15 @@ int check_dims(const moe_dims* dm, int32_t T) {
     return fail(MOE_EUNSUPPORTED, "d_ff = %d must be a multiple of 64 in [64, 8192]", dm->d_ff);
   if (dm->d_ff_shared < 0 || dm->d_ff_shared > 8192 || dm->d_ff_shared % 64)
     return fail(MOE_EUNSUPPORTED, "d_ff_shared = %d must be 0 or a multiple of 64 up to 8192", dm->d_ff_shared);
+  if (dm->code_bits != 0 && dm->code_bits != 2 && dm->code_bits != 3 && dm->code_bits != 4)
+    return fail(MOE_EUNSUPPORTED, "code_bits = %d must be 4 (or 0), 3 or 2", dm->code_bits);
   return MOE_OK;
 }
+
+int bits_of(const moe_dims& dm) { return dm.code_bits == 0 ? 4 : dm.code_bits; }
+
+// 16-byte loads of 4-bit codes, 12-byte (dword) loads of 3-bit and 8-byte loads of 2-bit codes
+size_t code_align(int bits) { return bits == 4 ? 16 : bits == 3 ? 4 : 8; }
 
 int32_t max_tiles_of(const moe_dims& dm, int32_t T) {
   const int64_t P = (int64_t)T * dm.top_k;
@@ -104,21 +111,22 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   return L;
 }
 
-int check_q4(const moe_q4& q, const char* what) {
+int check_q4(const moe_q4& q, const char* what, int bits) {
   if (!q.codes || !q.scales || !q.biases) return fail(MOE_EINVAL, "%s: NULL codes/scales/biases", what);
-  if (!aligned(q.codes, 16)) return fail(MOE_EINVAL, "%s: codes not 16-byte aligned", what);
+  if (!aligned(q.codes, code_align(bits)))
+    return fail(MOE_EINVAL, "%s: codes not %zu-byte aligned", what, code_align(bits));
   if (!aligned(q.scales, 4) || !aligned(q.biases, 4)) return fail(MOE_EINVAL, "%s: scales/biases not 4-byte aligned", what);
   return MOE_OK;
 }
 
-int check_ffn(const moe_ffn_q4* f, const char* what) {
+int check_ffn(const moe_ffn_q4* f, const char* what, int bits) {
   if (!f) return fail(MOE_EINVAL, "%s weights are NULL", what);
   char buf[64];
   const char* names[3] = {"gate", "up", "down"};
   const moe_q4* qs[3] = {&f->gate, &f->up, &f->down};
   for (int i = 0; i < 3; ++i) {
     snprintf(buf, sizeof(buf), "%s.%s", what, names[i]);
-    if (int rc = check_q4(*qs[i], buf)) return rc;
+    if (int rc = check_q4(*qs[i], buf, bits)) return rc;
   }
   return MOE_OK;
 }
@@ -205,6 +213,7 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.k = dm.top_k;
   c.I = dm.d_ff;
   c.Is = dm.d_ff_shared;
+  c.bits = bits_of(dm);
   c.T = T;
   c.P = T * dm.top_k;
   c.max_tiles = max_tiles_of(dm, T);
@@ -237,9 +246,13 @@ int check_layer_args(const moe_dims* dims, int32_t T, const uint16_t* x, const f
   if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x NULL or not 16-byte aligned");
   if (need_router && (!w_router || !aligned(w_router, 16)))
     return fail(MOE_EINVAL, "w_router NULL or not 16-byte aligned");
-  if (int rc = check_ffn(routed, "routed")) return rc;
+  const int bits = bits_of(*dims);
+  if (bits != 4 && !gemv_path(*dims, T))
+    return fail(MOE_EUNSUPPORTED, "%d-bit codes run on the GEMV path only (1..%d tokens per call, top_k * d_ff + "
+                "d_ff_shared <= %d, d_ff and d_ff_shared <= %d); T = %d", bits, kGemvMaxT, kGemvMaxH, kGemvMaxFF, T);
+  if (int rc = check_ffn(routed, "routed", bits)) return rc;
   if (dims->d_ff_shared > 0) {
-    if (int rc = check_ffn(shared, "shared")) return rc;
+    if (int rc = check_ffn(shared, "shared", bits)) return rc;
   } else if (shared) {
     return fail(MOE_EINVAL, "shared weights given but d_ff_shared == 0");
   }
@@ -367,17 +380,23 @@ int moe_launch_stage(int32_t stage, const moe_dims* dims, int32_t T, const uint1
   return run_stage(st[stage], c);
 }
 
-int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream) {
+int moe_debug_dequant_bits(const moe_q4* w, int64_t rows, int32_t in_dim, int32_t bits, uint16_t* out_bf16,
+                           void* stream) {
+  if (bits != 2 && bits != 3 && bits != 4) return fail(MOE_EUNSUPPORTED, "bits = %d must be 4, 3 or 2", bits);
   if (!w) return fail(MOE_EINVAL, "weights are NULL");
-  if (int rc = check_q4(*w, "weights")) return rc;
+  if (int rc = check_q4(*w, "weights", bits)) return rc;
   if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MOE_EINVAL, "out NULL or not 16-byte aligned");
   if (rows < 0) return fail(MOE_EINVAL, "rows < 0");
   if (in_dim < 64 || in_dim % 64) return fail(MOE_EUNSUPPORTED, "in_dim = %d must be a positive multiple of 64", in_dim);
   if (rows == 0) return MOE_OK;
   if (rows * (in_dim / 64) > (int64_t)1 << 38) return fail(MOE_EUNSUPPORTED, "too many rows");
-  hipError_t e = launch_dequant(*w, rows, in_dim, out_bf16, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_dequant(*w, rows, in_dim, bits, out_bf16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EHIP, "launch of dequant failed: %s", hipGetErrorString(e));
   return MOE_OK;
+}
+
+int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream) {
+  return moe_debug_dequant_bits(w, rows, in_dim, 4, out_bf16, stream);
 }
 
 size_t moe_vocab_topk_workspace_bytes(int32_t R, int32_t V, int32_t K) {

@@ -29,7 +29,8 @@ class MoeError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+                ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("code_bits", ctypes.c_int32)]
 
 
 class Q4(ctypes.Structure):
@@ -64,6 +65,7 @@ def lib():
         L.moe_expert_ffn.argtypes = [P(Dims), i32, vp, P(Routing), P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
         L.moe_forward_layer.argtypes = [P(Dims), i32, vp, vp, vp, P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
         L.moe_debug_dequant.argtypes = [P(Q4), i64, i32, vp, vp]
+        L.moe_debug_dequant_bits.argtypes = [P(Q4), i64, i32, i32, vp, vp]
         L.moe_num_stages.argtypes = [P(Dims), i32]
         L.moe_num_stages.restype = i32
         L.moe_stage_name.argtypes = [P(Dims), i32, i32]
@@ -77,7 +79,8 @@ def lib():
         L.moe_vocab_topk_workspace_bytes.restype = sz
         L.moe_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_vocab_topk_stage.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
-        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_launch_stage",
+        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_debug_dequant_bits",
+                  "moe_launch_stage",
                   "moe_vocab_topk", "moe_vocab_topk_stage"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -89,8 +92,8 @@ def _check(status: int, where: str) -> None:
         raise MoeError(status, where)
 
 
-def make_dims(d: int, E: int, k: int, I: int, Is: int) -> Dims:
-    return Dims(d, E, k, I, Is, 64)
+def make_dims(d: int, E: int, k: int, I: int, Is: int, bits: int = 4) -> Dims:
+    return Dims(d, E, k, I, Is, 64, bits)
 
 
 def _stream(device: torch.device) -> int:
@@ -113,10 +116,11 @@ def _ptr(t: Optional[torch.Tensor], dtype, name: str, device=None) -> Optional[i
 
 @dataclasses.dataclass
 class QProj:
-    """One projection of n experts: codes [n][out][in/2] uint8, scales/biases [n][out][in/64] bf16."""
+    """One projection of n experts: codes [n][out][in * bits / 8] uint8, scales/biases [n][out][in/64] bf16."""
     codes: torch.Tensor
     scales: torch.Tensor
     biases: torch.Tensor
+    bits: int = 4
 
     def struct(self, device=None) -> Q4:
         return Q4(_ptr(self.codes, torch.uint8, "codes", device), _ptr(self.scales, torch.bfloat16, "scales", device),
@@ -144,9 +148,22 @@ class QuantFFN:
     def d_model(self) -> int:
         return self.down.codes.shape[1]
 
+    @property
+    def bits(self) -> int:
+        if not self.gate.bits == self.up.bits == self.down.bits:
+            raise ValueError("gate, up and down must use the same code width")
+        return self.gate.bits
+
+
+def _bits_of(routed: QuantFFN, shared: Optional[QuantFFN]) -> int:
+    if shared is not None and shared.bits != routed.bits:
+        raise ValueError("routed and shared experts must use the same code width")
+    return routed.bits
+
 
 def _dims_for(x: torch.Tensor, routed: QuantFFN, shared: Optional[QuantFFN], k: int) -> Dims:
-    return make_dims(x.shape[1], routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff)
+    return make_dims(x.shape[1], routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff,
+                     _bits_of(routed, shared))
 
 
 def max_tiles(dims: Dims, T: int) -> int:
@@ -224,7 +241,8 @@ class Layer:
                  logit_bias: Optional[torch.Tensor] = None):
         self.dev = w_router.device
         self.w_router, self.routed, self.shared, self.k, self.logit_bias = w_router, routed, shared, k, logit_bias
-        self.dims = make_dims(routed.d_model, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff)
+        self.dims = make_dims(routed.d_model, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff,
+                              _bits_of(routed, shared))
         if w_router.shape != (self.dims.d_model, self.dims.n_experts):
             raise ValueError(f"w_router shape {tuple(w_router.shape)} does not match the experts")
         self._wr = _ptr(w_router, torch.float32, "w_router", self.dev)
@@ -270,12 +288,13 @@ def forward_layer(x: torch.Tensor, w_router: torch.Tensor, routed: QuantFFN, sha
 def debug_dequant(p: QProj) -> torch.Tensor:
     """moe_debug_dequant: bf16 expansion of a projection, with the grouped GEMM's own routine."""
     codes = p.codes
-    in_dim = codes.shape[-1] * 2
+    in_dim = codes.shape[-1] * 8 // p.bits
     rows = codes.numel() // codes.shape[-1]
     dev = codes.device
     out = torch.empty(tuple(codes.shape[:-1]) + (in_dim,), dtype=torch.bfloat16, device=dev)
     q = p.struct(dev)
-    rc = lib().moe_debug_dequant(ctypes.byref(q), rows, in_dim, _ptr(out, torch.bfloat16, "out", dev), _stream(dev))
+    rc = lib().moe_debug_dequant_bits(ctypes.byref(q), rows, in_dim, p.bits, _ptr(out, torch.bfloat16, "out", dev),
+                                      _stream(dev))
     _check(rc, "moe_debug_dequant")
     return out
 

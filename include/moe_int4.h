@@ -44,9 +44,14 @@
  *   logit_bias [E]                    fp32, or NULL; added to the router logits before the
  *                                     top-k choice and before the softmax
  *   moe_q4     codes  [n][out][in/2]  uint8, two 4-bit codes per byte, the even input index
- *                                     in the low nibble
+ *                                     in the low nibble; with b = code_bits of 3 or 2,
+ *                     [n][out][in*b/8] each row's codes form a little-endian bit stream
+ *                                     (code c at bits [b*c, b*c + b), bit j of the stream is
+ *                                     bit j % 8 of byte j / 8; for b = 4 this is the nibble
+ *                                     order above)
  *              scales [n][out][in/64] bf16 bits; biases likewise
- *              weight = scale * code + bias (code in 0..15), groups run along the input
+ *              weight = scale * code + bias (code in 0..2^b-1), groups run along the input
+ *              codes 16-byte aligned (b = 4), 4-byte (b = 3) or 8-byte (b = 2)
  *   routed     gate, up: n = E, out = d_ff, in = d;  down: n = E, out = d, in = d_ff
  *   shared     the same with n = 1 and d_ff_shared (NULL when d_ff_shared == 0)
  *   y          [T][d]                 bf16 bits
@@ -80,6 +85,10 @@ typedef struct {
   int32_t d_ff;         /* I, routed expert intermediate size */
   int32_t d_ff_shared;  /* I_s, shared expert intermediate size; 0 = no shared expert */
   int32_t group_size;   /* quantisation group along the input dimension; must be 64 */
+  int32_t code_bits;    /* bits per expert weight code: 4 (0 also means 4), or the 3- and 2-bit variant
+                           ("Squeezing a 26B diffusion LLM onto a Mac", "The physics ceiling: why 300+
+                           tok/s is blocked", which names 2-3 bit experts as the lever that cuts the
+                           streamed bytes); 3 and 2 run on the GEMV path only (see moe_expert_ffn) */
 } moe_dims;
 
 /* One projection of every expert (n matrices [out][in]). */
@@ -162,8 +171,12 @@ int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const 
                       uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Check export: dequantise `rows` rows of length in_dim (rows counts all matrices) to bf16
- * bits out_bf16 [rows][in_dim]: w = bf16(fp32(scale * code + bias)), round to nearest even. */
+ * bits out_bf16 [rows][in_dim]: w = bf16(fp32(scale * code + bias)), round to nearest even.
+ * moe_debug_dequant_bits takes codes of `bits` = 4, 3 or 2 bits (layout above); it reads them
+ * with the GEMV kernels' own unpacking. */
 int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream);
+int moe_debug_dequant_bits(const moe_q4* w, int64_t rows, int32_t in_dim, int32_t bits, uint16_t* out_bf16,
+                           void* stream);
 
 /* Profiling: moe_forward_layer runs moe_num_stages() kernels in sequence for this T; stage s
  * is named moe_stage_name(). moe_launch_stage enqueues stage s alone (same arguments as

@@ -24,7 +24,7 @@ def f32_of_bits(b: np.ndarray) -> np.ndarray:
 
 def proj_dev(p: dict) -> moe.QProj:
     return moe.QProj(torch.from_numpy(np.ascontiguousarray(p["codes"])).to(DEV), bf16_dev(p["scales"]),
-                     bf16_dev(p["biases"]))
+                     bf16_dev(p["biases"]), p.get("bits", 4))
 
 
 def ffn_dev(f: Optional[dict]) -> Optional[moe.QuantFFN]:

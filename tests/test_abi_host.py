@@ -176,3 +176,28 @@ def test_vocab_topk_sizing_and_validation():
     assert call(2, 1000, 8, ids=f() + 2) == moe.MOE_EINVAL
     assert call(2, 1000, 8, ws=f() + 128) == moe.MOE_EINVAL
     assert call(2, 1000, 8, ws_bytes=16) == moe.MOE_EWORKSPACE
+
+
+def test_code_bits_validation():
+    f = _Fake()
+    L = moe.lib()
+
+    def dims(bits, **kw):
+        d = _dims(**kw)
+        d.code_bits = bits
+        return d
+
+    assert _layer_call(dims(5), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(dims(1), 4, f) == moe.MOE_EUNSUPPORTED
+    assert _layer_call(dims(3), 33, f) == moe.MOE_EUNSUPPORTED      # 3- and 2-bit codes: GEMV path only
+    assert "GEMV path only" in L.moe_last_error().decode()
+    assert _layer_call(dims(2, k=16, I=2048), 1, f) == moe.MOE_EUNSUPPORTED  # too much h for the GEMV path
+    bad = _ffn(f)
+    bad.gate.codes = f() + 4                                         # 4-byte aligned: enough for 3-bit codes only
+    assert _layer_call(dims(2), 4, f, routed=bad) == moe.MOE_EINVAL
+    assert _layer_call(dims(4), 4, f, routed=bad) == moe.MOE_EINVAL
+    assert _layer_call(dims(3), 4, f, routed=bad, y=None) == moe.MOE_EINVAL  # the codes passed; y did not
+    assert "y NULL" in L.moe_last_error().decode()
+    q = moe.Q4(f() + 4, f(), f())
+    assert L.moe_debug_dequant_bits(ctypes.byref(q), 4, 128, 5, f(), None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_debug_dequant_bits(ctypes.byref(q), 4, 128, 2, f(), None) == moe.MOE_EINVAL

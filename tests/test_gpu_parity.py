@@ -30,8 +30,8 @@ def _oracle_routing(x, wr, bias, k, has_shared):
     return m
 
 
-def _custom(T, d, E, k, I, Is, sigma=0.05, seed=0, zipf=False):
-    return gen.Workload("custom", T, d, E, k, I, Is, sigma, 1, T, zipf=zipf, seed=seed)
+def _custom(T, d, E, k, I, Is, sigma=0.05, seed=0, zipf=False, bits=4):
+    return gen.Workload("custom", T, d, E, k, I, Is, sigma, 1, T, zipf=zipf, seed=seed, bits=bits)
 
 
 # ------------------------------------------------------------------ dequantisation (bit-exact)
@@ -198,6 +198,53 @@ def test_route_then_expert_ffn_equals_forward_and_is_deterministic(name):
         lay.launch_stage(s, x, y4, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y4.view(torch.int16))
+
+
+# ------------------------------------------------------------------ 3- and 2-bit expert codes
+@pytest.mark.parametrize("bits", [2, 3])
+def test_lowbit_dequant_bit_exact(bits):
+    """The kernels' unpacking of b-bit codes (through moe_debug_dequant_bits) against the oracle:
+    random codes and scales, and a projection of the low-bit decode workload."""
+    rng = np.random.default_rng(80 + bits)
+    for n, out, inn in ((3, 40, 192), (2, 64, 2048)):
+        codes = rng.integers(0, 256, (n, out, inn * bits // 8), dtype=np.uint8)
+        sc = oracle.round_bf16((np.abs(rng.standard_normal((n, out, inn // 64))) * 0.05).astype(np.float32))
+        bi = oracle.round_bf16((rng.standard_normal((n, out, inn // 64)) * 0.1).astype(np.float32))
+        want = oracle.dequant(codes, sc, bi, bits)
+        got = bits_host(moe.debug_dequant(proj_dev({"codes": codes, "scales": sc, "biases": bi, "bits": bits})))
+        assert (got == want).all(), (bits, n, out, inn)
+    w = gen.WORKLOADS[f"decode{bits}"]
+    p = gen.expert_weights(w, 3)["down"]
+    p = {"codes": p["codes"][:4], "scales": p["scales"][:4], "biases": p["biases"][:4], "bits": bits}
+    want = oracle.dequant(p["codes"], p["scales"], p["biases"], bits)
+    assert (bits_host(moe.debug_dequant(proj_dev(p))) == want).all()
+
+
+@pytest.mark.parametrize("name,layer", [("tiny3", 0), ("tiny2", 0), ("decode3", 0), ("decode3", 17), ("decode2", 5),
+                                        ("m32_3", 1), ("m32_2", 3)])
+def test_forward_lowbit_workloads(name, layer):
+    _forward_check(gen.WORKLOADS[name], layer=layer)
+
+
+@pytest.mark.parametrize("T,d,E,k,I,Is,bits", [(1, 192, 8, 2, 192, 64, 3), (5, 256, 16, 4, 128, 128, 2),
+                                               (3, 64, 4, 2, 64, 0, 3), (17, 320, 8, 3, 64, 192, 2),
+                                               (32, 128, 4, 2, 256, 64, 3), (1, 2112, 4, 2, 128, 64, 2)])
+def test_forward_lowbit_shapes(T, d, E, k, I, Is, bits):
+    """Ragged K (d = 64 mod 128), no shared expert, d above 2048 (several segments per lane)."""
+    _forward_check(_custom(T, d, E, k, I, Is, seed=T + d + bits, bits=bits))
+
+
+@pytest.mark.parametrize("name", ["decode3", "m32_2"])
+def test_lowbit_route_then_expert_ffn_equals_forward(name):
+    w = gen.WORKLOADS[name]
+    L = gen.layer(w, 2)
+    x = bf16_dev(gen.tokens(w, 2, 0))
+    lay = layer_dev(L, w.k)
+    y1 = lay.forward(x)
+    r = moe.route(x, lay.w_router, w.k, w.I, w.Is, lay.logit_bias)
+    y2 = moe.expert_ffn(x, r, lay.routed, lay.shared)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
 def test_zero_tokens_is_a_noop():
