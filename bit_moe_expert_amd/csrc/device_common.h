@@ -30,33 +30,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float a) { return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu); }
 
-// Groupwise-affine dequantisation of one 32-bit word of codes (8 inputs, byte j holds input
-// 2j in its low nibble and 2j+1 in its high nibble): w = bf16(fp32(s * q + b)). s * q is exact
-// in fp32, so fmaf gives the single fp32 rounding the definition asks for; the conversion to
-// bf16 rounds to nearest even. out[j] = packed bf16 pair (input 2j, input 2j+1).
-__device__ __forceinline__ void dequant_word(uint32_t w, float s, float b, uint32_t out[4]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float a = fmaf(s, (float)((lo >> (8 * j)) & 0xffu), b);
-    const float c = fmaf(s, (float)((hi >> (8 * j)) & 0xffu), b);
-    out[j] = pack_bf16x2(a, c);
-  }
-}
-
-// Dequantise one 64-input group (32 bytes of codes) into 32 packed bf16 pairs.
-__device__ __forceinline__ void dequant_group(const uint4& c0, const uint4& c1, float s, float b, uint32_t out[32]) {
-  dequant_word(c0.x, s, b, out + 0);
-  dequant_word(c0.y, s, b, out + 4);
-  dequant_word(c0.z, s, b, out + 8);
-  dequant_word(c0.w, s, b, out + 12);
-  dequant_word(c1.x, s, b, out + 16);
-  dequant_word(c1.y, s, b, out + 20);
-  dequant_word(c1.z, s, b, out + 24);
-  dequant_word(c1.w, s, b, out + 28);
-}
-
 // "128 + q" as bf16: 0x4300 is 128.0 and its 7 mantissa bits hold q exactly. From a word of
 // 8 codes, pair n (n = 0..3) holds inputs (n, n + 4) of the word.
 __device__ __forceinline__ uint32_t magic_pair(uint32_t w, int n) {
@@ -76,23 +49,10 @@ __device__ __forceinline__ void magic_pairs4(uint32_t w, uint32_t p[4]) {
   p[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u);
 }
 
-// The 32 weight codes of one 32-input segment as 16 bytes of nibbles, code i in nibble i (the
-// 4-bit layout): a row's codes are a little-endian bit stream of BITS bits per code, so the
-// segment occupies 4 * BITS bytes at p (16-, 12- or 8-byte loads). 2-bit codes are spread to
-// nibbles by three shift-or-mask steps per 8 codes; 3-bit codes are first cut into four 24-bit
-// windows (funnel shifts across the three words) and spread the same way.
-__device__ __forceinline__ uint32_t spread2(uint32_t u) {  // 8 codes in bits 0..15
-  u = (u | (u << 8)) & 0x00FF00FFu;
-  u = (u | (u << 4)) & 0x0F0F0F0Fu;
-  return (u | (u << 2)) & 0x33333333u;
-}
-__device__ __forceinline__ uint32_t spread3(uint32_t u) {  // 8 codes in bits 0..23
-  u = (u & 0xFFFu) | ((u & 0xFFF000u) << 4);
-  u = (u & 0x003F003Fu) | ((u & 0x0FC00FC0u) << 2);
-  return (u & 0x07070707u) | ((u & 0x38383838u) << 1);
-}
-// The load (load_code_words: the segment's raw words, unused ones zero) and the spread
-// (codes_to_nibbles) are separate so that the spread can wait until the codes are used.
+// The 32 weight codes of one 32-input segment: a row's codes are a little-endian bit stream of
+// BITS bits per code, so the segment occupies 4 * BITS bytes at p (16-, 12- or 8-byte loads);
+// load_code_words returns those words (unused ones zero). The load and the unpack (seg_pairs)
+// are separate so that the unpack can wait until the codes are used.
 template <int BITS>
 __device__ __forceinline__ uint4 load_code_words(const uint8_t* p) {
   if (BITS == 4) return *reinterpret_cast<const uint4*>(p);
@@ -103,17 +63,69 @@ __device__ __forceinline__ uint4 load_code_words(const uint8_t* p) {
   const uint3 w = *reinterpret_cast<const uint3*>(p);
   return make_uint4(w.x, w.y, w.z, 0u);
 }
+
+// A constant the compiler must hold in a VGPR: gfx9 VOP3 encodings take no literal, so
+// (t & mask) | magic with plain constants becomes an AND and an OR; with both in registers it is
+// one v_and_or_b32. The value is loop-invariant and the asm has no side effects, so it is
+// materialised once.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
+}
+
+// Which inputs of the segment magic pair k of seg_pairs<BITS> holds: (pair_input(k),
+// pair_input(k) + pair_gap). 4-bit pairs take inputs (n, n + 4) of each 8-input word; 3- and
+// 2-bit pairs take inputs (i, i + 8) of each 16-input half.
 template <int BITS>
-__device__ __forceinline__ uint4 codes_to_nibbles(const uint4& w) {
-  if (BITS == 4) return w;
-  if (BITS == 2)
-    return make_uint4(spread2(w.x & 0xFFFFu), spread2(w.x >> 16), spread2(w.y & 0xFFFFu), spread2(w.y >> 16));
-  return make_uint4(spread3(w.x & 0xFFFFFFu), spread3(__builtin_amdgcn_alignbit(w.y, w.x, 24) & 0xFFFFFFu),
-                    spread3(__builtin_amdgcn_alignbit(w.z, w.y, 16) & 0xFFFFFFu), spread3(w.z >> 8));
+__host__ __device__ constexpr int pair_gap() {
+  return BITS == 4 ? 4 : 8;
 }
 template <int BITS>
-__device__ __forceinline__ uint4 load_codes32(const uint8_t* p) {
-  return codes_to_nibbles<BITS>(load_code_words<BITS>(p));
+__host__ __device__ constexpr int pair_input(int k) {
+  return BITS == 4 ? 8 * (k / 4) + k % 4 : 16 * (k / 8) + k % 8;
+}
+
+// The segment's 16 "128 + q" magic pairs straight from its code words, in pair_input order.
+//  4 bits: magic_pairs4 per word (7 operations per 8 codes).
+//  2 bits: a word holds the 16 codes of one half, code c at bits 2c; shifted right by 2r, codes
+//          r and r + 8 sit at bits 0 and 16, codes 4 + r and 12 + r at bits 8 and 24, so each
+//          pair is one v_and_or_b32 (15 operations per 16 codes).
+//  3 bits: a half's 16 codes span 6 bytes and codes i, i + 8 lie 24 bits apart, so a byte
+//          permute that puts stream bits [8a, 8a + 16) and [8a + 24, 8a + 40) in the low and
+//          high halves of a dword leaves both codes at the same offset in their halves; one
+//          shift and one v_and_or_b32 then give the pair (a = 0 serves i = 0..4, a = 1 serves
+//          i = 5..7; 17 operations per 16 codes).
+template <int BITS>
+__device__ __forceinline__ void seg_pairs(const uint4& w, uint32_t p[16]) {
+  if (BITS == 4) {
+    magic_pairs4(w.x, p);
+    magic_pairs4(w.y, p + 4);
+    magic_pairs4(w.z, p + 8);
+    magic_pairs4(w.w, p + 12);
+  } else if (BITS == 2) {
+    const uint32_t m = opaque_v(0x00030003u), g = opaque_v(0x43004300u);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t t = (h ? w.y : w.x) >> (2 * r);
+        p[8 * h + r] = (t & m) | g;
+        p[8 * h + 4 + r] = ((t >> 8) & m) | g;
+      }
+  } else {
+    const uint32_t m = opaque_v(0x00070007u), g = opaque_v(0x43004300u);
+    // half 0: stream bytes (0, 1, 3, 4) and (1, 2, 4, 5) of words x, y;
+    // half 1: stream bytes (6, 7, 9, 10) and (7, 8, 10, 11) of words y, z.
+    const uint32_t t[4] = {__builtin_amdgcn_perm(w.y, w.x, 0x04030100u), __builtin_amdgcn_perm(w.y, w.x, 0x05040201u),
+                           __builtin_amdgcn_perm(w.z, w.y, 0x06050302u), __builtin_amdgcn_perm(w.z, w.y, 0x07060403u)};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t u = i < 5 ? t[2 * h] >> (3 * i) : t[2 * h + 1] >> (3 * i - 8);
+        p[8 * h + i] = (u & m) | g;
+      }
+  }
 }
 
 // Re-pair 8 bf16 values (4 dwords in natural order) to match magic_pair: pair n = (v[n], v[n+4]).

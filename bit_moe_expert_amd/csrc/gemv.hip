@@ -26,32 +26,39 @@ namespace moe {
 constexpr int kGvWaves = 4;  // waves per block
 constexpr int kGvRows = 4;   // h entries (each = one gate row + one up row) per wave
 
-// Segment of 32 consecutive inputs as 16 re-paired bf16 dwords (magic_pair order) + their sum.
+// Segment of 32 consecutive inputs as 16 re-paired bf16 dwords (seg_pairs order) + their sum.
 struct Seg32 {
   uint32_t p[16];
   float sum;
 };
 
+template <int BITS>
 __device__ __forceinline__ void make_seg(const uint32_t* v16, Seg32& s) {
+  if (BITS == 4) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) repair8(v16 + 4 * m, s.p + 4 * m);
+    for (int m = 0; m < 4; ++m) repair8(v16 + 4 * m, s.p + 4 * m);
+  } else {
+    // pair 8h + i = inputs (16h + i, 16h + i + 8), as seg_pairs<3> and seg_pairs<2> lay out codes
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        s.p[8 * h + i] = __builtin_amdgcn_perm(v16[8 * h + 4 + i / 2], v16[8 * h + i / 2], i % 2 ? 0x07060302u : 0x05040100u);
+  }
   float acc = 0.0f;
 #pragma unroll
   for (int m = 0; m < 16; ++m) acc = dot2_bf16(v16[m], 0x3F803F80u, acc);  // (1.0, 1.0)
   s.sum = acc;
 }
 
-// sum over the segment of act * (128 + q) for one 16-byte row piece of codes.
+// sum over the segment of act * (128 + q), from the segment's raw code words.
+template <int BITS>
 __device__ __forceinline__ float seg_dot(const uint4& cw, const Seg32& a) {
-  const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+  uint32_t q[16];
+  seg_pairs<BITS>(cw, q);
   float acc = 0.0f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    uint32_t q[4];
-    magic_pairs4(w[m], q);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) acc = dot2_bf16(q[n], a.p[4 * m + n], acc);
-  }
+  for (int n = 0; n < 16; ++n) acc = dot2_bf16(q[n], a.p[n], acc);
   return acc;
 }
 
@@ -136,11 +143,11 @@ __device__ __forceinline__ void gateup_wave(int d, size_t row0, const uint8_t* g
     }
     issue_fence();
     Seg32 a;
-    make_seg(xv, a);
+    make_seg<BITS>(xv, a);
 #pragma unroll
     for (int r = 0; r < 2 * kGvRows; ++r) {
       const float s = bf16_to_f32(sr[r]), b = bf16_to_f32(br[r]);
-      const float pd = seg_dot(codes_to_nibbles<BITS>(cw[r]), a);
+      const float pd = seg_dot<BITS>(cw[r], a);
       acc[r] = fmaf(s, pd, acc[r]);
       acc[r] = fmaf(fmaf(-128.0f, s, b), a.sum, acc[r]);
     }
@@ -264,7 +271,7 @@ __device__ __forceinline__ void gu_finish(const GuLoads& L, const Seg32& a, bool
 #pragma unroll
   for (int r = 0; r < 2 * kGvRows; ++r) {
     const float s = bf16lo(L.sb[r]), b = bf16hi(L.sb[r]);
-    const float pd = seg_dot(codes_to_nibbles<BITS>(L.cw[r]), a);
+    const float pd = seg_dot<BITS>(L.cw[r], a);
     // the same operations, in the same order, as one segment of gateup_wave
     const float v = fmaf(fmaf(-128.0f, s, b), a.sum, fmaf(s, pd, 0.0f));
     acc[r] = active ? v : 0.0f;
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void k_gemv_gateup(int d, int E, int
   }
   issue_fence();
   Seg32 a;
-  make_seg(xv, a);
+  make_seg<BITS>(xv, a);
   for (int rep = 0;; ++rep) {
     GuRows gn;
     const bool more = rows_of(rep + 1, gn);
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
           }
         }
         Seg32 a;
-        make_seg(hv, a);
+        make_seg<BITS>(hv, a);
 #pragma unroll
         for (int q = 0; q < 16; ++q) s_h[(size_t)g * 16 + q] = a.p[q];
         s_sum[g] = a.sum;
@@ -577,7 +584,7 @@ __global__ __launch_bounds__(kGdWaves * 64) void k_gemv_down_combine(int d, int 
         a.sum = s_sum[gi];
         const uint32_t w2 = sb[b * PIECES + q];
         const float s = bf16lo(w2), bb = bf16hi(w2);
-        const float pd = seg_dot(codes_to_nibbles<BITS>(cw[b * PIECES + q]), a);
+        const float pd = seg_dot<BITS>(cw[b * PIECES + q], a);
         const float c = fmaf(s, pd, fmaf(-128.0f, s, bb) * a.sum);
         acc = fmaf(use ? wj[b] : 0.0f, c, acc);
       }
