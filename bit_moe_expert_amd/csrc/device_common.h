@@ -30,10 +30,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float a) { return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu); }
 
+// A constant the compiler must hold in a VGPR: gfx9 VOP3 encodings take no literal, so
+// (t & mask) | magic with plain constants becomes an AND and an OR; with both in registers it is
+// one v_and_or_b32. The value is loop-invariant and the asm has no side effects, so it is
+// materialised once.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
+}
+
 // "128 + q" as bf16: 0x4300 is 128.0 and its 7 mantissa bits hold q exactly. From a word of
-// 8 codes, pair n (n = 0..3) holds inputs (n, n + 4) of the word.
+// 8 codes, pair n (n = 0..3) holds inputs (n, n + 4) of the word: a shift and one v_and_or_b32.
 __device__ __forceinline__ uint32_t magic_pair(uint32_t w, int n) {
-  return ((w >> (4 * n)) & 0x000F000Fu) | 0x43004300u;
+  return ((w >> (4 * n)) & opaque_v(0x000F000Fu)) | opaque_v(0x43004300u);
 }
 
 // All four magic_pair(w, n), n = 0..3, in 7 operations: the low and high nibbles of every byte
@@ -62,15 +71,6 @@ __device__ __forceinline__ uint4 load_code_words(const uint8_t* p) {
   }
   const uint3 w = *reinterpret_cast<const uint3*>(p);
   return make_uint4(w.x, w.y, w.z, 0u);
-}
-
-// A constant the compiler must hold in a VGPR: gfx9 VOP3 encodings take no literal, so
-// (t & mask) | magic with plain constants becomes an AND and an OR; with both in registers it is
-// one v_and_or_b32. The value is loop-invariant and the asm has no side effects, so it is
-// materialised once.
-__device__ __forceinline__ uint32_t opaque_v(uint32_t c) {
-  asm("" : "+v"(c));
-  return c;
 }
 
 // Which inputs of the segment magic pair k of seg_pairs<BITS> holds: (pair_input(k),

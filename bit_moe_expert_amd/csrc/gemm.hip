@@ -11,9 +11,8 @@
 //   - a block is 4 waves and covers 128 weight rows (gate/up: 64 gate + 64 up rows, giving 64 h
 //     columns; down: 128 output columns); K advances 128 inputs (two quantisation groups) a step;
 //   - the grid is an upper bound (moe_max_tiles x column blocks); blocks past the device-side
-//     tile count exit at once. Blocks are renumbered so that each XCD (blocks are dealt to the
-//     8 XCDs round-robin) gets a contiguous range ordered (column block, tile): tiles of one
-//     expert that read the same weight rows then run on the same XCD and share its L2.
+//     tile count exit at once. Blocks are renumbered so that all column blocks of a tile run on
+//     one XCD and read its A rows through that XCD's L2 (block_tile).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -22,6 +21,7 @@ namespace moe {
 constexpr int kBK = 128;             // inputs per K step
 constexpr int kGuCols = 64;          // h columns per gate/up block (64 gate + 64 up weight rows)
 constexpr int kDnCols = 128;         // output columns per down block
+constexpr int kTileGroup = 2;        // tiles per XCD work unit
 
 struct GemmArgs {
   int d, E, k, I, Is, T, P, max_tiles, nb;  // nb: runs of column blocks
@@ -41,13 +41,17 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
 }
 
 // Decode the block's (run of column blocks, tile) and validate the tile. Returns false when the
-// block has nothing to do.
+// block has nothing to do. Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD
+// b % 8); each XCD takes whole units of kTileGroup consecutive tiles with all their runs, so a
+// tile's A rows are fetched into one L2 and served from there to every column block, and tiles of
+// one expert within a unit share the weight rows. Units are dealt to the XCDs round-robin as well,
+// which spreads the live tiles evenly whatever the grid's upper bound.
 __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, int& row0, int& rows) {
-  const int per_xcd = gridDim.x / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  run = L / a.max_tiles;
-  const int ti = L % a.max_tiles;
-  if (run >= a.nb) return false;
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int unit_blocks = kTileGroup * a.nb;
+  const int r = j % unit_blocks;
+  const int ti = ((j / unit_blocks) * 8 + xcd) * kTileGroup + r / a.nb;
+  run = r % a.nb;
   const int nt = min(*a.n_tiles, a.max_tiles);
   if (ti >= nt) return false;
   e = a.tiles[3 * ti];
@@ -149,7 +153,7 @@ __device__ __forceinline__ void step_barrier() {
 // PAIRED: K is a multiple of 128 (whole steps; scale/bias pairs load as one dword).
 template <int MT, bool GU, bool PAIRED>
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, const GemmLds& L) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool sh = (e == a.E);
   const int Ie = sh ? a.Is : a.I;
   const int mat = sh ? 0 : e;
@@ -451,7 +455,11 @@ static GemmArgs gemm_args(const Ctx& c, int nruns) {
   return a;
 }
 
-static int grid_blocks(int max_tiles, int nruns) { return ((max_tiles * nruns + 7) / 8) * 8; }
+// Every (tile < max_tiles, run) pair has one block (see block_tile).
+static int grid_blocks(int max_tiles, int nruns) {
+  const int units = (max_tiles + kTileGroup - 1) / kTileGroup;
+  return ((units + 7) / 8) * 8 * kTileGroup * nruns;
+}
 
 hipError_t launch_gateup_gemm(const Ctx& c) {
   const int ncb = (max(c.I, c.Is) + kGuCols - 1) / kGuCols;
