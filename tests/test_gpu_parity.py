@@ -162,6 +162,10 @@ SHAPES = [
     (33, 256, 8, 3, 64, 128), (257, 128, 16, 2, 128, 64), (130, 320, 2, 2, 64, 192), (5, 64, 1, 1, 64, 64),
     (40, 128, 4, 4, 256, 0), (1, 128, 1, 1, 64, 0), (13, 256, 16, 4, 128, 128), (16, 192, 8, 3, 64, 64),
     (31, 192, 8, 3, 64, 0), (32, 256, 16, 4, 128, 128),
+    # larger reductions (the prefill router stages d in passes of 2048 inputs), the largest top-k,
+    # 1024 experts (the long top-k path), expert counts that are not a multiple of 64
+    (40, 4096, 64, 8, 256, 128), (1, 4096, 64, 8, 256, 128), (3, 256, 1024, 16, 64, 64),
+    (70, 256, 1024, 16, 64, 0), (64, 128, 300, 5, 192, 64), (2, 128, 300, 5, 192, 64),
 ]
 
 
