@@ -232,9 +232,11 @@ def test_forward_lowbit_workloads(name, layer):
 
 @pytest.mark.parametrize("T,d,E,k,I,Is,bits", [(1, 192, 8, 2, 192, 64, 3), (5, 256, 16, 4, 128, 128, 2),
                                                (3, 64, 4, 2, 64, 0, 3), (17, 320, 8, 3, 64, 192, 2),
-                                               (32, 128, 4, 2, 256, 64, 3), (1, 2112, 4, 2, 128, 64, 2)])
+                                               (32, 128, 4, 2, 256, 64, 3), (1, 2112, 4, 2, 128, 64, 2),
+                                               (2, 4096, 1024, 16, 64, 64, 3), (9, 256, 300, 16, 64, 0, 2)])
 def test_forward_lowbit_shapes(T, d, E, k, I, Is, bits):
-    """Ragged K (d = 64 mod 128), no shared expert, d above 2048 (several segments per lane)."""
+    """Ragged K (d = 64 mod 128), no shared expert, d above 2048 (several segments per lane), the
+    largest top-k over 1024 experts, an expert count that is not a multiple of 64."""
     _forward_check(_custom(T, d, E, k, I, Is, seed=T + d + bits, bits=bits))
 
 
