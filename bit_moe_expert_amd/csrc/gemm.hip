@@ -487,31 +487,44 @@ hipError_t launch_down_gemm(const Ctx& c) {
 
 // ---------------------------------------------------------------------------------------------
 // Weighted gather back to token order: y[t] = bf16(sum_j w[t][j] * y_rows[inv_pos[t][j]] +
-// y_rows[P + t]), j ascending, in fp32. One thread per 4 outputs.
-__global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int P, int has_shared,
-                                                 const int32_t* __restrict__ inv_pos, const float* __restrict__ w,
-                                                 const float* __restrict__ y_rows, uint16_t* __restrict__ y) {
-  const int q = d / 4;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)T * q) return;
-  const int t = (int)(idx / q), o = (int)(idx % q) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int row = inv_pos[(size_t)t * k + j];
-    if ((unsigned)row >= (unsigned)P) continue;
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y_rows + (size_t)row * d + o);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+// y_rows[P + t]), j ascending, in fp32. A block covers 1024 outputs of one token (one thread per
+// 4 outputs), so the token's k row indices and weights are block-uniform scalar loads.
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void k_combine(int T, int d, int k, int P, int has_shared,
+                                                             const int32_t* __restrict__ inv_pos,
+                                                             const float* __restrict__ w,
+                                                             const float* __restrict__ y_rows, uint16_t* __restrict__ y) {
+  const int nb = (d + 4 * kCombineThreads - 1) / (4 * kCombineThreads);  // blocks per token
+  const int t = blockIdx.x / nb;
+  const int o = ((blockIdx.x % nb) * kCombineThreads + threadIdx.x) * 4;
+  if (t >= T || o >= d) return;
+  // every index and row load is issued before the first add
+  int row[kMaxTopK];
+  float wj[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    row[j] = j < k ? inv_pos[(size_t)t * k + j] : -1;
+    wj[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
+  float4 v[kMaxTopK], vs = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if ((unsigned)row[j] < (unsigned)P) v[j] = *reinterpret_cast<const float4*>(y_rows + (size_t)row[j] * d + o);
+  if (has_shared) vs = *reinterpret_cast<const float4*>(y_rows + (size_t)(P + t) * d + o);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if ((unsigned)row[j] < (unsigned)P) {
+      acc.x = fmaf(wj[j], v[j].x, acc.x);
+      acc.y = fmaf(wj[j], v[j].y, acc.y);
+      acc.z = fmaf(wj[j], v[j].z, acc.z);
+      acc.w = fmaf(wj[j], v[j].w, acc.w);
+    }
   if (has_shared) {
-    const float4 v = *reinterpret_cast<const float4*>(y_rows + (size_t)(P + t) * d + o);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    acc.x += vs.x;
+    acc.y += vs.y;
+    acc.z += vs.z;
+    acc.w += vs.w;
   }
   uint2 out;
   out.x = pack_bf16x2(acc.x, acc.y);
@@ -520,10 +533,9 @@ __global__ __launch_bounds__(256) void k_combine(int T, int d, int k, int P, int
 }
 
 hipError_t launch_combine(const Ctx& c) {
-  const size_t n = (size_t)c.T * (c.d / 4);
-  const int nblk = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(k_combine, dim3(nblk), dim3(256), 0, c.stream, c.T, c.d, c.k, c.P, c.Is > 0 ? 1 : 0,
-                     c.r.inv_pos, c.r.topk_w, c.y_rows, c.y);
+  const int nb = (c.d + 4 * kCombineThreads - 1) / (4 * kCombineThreads);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((size_t)c.T * nb)), dim3(kCombineThreads), 0, c.stream, c.T, c.d, c.k,
+                     c.P, c.Is > 0 ? 1 : 0, c.r.inv_pos, c.r.topk_w, c.y_rows, c.y);
   return hipGetLastError();
 }
 
