@@ -186,7 +186,9 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
   __shared__ int s_wsum[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
-  for (int i = tid; i < 16 * E; i += 1024) s_tab[i / E][i % E] = 0;
+  for (int e = tid; e < E; e += 1024)
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) s_tab[w2][e] = 0;
   __syncthreads();
   const int span = (((P + 15) / 16) + 63) & ~63;
   const int p_begin = min(P, wave * span), p_end = min(P, p_begin + span);
@@ -203,19 +205,23 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
       if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&s_tab[wave][ev[i]], 1);
   }
   __syncthreads();
+  // this expert's 16 per-wave counts, read once (all reads in flight together)
+  int wc[16];
+#pragma unroll
+  for (int w2 = 0; w2 < 16; ++w2) wc[w2] = tid < E ? s_tab[w2][tid] : 0;
   int cnt = 0;
-  if (tid < E)
-    for (int w2 = 0; w2 < 16; ++w2) cnt += s_tab[w2][tid];
+#pragma unroll
+  for (int w2 = 0; w2 < 16; ++w2) cnt += wc[w2];
   int total = 0;
   const int off = block_excl_scan(tid < E ? cnt : 0, s_wsum, &total);
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = off;
     int run = off;
+#pragma unroll
     for (int w2 = 0; w2 < 16; ++w2) {
-      const int c2 = s_tab[w2][tid];
       s_tab[w2][tid] = run;
-      run += c2;
+      run += wc[w2];
     }
   }
   if (tid == 0) offsets[E] = total;
