@@ -93,18 +93,14 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 // next stage has then landed.
 constexpr int kStages = 3;                 // LDS ring depth (2 steps in flight)
 constexpr int kCodeStageBytes = 128 * 64;  // 128 weight rows x 128 inputs of codes
+constexpr int kPairCodeStageBytes = 128 * 128;  // 128 weight rows x 256 inputs (tiles of <= 16 rows)
 constexpr int kAStageBytes = 32 * 256;     // 32 A rows x 128 bf16
 constexpr int kRunGu = 1;                  // column blocks per gate/up work item
 constexpr int kRunDn = 2;                  // column blocks per down work item
 
-// The stages are separate LDS arrays so that the compiler can tell them apart.
-struct GemmLds {
-  uint8_t* c[kStages];
-  uint32_t* sb[kStages];
-  uint8_t* a[kStages];
-};
 
 __device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int code_swz8(int r) { return r & 7; }
 __device__ __forceinline__ int a_swz(int r) { return r & 7; }
 
 // Direct loads are written as inline assembly: the compiler's own wait insertion cannot follow
@@ -152,7 +148,12 @@ __device__ __forceinline__ void step_barrier() {
 // otherwise down (A = h rows, 128 weight rows of the down matrix, fp32 y_rows epilogue).
 // PAIRED: K is a multiple of 128 (whole steps; scale/bias pairs load as one dword).
 template <int MT, bool GU, bool PAIRED>
-__device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, const GemmLds& L) {
+__device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
+  constexpr int kSbBytes = PAIRED ? 1024 : 2048;
+  // stage st of the codes, the scales and biases, and A in the block's LDS
+  const auto Lc = [lds](int st) { return lds + st * kCodeStageBytes; };
+  const auto Lsb = [lds](int st) { return reinterpret_cast<uint32_t*>(lds + 3 * kCodeStageBytes + st * kSbBytes); };
+  const auto La = [lds](int st) { return lds + 3 * kCodeStageBytes + 3 * kSbBytes + st * kAStageBytes; };
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool sh = (e == a.E);
   const int Ie = sh ? a.Is : a.I;
@@ -237,7 +238,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     const int n0 = (nb0 + j) * cols;
     const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
     const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
-    uint8_t* cdst = L.c[st] + wave * 2048;
+    uint8_t* cdst = Lc(st) + wave * 2048;
     const uint8_t* cb = wc + (mrow + n0) * (size_t)ldc + 64 * s;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -247,21 +248,21 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     }
     if (PAIRED) {
       const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
-      dma4(sbb, (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg), L.sb[st] + 128 * (wave >> 1) + 64 * (wave & 1));
+      dma4(sbb, (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg), Lsb(st) + 128 * (wave >> 1) + 64 * (wave & 1));
     } else {
       const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint32_t g = tail ? 0u : (uint32_t)(lane & 1);
         dma2(sbb, ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + g) * 2u,
-             L.sb[st] + 256 * (wave >> 1) + 128 * (wave & 1) + 64 * t);
+             Lsb(st) + 256 * (wave >> 1) + 128 * (wave & 1) + 64 * t);
       }
     }
     const uint16_t* ab = abase + 128 * s;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const uint32_t ch = tail ? (achk[t] & 127u) : achk[t];  // chunks past K re-read the first half
-      dma16(ab, aoff[t] + ch, L.a[st] + 1024 * (wave + 4 * t));
+      dma16(ab, aoff[t] + ch, La(st) + 1024 * (wave + 4 * t));
     }
   };
 
@@ -279,9 +280,9 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   auto compute = [&](int st, bool half) __attribute__((always_inline)) {
-    const uint8_t* cs = L.c[st];
-    const uint32_t* sb = L.sb[st];
-    const uint8_t* as = L.a[st];
+    const uint8_t* cs = Lc(st);
+    const uint32_t* sb = Lsb(st);
+    const uint8_t* as = La(st);
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
       const int q = 2 * gg + (kb >> 1);
@@ -402,13 +403,313 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Tiles of at most 16 rows: the same pipeline, except that codes move per pair of K steps:
+// 128 weight rows x 128 bytes (a whole 128-byte line of every row at once, which the memory
+// system serves better than two 64-byte halves a step apart) into a ring of two such stages,
+// issued at the first step of a pair for the next pair; each row's eight 16-byte chunks are
+// XOR-swizzled by row. A and the scales keep their three-stage ring. A job's steps are padded to
+// an even count: the padding step loads in-bounds stand-in data and multiplies nothing. The
+// 16-row A stages (4 KB) leave room for the larger code stages in the same LDS.
+template <int MT, bool GU, bool PAIRED>
+__device__ __forceinline__ void run_body_pair(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
+  constexpr int kSbBytes = PAIRED ? 1024 : 2048;
+  constexpr int kA16 = kAStageBytes / 2;  // A stages of 16 rows
+  // code pair stage st (0, 1), and stage st of the scales and biases and of A, in the block's LDS
+  const auto Lc = [lds](int st) { return lds + st * kPairCodeStageBytes; };
+  const auto La = [lds](int st) { return lds + 2 * kPairCodeStageBytes + st * kA16; };
+  const auto Lsb = [lds](int st) {
+    return reinterpret_cast<uint32_t*>(lds + 2 * kPairCodeStageBytes + 3 * kA16 + st * kSbBytes);
+  };
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool sh = (e == a.E);
+  const int Ie = sh ? a.Is : a.I;
+  const int mat = sh ? 0 : e;
+  const int d = a.d;
+  const int K = GU ? d : Ie;        // reduction length
+  const int ldc = K / 2;            // code bytes per weight row
+  const int ldg = K / kGroup;       // groups per weight row
+  const int nrows_w = GU ? Ie : d;  // weight rows of the matrix (per expert)
+  const int S = (K + kBK - 1) / kBK;
+  const int cols = GU ? kGuCols : kDnCols;
+  const int ncb = (nrows_w + cols - 1) / cols;  // column blocks of this matrix
+  const int R = GU ? kRunGu : kRunDn;
+  const int nb0 = run * R;
+  const int njobs = min(R, ncb - nb0);
+  if (njobs <= 0) return;
+  const int P = njobs * S;  // pipeline length in K steps
+
+  // ---- weight matrices (for GU, waves 0, 1 load gate rows and waves 2, 3 up rows)
+  const uint8_t* wc;
+  const uint16_t *ws, *wb;  // scale / bias arrays of this wave's direct loads
+  const uint16_t* sb_arr;
+  if (GU) {
+    const bool upw = wave >= 2;
+    wc = sh ? (upw ? a.shared.up.codes : a.shared.gate.codes) : (upw ? a.routed.up.codes : a.routed.gate.codes);
+    // scale/bias loads: wave w loads array (w >> 1) for block rows 64 (w & 1) .. +63, which are
+    // gate rows for w & 1 == 0 and up rows for w & 1 == 1
+    const bool ups = (wave & 1) != 0;
+    ws = sh ? (ups ? a.shared.up.scales : a.shared.gate.scales) : (ups ? a.routed.up.scales : a.routed.gate.scales);
+    wb = sh ? (ups ? a.shared.up.biases : a.shared.gate.biases) : (ups ? a.routed.up.biases : a.routed.gate.biases);
+  } else {
+    wc = sh ? a.shared.down.codes : a.routed.down.codes;
+    ws = sh ? a.shared.down.scales : a.routed.down.scales;
+    wb = sh ? a.shared.down.biases : a.routed.down.biases;
+  }
+  sb_arr = (wave >> 1) ? wb : ws;
+  const size_t mrow = (size_t)mat * nrows_w;  // first row of this expert's matrix
+
+  // ---- per-lane fixed offsets
+  // codes: block row r = 32 wave + 8 t + (lane >> 3), chunk slot lane & 7
+  int crow[4];
+  uint32_t cq16[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 32 * wave + 8 * t + (lane >> 3);
+    crow[t] = GU ? (r & (kGuCols - 1)) : r;  // row within the column block's weight rows
+    cq16[t] = 16 * ((lane & 7) ^ code_swz8(r));
+  }
+  // scale/bias: PAIRED: block row 64 (wave & 1) + lane; else (row, group) = (p >> 1, p & 1) for
+  // p = 64 (2 (wave & 1) + t) + lane
+  int srow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = PAIRED ? (64 * (wave & 1) + lane) : ((64 * (2 * (wave & 1) + t) + lane) >> 1);
+    srow[t] = GU ? (r & (kGuCols - 1)) : r;
+  }
+  // A: row 4 (wave + 4 t) + (lane >> 4), chunk slot lane & 15
+  const uint16_t* abase;
+  uint32_t aoff[MT], achk[MT];  // row offset, swizzled chunk offset within the step
+  if (GU) {
+    abase = a.x;
+  } else {
+    abase = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int r = 4 * (wave + 4 * t) + (lane >> 4);
+    const int rr = min(r, rows - 1);
+    int arow;
+    if (GU) {
+      arow = sh ? (row0 - a.P + rr) : a.sorted_token[row0 + rr];
+      arow = min(max(arow, 0), a.T - 1);
+    } else {
+      arow = rr;
+    }
+    aoff[t] = (uint32_t)arow * (uint32_t)(2 * K);
+    achk[t] = 16u * (uint32_t)((lane & 15) ^ a_swz(r));
+  }
+
+  // issue the code loads of step pair (job j, pair ss) into code stage st
+  auto issue_codes = [&](int j, int ss, int st) __attribute__((always_inline)) {
+    const int n0 = (nb0 + j) * cols;
+    const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
+    const uint32_t valid = (uint32_t)(ldc - 128 * ss);  // code bytes of the pair (32 .. 128)
+    uint8_t* cdst = Lc(st) + wave * 4096;
+    const uint8_t* cb = wc + (mrow + n0) * (size_t)ldc + 128 * ss;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t q = cq16[t];
+      if (q + 16u > valid) q &= 16u;  // chunks past K re-read the pair's first group
+      dma16(cb, (uint32_t)min(crow[t], lim) * (uint32_t)ldc + q, cdst + 1024 * t);
+    }
+  };
+  // issue the A and scale/bias loads of pipeline position (job j, step s) into stage st; the
+  // padding step (s == S) re-reads step S - 1
+  auto issue = [&](int j, int s, int st) __attribute__((always_inline)) {
+    s = min(s, S - 1);
+    const int n0 = (nb0 + j) * cols;
+    const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
+    const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
+    if (PAIRED) {
+      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
+      dma4(sbb, (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg), Lsb(st) + 128 * (wave >> 1) + 64 * (wave & 1));
+    } else {
+      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t g = tail ? 0u : (uint32_t)(lane & 1);
+        dma2(sbb, ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + g) * 2u,
+             Lsb(st) + 256 * (wave >> 1) + 128 * (wave & 1) + 64 * t);
+      }
+    }
+    const uint16_t* ab = abase + 128 * s;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint32_t ch = tail ? (achk[t] & 127u) : achk[t];  // chunks past K re-read the first half
+      dma16(ab, aoff[t] + ch, La(st) + 1024 * (wave + 4 * t));
+    }
+  };
+
+  const int n = lane & 15, kb = lane >> 4;
+  // this lane's two weight rows in the block (subtiles 0 and 1)
+  const int wrow0 = GU ? 16 * wave + n : 32 * wave + n;
+  const int wrow1 = GU ? kGuCols + 16 * wave + n : 32 * wave + 16 + n;
+  const int cread0 = wrow0 * 128 + 8 * (kb & 1), cread1 = wrow1 * 128 + 8 * (kb & 1);
+  const int cswz0 = code_swz8(wrow0), cswz1 = code_swz8(wrow1);
+  f32x4_t acc[2][MT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+
+  // step of A/scale stage st, codes from stage cst, second step of its pair when h
+  auto compute = [&](int st, int cst, int h, bool half) __attribute__((always_inline)) {
+    const uint8_t* cs = Lc(cst);
+    const uint32_t* sb = Lsb(st);
+    const uint8_t* as = La(st);
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int q = 4 * h + 2 * gg + (kb >> 1);
+      const uint2 w0 = *reinterpret_cast<const uint2*>(cs + cread0 + 16 * (q ^ cswz0));
+      const uint2 w1 = *reinterpret_cast<const uint2*>(cs + cread1 + 16 * (q ^ cswz1));
+      f32x4_t tmp[2][MT], xs[MT];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t c0 = kk ? w0.y : w0.x, c1 = kk ? w1.y : w1.x;
+        const uint4 b0 = make_uint4(magic_pair(c0, 0), magic_pair(c0, 1), magic_pair(c0, 2), magic_pair(c0, 3));
+        const uint4 b1 = make_uint4(magic_pair(c1, 0), magic_pair(c1, 1), magic_pair(c1, 2), magic_pair(c1, 3));
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) {
+          const int r = 16 * mm + n, c = 8 * gg + 2 * kb + kk;
+          const uint4 raw = *reinterpret_cast<const uint4*>(as + r * 256 + 16 * (c ^ a_swz(r)));
+          const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+          uint32_t pr[4];
+          repair8(v, pr);
+          const uint4 av = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+          const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          tmp[0][mm] = mfma16x16x32(av, b0, kk == 0 ? z : tmp[0][mm]);
+          tmp[1][mm] = mfma16x16x32(av, b1, kk == 0 ? z : tmp[1][mm]);
+          xs[mm] = mfma16x16x32(raw, ones, kk == 0 ? z : xs[mm]);
+        }
+      }
+      float s0, b0v, s1, b1v;
+      if (PAIRED) {
+        const uint32_t sc0 = sb[wrow0], bi0 = sb[128 + wrow0], sc1 = sb[wrow1], bi1 = sb[128 + wrow1];
+        s0 = gg ? bf16hi(sc0) : bf16lo(sc0);
+        b0v = gg ? bf16hi(bi0) : bf16lo(bi0);
+        s1 = gg ? bf16hi(sc1) : bf16lo(sc1);
+        b1v = gg ? bf16hi(bi1) : bf16lo(bi1);
+      } else {
+        s0 = bf16lo(sb[2 * wrow0 + gg]);
+        b0v = bf16lo(sb[256 + 2 * wrow0 + gg]);
+        s1 = bf16lo(sb[2 * wrow1 + gg]);
+        b1v = bf16lo(sb[256 + 2 * wrow1 + gg]);
+        if (gg == 1 && half) s0 = b0v = s1 = b1v = 0.0f;  // the group past K adds nothing
+      }
+      const float c0 = fmaf(-128.0f, s0, b0v), c1 = fmaf(-128.0f, s1, b1v);
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[0][mm][r] = fmaf(c0, xs[mm][r], fmaf(s0, tmp[0][mm][r], acc[0][mm][r]));
+          acc[1][mm][r] = fmaf(c1, xs[mm][r], fmaf(s1, tmp[1][mm][r], acc[1][mm][r]));
+        }
+    }
+  };
+
+  auto finish = [&](int j) __attribute__((always_inline)) {
+    const int n0 = (nb0 + j) * cols;
+    if (GU) {
+      uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
+      const int col = n0 + 16 * wave + n;
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mm + 4 * kb + r;
+          if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = n0 + 32 * wave + 16 * t + n;
+        if (col >= d) continue;
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mm + 4 * kb + r;
+            if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
+          }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // Positions run over (job, step) with each job's steps padded to an even count S2, so every
+  // code pair is two positions. Positions past the end issue clamped re-loads of the last
+  // position (same sequence every iteration); their data lands in a stage that is not read
+  // again. Issue order per position p: A/scales of p + 2, then, at the first step of a pair,
+  // the codes of the next pair. So at an even position the loads younger than the ones it needs
+  // are one position's A/scales, at an odd position those plus one pair's codes.
+  constexpr int kOpsA = (PAIRED ? 1 : 2) + MT;  // A and scale/bias loads one wave issues per position
+  constexpr int kOpsC = 4;                      // code loads one wave issues per pair
+  const int S2 = (S + 1) & ~1;
+  const int SP = S2 / 2;                        // code pairs per job
+  const int P2 = njobs * S2;
+  int ij = 0, is = 0;    // position being issued (job, step); stays at the last position
+  int icj = 0, ics = 0;  // code pair being issued (job, pair); stays at the last pair
+  int cj = 0, cs = 0;    // position being computed
+  int kc = 0;            // code pairs issued so far (its parity picks the stage)
+  issue_codes(0, 0, 0);
+  kc = 1;
+  issue(0, 0, 0);
+  ij = S2 > 1 ? 0 : 1;
+  is = S2 > 1 ? 1 : 0;
+  issue(ij, is, 1);
+  for (int p = 0; p < P2; p += 2 * kStages) {
+#pragma unroll
+    for (int q = 0; q < 2 * kStages; ++q) {
+      if (q == 0 || p + q < P2) {
+        if (q & 1)
+          step_barrier<kOpsA + kOpsC>();
+        else
+          step_barrier<kOpsA>();
+        if (ij < njobs - 1 || is < S2 - 1) {
+          if (++is == S2) {
+            is = 0;
+            ++ij;
+          }
+        }
+        issue(ij, is, (q + 2) % kStages);
+        if ((q & 1) == 0) {
+          if (icj < njobs - 1 || ics < SP - 1) {
+            if (++ics == SP) {
+              ics = 0;
+              ++icj;
+            }
+          }
+          issue_codes(icj, ics, kc & 1);
+          ++kc;
+        }
+        if (cs < S) compute(q % kStages, (cj * SP + (cs >> 1)) & 1, cs & 1, !PAIRED && cs == S - 1 && (ldg & 1));
+        if (cs == S2 - 1) {
+          finish(cj);
+          cs = 0;
+          ++cj;
+        } else {
+          ++cs;
+        }
+      }
+    }
+  }
+  // the clamped loads past the end must land before the block (and its LDS) is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <bool GU, bool PAIRED>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
-  __shared__ __attribute__((aligned(16))) uint8_t c0[kCodeStageBytes], c1[kCodeStageBytes], c2[kCodeStageBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t s0[PAIRED ? 256 : 512], s1[PAIRED ? 256 : 512],
-      s2[PAIRED ? 256 : 512];
-  __shared__ __attribute__((aligned(16))) uint8_t a0[kAStageBytes], a1[kAStageBytes], a2[kAStageBytes];
-  const GemmLds L = {{c0, c1, c2}, {s0, s1, s2}, {a0, a1, a2}};
+  constexpr int kSbBytes = PAIRED ? 1024 : 2048;
+  // One LDS buffer, carved per tile height: three stages of codes, scales and A for tiles of 17-32
+  // rows; two pair stages of codes, three 16-row A stages and three scale stages for the rest.
+  constexpr int kLds = 3 * kCodeStageBytes + 3 * kSbBytes + 3 * kAStageBytes;
+  constexpr int kA16 = kAStageBytes / 2;
+  static_assert(2 * kPairCodeStageBytes + 3 * kA16 + 3 * kSbBytes <= kLds, "the pair layout fits");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   int run, e, row0, rows;
   if (!block_tile(a, run, e, row0, rows)) return;
   // the tile is the same for the whole block: keep it (and all that derives from it) scalar
@@ -417,9 +718,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    run_body<1, GU, PAIRED>(a, run, e, row0, rows, L);
+    run_body_pair<1, GU, PAIRED>(a, run, e, row0, rows, lds);
   else
-    run_body<2, GU, PAIRED>(a, run, e, row0, rows, L);
+    run_body<2, GU, PAIRED>(a, run, e, row0, rows, lds);
 }
 
 template <bool PAIRED>
