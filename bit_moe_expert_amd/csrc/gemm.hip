@@ -75,31 +75,32 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 // 64 up weight rows; down: 128 output columns). The block streams the run's column blocks
 // through one continuous pipeline, so the load latency at the start is paid once per run.
 //
-// Pipeline: every input of a K step (128 inputs) goes straight from memory to LDS with direct
-// loads (no registers on the way), two steps ahead, into a ring of three stages:
-//   - codes: 128 weight rows x 64 bytes; each row's four 16-byte quarters are XOR-swizzled by
-//     row so the MFMA-side 8-byte reads spread over the banks;
-//   - scales and biases: with an even number of groups per row, one 4-byte load per weight row
-//     and array (the step's two groups); otherwise one 2-byte load per (row, group), each
-//     landing zero-extended in its own dword;
-//   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes; the 16-byte chunks of a row are
-//     XOR-swizzled by row. A rows past the tile's rows repeat its last row and only reach
-//     accumulator rows that are never written out.
+// Pipeline: every input goes straight from memory to LDS with direct loads (no registers on
+// the way). A K step is 128 inputs (two quantisation groups).
+//   - codes move per pair of K steps: 128 weight rows x 128 bytes, a whole 128-byte line of
+//     every row at once, which the memory system serves better than two 64-byte halves a step
+//     apart. They go into a ring of two pair stages, issued at the first step of a pair for the
+//     next pair; each row's eight 16-byte chunks are XOR-swizzled by row so the MFMA-side 8-byte
+//     reads spread over the banks. A job's steps are padded to an even count: the padding step
+//     loads in-bounds stand-in data and multiplies nothing;
+//   - scales and biases, per step: with an even number of groups per row, one 4-byte load per
+//     weight row and array (the step's two groups); otherwise one 2-byte load per (row, group),
+//     each landing zero-extended in its own dword;
+//   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes per step; the 16-byte chunks of
+//     a row are XOR-swizzled by row. A rows past the tile's rows repeat its last row and only
+//     reach accumulator rows that are never written out.
+// A and the scales run in a ring of AS stages, AS - 1 steps ahead.
 // Addresses are a scalar base that advances per step plus a per-lane offset fixed for the run.
 // When K is an odd number of groups, the last step's second group reads in-bounds stand-in data
 // and is given scale and bias 0 when it is multiplied. Weight rows past the down matrix repeat
 // its last row; their outputs are not written. Loads complete in issue order, so before each
-// barrier a wave waits until only the younger step's loads are outstanding: its part of the
-// next stage has then landed.
-constexpr int kStages = 3;                 // LDS ring depth (2 steps in flight)
-constexpr int kCodeStageBytes = 128 * 64;  // 128 weight rows x 128 inputs of codes
-constexpr int kPairCodeStageBytes = 128 * 128;  // 128 weight rows x 256 inputs (tiles of <= 16 rows)
-constexpr int kAStageBytes = 32 * 256;     // 32 A rows x 128 bf16
-constexpr int kRunGu = 1;                  // column blocks per gate/up work item
-constexpr int kRunDn = 2;                  // column blocks per down work item
+// barrier a wave waits until only the loads younger than the ones the step needs are
+// outstanding: its part of the stages the step reads has then landed.
+constexpr int kPairCodeStageBytes = 128 * 128;  // 128 weight rows x 256 inputs of codes
+constexpr int kA16StageBytes = 16 * 256;        // 16 A rows x 128 bf16
+constexpr int kRunGu = 1;                       // column blocks per gate/up work item
+constexpr int kRunDn = 2;                       // column blocks per down work item
 
-
-__device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int code_swz8(int r) { return r & 7; }
 __device__ __forceinline__ int a_swz(int r) { return r & 7; }
 
@@ -147,278 +148,18 @@ __device__ __forceinline__ void step_barrier() {
 // GU: gate/up (A = gathered x rows, 64 gate + 64 up weight rows, SwiGLU epilogue to h);
 // otherwise down (A = h rows, 128 weight rows of the down matrix, fp32 y_rows epilogue).
 // PAIRED: K is a multiple of 128 (whole steps; scale/bias pairs load as one dword).
-template <int MT, bool GU, bool PAIRED>
+// MT: 16-row subtiles of A (1 for tiles of at most 16 rows, else 2); AS: depth of the A and
+// scale/bias ring (3 for MT = 1, 2 for MT = 2, so that both layouts fit the same LDS).
+template <int MT, int AS, bool GU, bool PAIRED>
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
+  static_assert(AS == 2 || AS == 3, "A and scales run AS - 1 steps ahead");
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
-  // stage st of the codes, the scales and biases, and A in the block's LDS
-  const auto Lc = [lds](int st) { return lds + st * kCodeStageBytes; };
-  const auto Lsb = [lds](int st) { return reinterpret_cast<uint32_t*>(lds + 3 * kCodeStageBytes + st * kSbBytes); };
-  const auto La = [lds](int st) { return lds + 3 * kCodeStageBytes + 3 * kSbBytes + st * kAStageBytes; };
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const bool sh = (e == a.E);
-  const int Ie = sh ? a.Is : a.I;
-  const int mat = sh ? 0 : e;
-  const int d = a.d;
-  const int K = GU ? d : Ie;        // reduction length
-  const int ldc = K / 2;            // code bytes per weight row
-  const int ldg = K / kGroup;       // groups per weight row
-  const int nrows_w = GU ? Ie : d;  // weight rows of the matrix (per expert)
-  const int S = (K + kBK - 1) / kBK;
-  const int cols = GU ? kGuCols : kDnCols;
-  const int ncb = (nrows_w + cols - 1) / cols;  // column blocks of this matrix
-  const int R = GU ? kRunGu : kRunDn;
-  const int nb0 = run * R;
-  const int njobs = min(R, ncb - nb0);
-  if (njobs <= 0) return;
-  const int P = njobs * S;  // pipeline length in K steps
-
-  // ---- weight matrices (for GU, waves 0, 1 load gate rows and waves 2, 3 up rows)
-  const uint8_t* wc;
-  const uint16_t *ws, *wb;  // scale / bias arrays of this wave's direct loads
-  const uint16_t* sb_arr;
-  if (GU) {
-    const bool upw = wave >= 2;
-    wc = sh ? (upw ? a.shared.up.codes : a.shared.gate.codes) : (upw ? a.routed.up.codes : a.routed.gate.codes);
-    // scale/bias loads: wave w loads array (w >> 1) for block rows 64 (w & 1) .. +63, which are
-    // gate rows for w & 1 == 0 and up rows for w & 1 == 1
-    const bool ups = (wave & 1) != 0;
-    ws = sh ? (ups ? a.shared.up.scales : a.shared.gate.scales) : (ups ? a.routed.up.scales : a.routed.gate.scales);
-    wb = sh ? (ups ? a.shared.up.biases : a.shared.gate.biases) : (ups ? a.routed.up.biases : a.routed.gate.biases);
-  } else {
-    wc = sh ? a.shared.down.codes : a.routed.down.codes;
-    ws = sh ? a.shared.down.scales : a.routed.down.scales;
-    wb = sh ? a.shared.down.biases : a.routed.down.biases;
-  }
-  sb_arr = (wave >> 1) ? wb : ws;
-  const size_t mrow = (size_t)mat * nrows_w;  // first row of this expert's matrix
-
-  // ---- per-lane fixed offsets
-  // codes: block row r = 32 wave + 16 t + (lane >> 2), quarter slot lane & 3
-  int crow[2];
-  uint32_t cq16[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r = 32 * wave + 16 * t + (lane >> 2);
-    crow[t] = GU ? (r & (kGuCols - 1)) : r;  // row within the column block's weight rows
-    cq16[t] = 16 * ((lane & 3) ^ code_swz(r));
-  }
-  // scale/bias: PAIRED: block row 64 (wave & 1) + lane; else (row, group) = (p >> 1, p & 1) for
-  // p = 64 (2 (wave & 1) + t) + lane
-  int srow[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r = PAIRED ? (64 * (wave & 1) + lane) : ((64 * (2 * (wave & 1) + t) + lane) >> 1);
-    srow[t] = GU ? (r & (kGuCols - 1)) : r;
-  }
-  // A: row 4 (wave + 4 t) + (lane >> 4), chunk slot lane & 15
-  const uint16_t* abase;
-  uint32_t aoff[MT], achk[MT];  // row offset, swizzled chunk offset within the step
-  if (GU) {
-    abase = a.x;
-  } else {
-    abase = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
-  }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = 4 * (wave + 4 * t) + (lane >> 4);
-    const int rr = min(r, rows - 1);
-    int arow;
-    if (GU) {
-      arow = sh ? (row0 - a.P + rr) : a.sorted_token[row0 + rr];
-      arow = min(max(arow, 0), a.T - 1);
-    } else {
-      arow = rr;
-    }
-    aoff[t] = (uint32_t)arow * (uint32_t)(2 * K);
-    achk[t] = 16u * (uint32_t)((lane & 15) ^ a_swz(r));
-  }
-
-  // issue the direct loads of pipeline position (job j, step s) into stage st
-  auto issue = [&](int j, int s, int st) __attribute__((always_inline)) {
-    const int n0 = (nb0 + j) * cols;
-    const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
-    const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
-    uint8_t* cdst = Lc(st) + wave * 2048;
-    const uint8_t* cb = wc + (mrow + n0) * (size_t)ldc + 64 * s;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t q = cq16[t];
-      if (tail) q &= 16u;  // the missing half-step: re-read the step's first group
-      dma16(cb, (uint32_t)min(crow[t], lim) * (uint32_t)ldc + q, cdst + 1024 * t);
-    }
-    if (PAIRED) {
-      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
-      dma4(sbb, (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg), Lsb(st) + 128 * (wave >> 1) + 64 * (wave & 1));
-    } else {
-      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t g = tail ? 0u : (uint32_t)(lane & 1);
-        dma2(sbb, ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + g) * 2u,
-             Lsb(st) + 256 * (wave >> 1) + 128 * (wave & 1) + 64 * t);
-      }
-    }
-    const uint16_t* ab = abase + 128 * s;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint32_t ch = tail ? (achk[t] & 127u) : achk[t];  // chunks past K re-read the first half
-      dma16(ab, aoff[t] + ch, La(st) + 1024 * (wave + 4 * t));
-    }
-  };
-
-  const int n = lane & 15, kb = lane >> 4;
-  // this lane's two weight rows in the block (subtiles 0 and 1)
-  const int wrow0 = GU ? 16 * wave + n : 32 * wave + n;
-  const int wrow1 = GU ? kGuCols + 16 * wave + n : 32 * wave + 16 + n;
-  const int cread0 = wrow0 * 64 + 8 * (kb & 1), cread1 = wrow1 * 64 + 8 * (kb & 1);
-  const int cswz0 = code_swz(wrow0), cswz1 = code_swz(wrow1);
-  f32x4_t acc[2][MT];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-
-  auto compute = [&](int st, bool half) __attribute__((always_inline)) {
-    const uint8_t* cs = Lc(st);
-    const uint32_t* sb = Lsb(st);
-    const uint8_t* as = La(st);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int q = 2 * gg + (kb >> 1);
-      const uint2 w0 = *reinterpret_cast<const uint2*>(cs + cread0 + 16 * (q ^ cswz0));
-      const uint2 w1 = *reinterpret_cast<const uint2*>(cs + cread1 + 16 * (q ^ cswz1));
-      f32x4_t tmp[2][MT], xs[MT];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint32_t c0 = kk ? w0.y : w0.x, c1 = kk ? w1.y : w1.x;
-        const uint4 b0 = make_uint4(magic_pair(c0, 0), magic_pair(c0, 1), magic_pair(c0, 2), magic_pair(c0, 3));
-        const uint4 b1 = make_uint4(magic_pair(c1, 0), magic_pair(c1, 1), magic_pair(c1, 2), magic_pair(c1, 3));
-#pragma unroll
-        for (int mm = 0; mm < MT; ++mm) {
-          const int r = 16 * mm + n, c = 8 * gg + 2 * kb + kk;
-          const uint4 raw = *reinterpret_cast<const uint4*>(as + r * 256 + 16 * (c ^ a_swz(r)));
-          const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
-          uint32_t pr[4];
-          repair8(v, pr);
-          const uint4 av = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-          const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          tmp[0][mm] = mfma16x16x32(av, b0, kk == 0 ? z : tmp[0][mm]);
-          tmp[1][mm] = mfma16x16x32(av, b1, kk == 0 ? z : tmp[1][mm]);
-          xs[mm] = mfma16x16x32(raw, ones, kk == 0 ? z : xs[mm]);
-        }
-      }
-      float s0, b0v, s1, b1v;
-      if (PAIRED) {
-        const uint32_t sc0 = sb[wrow0], bi0 = sb[128 + wrow0], sc1 = sb[wrow1], bi1 = sb[128 + wrow1];
-        s0 = gg ? bf16hi(sc0) : bf16lo(sc0);
-        b0v = gg ? bf16hi(bi0) : bf16lo(bi0);
-        s1 = gg ? bf16hi(sc1) : bf16lo(sc1);
-        b1v = gg ? bf16hi(bi1) : bf16lo(bi1);
-      } else {
-        s0 = bf16lo(sb[2 * wrow0 + gg]);
-        b0v = bf16lo(sb[256 + 2 * wrow0 + gg]);
-        s1 = bf16lo(sb[2 * wrow1 + gg]);
-        b1v = bf16lo(sb[256 + 2 * wrow1 + gg]);
-        if (gg == 1 && half) s0 = b0v = s1 = b1v = 0.0f;  // the group past K adds nothing
-      }
-      const float c0 = fmaf(-128.0f, s0, b0v), c1 = fmaf(-128.0f, s1, b1v);
-#pragma unroll
-      for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[0][mm][r] = fmaf(c0, xs[mm][r], fmaf(s0, tmp[0][mm][r], acc[0][mm][r]));
-          acc[1][mm][r] = fmaf(c1, xs[mm][r], fmaf(s1, tmp[1][mm][r], acc[1][mm][r]));
-        }
-    }
-  };
-
-  auto finish = [&](int j) __attribute__((always_inline)) {
-    const int n0 = (nb0 + j) * cols;
-    if (GU) {
-      uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
-      const int col = n0 + 16 * wave + n;
-#pragma unroll
-      for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mm + 4 * kb + r;
-          if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
-        }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int col = n0 + 32 * wave + 16 * t + n;
-        if (col >= d) continue;
-#pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mm + 4 * kb + r;
-            if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
-          }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-
-  // Positions past the end issue clamped re-loads of the last position (same sequence every
-  // iteration); their data lands in a stage that is not read again.
-  constexpr int kOps = 2 + (PAIRED ? 1 : 2) + MT;  // loads one wave issues per position
-  int ij = 0, is = 0;  // position being issued (job, step); stays at the last position
-  int cj = 0, cs = 0;  // position being computed
-  issue(0, 0, 0);
-  if (P > 1) {
-    ij = S > 1 ? 0 : 1;
-    is = S > 1 ? 1 : 0;
-  }
-  issue(ij, is, 1);
-  for (int p = 0; p < P; p += kStages) {
-#pragma unroll
-    for (int q = 0; q < kStages; ++q) {
-      if (q == 0 || p + q < P) {
-        step_barrier<kOps>();
-        if (ij < njobs - 1 || is < S - 1) {
-          if (++is == S) {
-            is = 0;
-            ++ij;
-          }
-        }
-        issue(ij, is, (q + 2) % kStages);
-        compute(q, !PAIRED && cs == S - 1 && (ldg & 1));
-        if (cs == S - 1) {
-          finish(cj);
-          cs = 0;
-          ++cj;
-        } else {
-          ++cs;
-        }
-      }
-    }
-  }
-  // the clamped loads past the end must land before the block (and its LDS) is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// Tiles of at most 16 rows: the same pipeline, except that codes move per pair of K steps:
-// 128 weight rows x 128 bytes (a whole 128-byte line of every row at once, which the memory
-// system serves better than two 64-byte halves a step apart) into a ring of two such stages,
-// issued at the first step of a pair for the next pair; each row's eight 16-byte chunks are
-// XOR-swizzled by row. A and the scales keep their three-stage ring. A job's steps are padded to
-// an even count: the padding step loads in-bounds stand-in data and multiplies nothing. The
-// 16-row A stages (4 KB) leave room for the larger code stages in the same LDS.
-template <int MT, bool GU, bool PAIRED>
-__device__ __forceinline__ void run_body_pair(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
-  constexpr int kSbBytes = PAIRED ? 1024 : 2048;
-  constexpr int kA16 = kAStageBytes / 2;  // A stages of 16 rows
+  constexpr int kAS = MT * kA16StageBytes;  // an A stage: 16 MT rows
   // code pair stage st (0, 1), and stage st of the scales and biases and of A, in the block's LDS
   const auto Lc = [lds](int st) { return lds + st * kPairCodeStageBytes; };
-  const auto La = [lds](int st) { return lds + 2 * kPairCodeStageBytes + st * kA16; };
+  const auto La = [lds](int st) { return lds + 2 * kPairCodeStageBytes + st * kAS; };
   const auto Lsb = [lds](int st) {
-    return reinterpret_cast<uint32_t*>(lds + 2 * kPairCodeStageBytes + 3 * kA16 + st * kSbBytes);
+    return reinterpret_cast<uint32_t*>(lds + 2 * kPairCodeStageBytes + AS * kAS + st * kSbBytes);
   };
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool sh = (e == a.E);
@@ -643,9 +384,11 @@ __device__ __forceinline__ void run_body_pair(const GemmArgs& a, int run, int e,
   // Positions run over (job, step) with each job's steps padded to an even count S2, so every
   // code pair is two positions. Positions past the end issue clamped re-loads of the last
   // position (same sequence every iteration); their data lands in a stage that is not read
-  // again. Issue order per position p: A/scales of p + 2, then, at the first step of a pair,
-  // the codes of the next pair. So at an even position the loads younger than the ones it needs
-  // are one position's A/scales, at an odd position those plus one pair's codes.
+  // again. Issue order per position p: A/scales of p + AS - 1, then, at the first step of a
+  // pair, the codes of the next pair. With AS = 3 the loads younger than the ones a position
+  // needs are one position's A/scales at an even position, and those plus one pair's codes at an
+  // odd one; with AS = 2 they are nothing at an even position and one pair's codes at an odd one.
+  // A stage is overwritten only after the barrier that follows its last read.
   constexpr int kOpsA = (PAIRED ? 1 : 2) + MT;  // A and scale/bias loads one wave issues per position
   constexpr int kOpsC = 4;                      // code loads one wave issues per pair
   const int S2 = (S + 1) & ~1;
@@ -658,24 +401,27 @@ __device__ __forceinline__ void run_body_pair(const GemmArgs& a, int run, int e,
   issue_codes(0, 0, 0);
   kc = 1;
   issue(0, 0, 0);
-  ij = S2 > 1 ? 0 : 1;
-  is = S2 > 1 ? 1 : 0;
-  issue(ij, is, 1);
-  for (int p = 0; p < P2; p += 2 * kStages) {
+  if (AS == 3) {
+    ij = S2 > 1 ? 0 : 1;
+    is = S2 > 1 ? 1 : 0;
+    issue(ij, is, 1);
+  }
+  constexpr int kWaitEven = AS == 3 ? kOpsA : 0, kWaitOdd = kWaitEven + kOpsC;
+  for (int p = 0; p < P2; p += 2 * AS) {
 #pragma unroll
-    for (int q = 0; q < 2 * kStages; ++q) {
+    for (int q = 0; q < 2 * AS; ++q) {
       if (q == 0 || p + q < P2) {
         if (q & 1)
-          step_barrier<kOpsA + kOpsC>();
+          step_barrier<kWaitOdd>();
         else
-          step_barrier<kOpsA>();
+          step_barrier<kWaitEven>();
         if (ij < njobs - 1 || is < S2 - 1) {
           if (++is == S2) {
             is = 0;
             ++ij;
           }
         }
-        issue(ij, is, (q + 2) % kStages);
+        issue(ij, is, (q + AS - 1) % AS);
         if ((q & 1) == 0) {
           if (icj < njobs - 1 || ics < SP - 1) {
             if (++ics == SP) {
@@ -686,7 +432,7 @@ __device__ __forceinline__ void run_body_pair(const GemmArgs& a, int run, int e,
           issue_codes(icj, ics, kc & 1);
           ++kc;
         }
-        if (cs < S) compute(q % kStages, (cj * SP + (cs >> 1)) & 1, cs & 1, !PAIRED && cs == S - 1 && (ldg & 1));
+        if (cs < S) compute(q % AS, (cj * SP + (cs >> 1)) & 1, cs & 1, !PAIRED && cs == S - 1 && (ldg & 1));
         if (cs == S2 - 1) {
           finish(cj);
           cs = 0;
@@ -704,11 +450,11 @@ __device__ __forceinline__ void run_body_pair(const GemmArgs& a, int run, int e,
 template <bool GU, bool PAIRED>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
-  // One LDS buffer, carved per tile height: three stages of codes, scales and A for tiles of 17-32
-  // rows; two pair stages of codes, three 16-row A stages and three scale stages for the rest.
-  constexpr int kLds = 3 * kCodeStageBytes + 3 * kSbBytes + 3 * kAStageBytes;
-  constexpr int kA16 = kAStageBytes / 2;
-  static_assert(2 * kPairCodeStageBytes + 3 * kA16 + 3 * kSbBytes <= kLds, "the pair layout fits");
+  // One LDS buffer, carved per tile height: two code pair stages, then three 16-row A stages and
+  // three scale stages (tiles of at most 16 rows) or two 32-row A stages and two scale stages.
+  constexpr int kLds1 = 2 * kPairCodeStageBytes + 3 * kA16StageBytes + 3 * kSbBytes;
+  constexpr int kLds2 = 2 * kPairCodeStageBytes + 2 * 2 * kA16StageBytes + 2 * kSbBytes;
+  constexpr int kLds = kLds1 > kLds2 ? kLds1 : kLds2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   int run, e, row0, rows;
   if (!block_tile(a, run, e, row0, rows)) return;
@@ -718,9 +464,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    run_body_pair<1, GU, PAIRED>(a, run, e, row0, rows, lds);
+    run_body<1, 3, GU, PAIRED>(a, run, e, row0, rows, lds);
   else
-    run_body<2, GU, PAIRED>(a, run, e, row0, rows, lds);
+    run_body<2, 2, GU, PAIRED>(a, run, e, row0, rows, lds);
 }
 
 template <bool PAIRED>
