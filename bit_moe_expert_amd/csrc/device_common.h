@@ -129,11 +129,19 @@ __device__ __forceinline__ void seg_pairs(const uint4& w, uint32_t p[16]) {
 }
 
 // Re-pair 8 bf16 values (4 dwords in natural order) to match magic_pair: pair n = (v[n], v[n+4]).
+// The result holds the inputs of the chunk in "pair order": 0, 4, 1, 5, 2, 6, 3, 7.
 __device__ __forceinline__ void repair8(const uint32_t v[4], uint32_t p[4]) {
   p[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
   p[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
   p[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
   p[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+}
+
+// Position of input i in pair order: within its chunk of 8, input j goes to 2j (j < 4) or
+// 2(j - 4) + 1 (j >= 4).
+__device__ __forceinline__ int pair_pos(int i) {
+  const int j = i & 7;
+  return (i & ~7) | (j < 4 ? 2 * j : 2 * j - 7);
 }
 
 // fp32 += a.lo * b.lo + a.hi * b.hi over bf16 pairs.

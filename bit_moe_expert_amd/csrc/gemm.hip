@@ -25,7 +25,7 @@ constexpr int kTileGroup = 2;        // tiles per XCD work unit
 
 struct GemmArgs {
   int d, E, k, I, Is, T, P, max_tiles, nb;  // nb: runs of column blocks
-  const uint16_t* x;
+  const uint16_t* xp;  // x, each 8-input chunk in pair order
   const int32_t* sorted_token;
   const int32_t* tiles;
   const int32_t* n_tiles;
@@ -88,7 +88,10 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 //     each landing zero-extended in its own dword;
 //   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes per step; the 16-byte chunks of
 //     a row are XOR-swizzled by row. A rows past the tile's rows repeat its last row and only
-//     reach accumulator rows that are never written out.
+//     reach accumulator rows that are never written out. Both x (paired once per call, before
+//     the GEMMs) and h (written so by the gate/up epilogue) hold each chunk of 8 inputs in pair
+//     order 0, 4, 1, 5, 2, 6, 3, 7, the order of the "128 + q" pairs, so A goes from LDS to the
+//     matrix cores unchanged.
 // A and the scales run in a ring of AS stages, AS - 1 steps ahead.
 // Addresses are a scalar base that advances per step plus a per-lane offset fixed for the run.
 // When K is an odd number of groups, the last step's second group reads in-bounds stand-in data
@@ -177,7 +180,6 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const int nb0 = run * R;
   const int njobs = min(R, ncb - nb0);
   if (njobs <= 0) return;
-  const int P = njobs * S;  // pipeline length in K steps
 
   // ---- weight matrices (for GU, waves 0, 1 load gate rows and waves 2, 3 up rows)
   const uint8_t* wc;
@@ -221,7 +223,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const uint16_t* abase;
   uint32_t aoff[MT], achk[MT];  // row offset, swizzled chunk offset within the step
   if (GU) {
-    abase = a.x;
+    abase = a.xp;
   } else {
     abase = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
   }
@@ -313,15 +315,11 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) {
           const int r = 16 * mm + n, c = 8 * gg + 2 * kb + kk;
-          const uint4 raw = *reinterpret_cast<const uint4*>(as + r * 256 + 16 * (c ^ a_swz(r)));
-          const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
-          uint32_t pr[4];
-          repair8(v, pr);
-          const uint4 av = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+          const uint4 av = *reinterpret_cast<const uint4*>(as + r * 256 + 16 * (c ^ a_swz(r)));
           const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
           tmp[0][mm] = mfma16x16x32(av, b0, kk == 0 ? z : tmp[0][mm]);
           tmp[1][mm] = mfma16x16x32(av, b1, kk == 0 ? z : tmp[1][mm]);
-          xs[mm] = mfma16x16x32(raw, ones, kk == 0 ? z : xs[mm]);
+          xs[mm] = mfma16x16x32(av, ones, kk == 0 ? z : xs[mm]);
         }
       }
       float s0, b0v, s1, b1v;
@@ -353,7 +351,8 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     const int n0 = (nb0 + j) * cols;
     if (GU) {
       uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
-      const int col = n0 + 16 * wave + n;
+      // h is stored in pair order, so that the down GEMM reads it as its A operand unchanged
+      const int col = pair_pos(n0 + 16 * wave + n);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
@@ -490,7 +489,7 @@ static GemmArgs gemm_args(const Ctx& c, int nruns) {
   a.P = c.P;
   a.max_tiles = c.max_tiles;
   a.nb = nruns;
-  a.x = c.x;
+  a.xp = c.xp;
   a.sorted_token = c.r.sorted_token;
   a.tiles = c.r.tiles;
   a.n_tiles = c.r.n_tiles;

@@ -21,7 +21,9 @@ struct Ctx {
   moe_routing r;      // routing arrays (caller's or carved from the workspace)
   float* router_parts;    // [T][E][d/64] router chunk partials (GEMV path, T <= kGemvMaxT)
   float* logits;          // [T][E] router logits (T >= 2)
-  uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1)
+  uint16_t* xp;           // [T][d] bf16: x with each 8-input chunk in pair order (grouped GEMM operand)
+  bool pair_in_meta;      // the routing-metadata launch also writes xp
+  uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1); pair order on the GEMM path
   uint16_t* hs;           // [T][Is] bf16
   float* y_rows;          // [P + T][d] fp32, grouped order, shared rows last
   uint16_t* y;            // [T][d] bf16
@@ -33,7 +35,8 @@ hipError_t launch_router_decode(const Ctx& c);
 hipError_t launch_decode_topk(const Ctx& c);
 hipError_t launch_router_prefill(const Ctx& c);  // logits [T][E]
 hipError_t launch_topk_prefill(const Ctx& c);    // logits -> topk_ids, topk_w
-hipError_t launch_route_meta(const Ctx& c);
+hipError_t launch_route_meta(const Ctx& c);  // + xp from x in extra blocks when c.pair_in_meta
+hipError_t launch_pair_x(const Ctx& c);      // xp from x
 // fused_topk: take the top-k from the router partials in every block, plus the shared expert's
 // rows in blocks of their own when its weights are set; otherwise read topk_ids and compute the
 // shared slot after each token's routed slots

@@ -74,7 +74,7 @@ bool gemv_path_ctx(const Ctx& c) {
 }
 
 struct Layout {
-  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, h, hs, y_rows, total;
+  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, xp, h, hs, y_rows, total;
 };
 
 Layout layout_of(const moe_dims& dm, int32_t T) {
@@ -101,6 +101,8 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   o += up((size_t)max_tiles_of(dm, T) * 12);
   L.n_tiles = o;
   o += up(4);
+  L.xp = o;
+  o += up((size_t)T * d * 2);
   L.h = o;
   o += up(P * dm.d_ff * 2);
   L.hs = o;
@@ -158,10 +160,12 @@ enum Stage {
   kGemvDown,          // GEMV down + weighted combine + shared
   kGemmGateup,
   kGemmDown,
-  kCombine
+  kCombine,
+  kPairX              // x in pair order for the grouped GEMM (moe_expert_ffn; the layer does it in kMeta)
 };
 const char* kStageNames[] = {"router_decode", "decode_topk", "router_prefill", "topk_prefill", "route_meta", "gemv_gateup_topk",
-                             "gemv_gateup", "gemv_down_combine", "gateup_gemm", "down_gemm", "combine"};
+                             "gemv_gateup", "gemv_down_combine", "gateup_gemm", "down_gemm", "combine",
+                             "pair_x"};
 
 int layer_stages(const moe_dims& dm, int32_t T, Stage* out) {
   int n = 0;
@@ -200,6 +204,7 @@ int run_stage(Stage s, const Ctx& c0) {
     case kGemmGateup: e = launch_gateup_gemm(c); break;
     case kGemmDown: e = launch_down_gemm(c); break;
     case kCombine: e = launch_combine(c); break;
+    case kPairX: e = launch_pair_x(c); break;
   }
   if (e != hipSuccess) return fail(MOE_EHIP, "launch of %s failed: %s", kStageNames[s], hipGetErrorString(e));
   return MOE_OK;
@@ -219,6 +224,8 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.max_tiles = max_tiles_of(dm, T);
   c.router_parts = reinterpret_cast<float*>(b + L.parts);
   c.logits = reinterpret_cast<float*>(b + L.logits);
+  c.xp = reinterpret_cast<uint16_t*>(b + L.xp);
+  c.pair_in_meta = false;
   c.h = reinterpret_cast<uint16_t*>(b + L.h);
   c.hs = reinterpret_cast<uint16_t*>(b + L.hs);
   c.y_rows = reinterpret_cast<float*>(b + L.y_rows);
@@ -271,6 +278,7 @@ int layer_ctx(Ctx& c, const moe_dims* dims, int32_t T, const uint16_t* x, const 
   c.routed = *routed;
   if (shared) c.shared = *shared;
   c.y = y;
+  c.pair_in_meta = true;  // the layer's metadata launch pairs x for its GEMMs
   return MOE_OK;
 }
 
@@ -332,6 +340,7 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe
     if (int rc = run_stage(kGemvGateup, c)) return rc;
     return run_stage(kGemvDown, c);
   }
+  if (int rc = run_stage(kPairX, c)) return rc;
   if (int rc = run_stage(kGemmGateup, c)) return rc;
   if (int rc = run_stage(kGemmDown, c)) return rc;
   return run_stage(kCombine, c);

@@ -8,6 +8,8 @@
 // Logit order (fixed so the top-k choice is unique): the input dimension is cut into chunks of
 // 64; a chunk partial is an fp32 fma chain over ascending inputs from +0; partials are added in
 // ascending chunk order to a +0 accumulator; the bias is added last.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -177,14 +179,52 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
 
 constexpr int kMetaBatch = 8;  // pairs per lane whose ids are loaded together
 
+// x in pair order for the grouped GEMM's A operand: each 16-byte chunk of 8 inputs is rewritten
+// as inputs 0, 4, 1, 5, 2, 6, 3, 7, the order of the weight pairs its matrix cores multiply, so
+// the GEMM reads it without re-pairing every time a column block uses the row. Thread i of
+// `nthreads` takes chunks i, i + nthreads, ...
+__device__ __forceinline__ void pair_x_chunks(const uint4* __restrict__ x, uint4* __restrict__ xp, int64_t nchunks,
+                                              int64_t i, int64_t nthreads) {
+  for (; i < nchunks; i += nthreads) {
+    const uint4 v = x[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t p[4];
+    repair8(w, p);
+    xp[i] = make_uint4(p[0], p[1], p[2], p[3]);
+  }
+}
+
+constexpr int kPairBlocks = 256;  // blocks that pair x (beside the metadata block, or alone)
+
+__global__ __launch_bounds__(256) void k_pair_x(const uint4* __restrict__ x, uint4* __restrict__ xp, int64_t nchunks) {
+  pair_x_chunks(x, xp, nchunks, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
+}
+
+static int pair_blocks(int64_t nchunks, int threads) {
+  return (int)std::min<int64_t>(kPairBlocks, (nchunks + threads - 1) / threads);
+}
+
+hipError_t launch_pair_x(const Ctx& c) {
+  const int64_t nchunks = (int64_t)c.T * c.d / 8;
+  hipLaunchKernelGGL(k_pair_x, dim3(pair_blocks(nchunks, 256)), dim3(256), 0, c.stream,
+                     reinterpret_cast<const uint4*>(c.x), reinterpret_cast<uint4*>(c.xp), nchunks);
+  return hipGetLastError();
+}
+
+// Blocks 1 .. gridDim.x - 1, when present, pair x instead (they need nothing from block 0).
 __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared,
                                                      const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
                                                      int32_t* __restrict__ inv_pos, int32_t* __restrict__ tiles,
-                                                     int32_t* __restrict__ n_tiles) {
+                                                     int32_t* __restrict__ n_tiles, const uint4* __restrict__ x,
+                                                     uint4* __restrict__ xp, int64_t nchunks) {
   __shared__ int s_tab[16][kMaxExperts];  // 64 KB: per-wave counts, then per-wave cursors
   __shared__ int s_wsum[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (blockIdx.x > 0) {
+    pair_x_chunks(x, xp, nchunks, (int64_t)(blockIdx.x - 1) * 1024 + tid, (int64_t)(gridDim.x - 1) * 1024);
+    return;
+  }
   const int P = T * k;
   for (int e = tid; e < E; e += 1024)
 #pragma unroll
@@ -279,8 +319,11 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
 }
 
 hipError_t launch_route_meta(const Ctx& c) {
-  hipLaunchKernelGGL(k_route_meta, dim3(1), dim3(1024), 0, c.stream, c.T, c.E, c.k, c.Is > 0 ? 1 : 0, c.r.topk_ids,
-                     c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos, c.r.tiles, c.r.n_tiles);
+  const int64_t nchunks = c.pair_in_meta ? (int64_t)c.T * c.d / 8 : 0;
+  const int nblocks = 1 + (nchunks ? pair_blocks(nchunks, 1024) : 0);
+  hipLaunchKernelGGL(k_route_meta, dim3(nblocks), dim3(1024), 0, c.stream, c.T, c.E, c.k, c.Is > 0 ? 1 : 0,
+                     c.r.topk_ids, c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos, c.r.tiles, c.r.n_tiles,
+                     reinterpret_cast<const uint4*>(c.x), reinterpret_cast<uint4*>(c.xp), nchunks);
   return hipGetLastError();
 }
 
