@@ -120,19 +120,20 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, void* l) {
+// The LDS destination is a wave-uniform 32-bit LDS address (the m0 value).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
-               "s"(lds_addr(l))
+               "s"(l)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, void* l) {
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t l) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
-               "s"(lds_addr(l))
+               "s"(l)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma2(const void* base, uint32_t off, void* l) {
+__device__ __forceinline__ void dma2(const void* base, uint32_t off, uint32_t l) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
-               "s"(lds_addr(l))
+               "s"(l)
                : "memory", "m0");
 }
 
@@ -178,8 +179,8 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const int ncb = (nrows_w + cols - 1) / cols;  // column blocks of this matrix
   const int R = GU ? kRunGu : kRunDn;
   const int nb0 = run * R;
-  const int njobs = min(R, ncb - nb0);
-  if (njobs <= 0) return;
+  if (nb0 >= ncb) return;
+  const int njobs = R == 1 ? 1 : min(R, ncb - nb0);
 
   // ---- weight matrices (for GU, waves 0, 1 load gate rows and waves 2, 3 up rows)
   const uint8_t* wc;
@@ -242,45 +243,77 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     achk[t] = 16u * (uint32_t)((lane & 15) ^ a_swz(r));
   }
 
-  // issue the code loads of step pair (job j, pair ss) into code stage st
-  auto issue_codes = [&](int j, int ss, int st) __attribute__((always_inline)) {
+  const int S2 = (S + 1) & ~1;
+  const int SP = S2 / 2;  // code pairs per job
+
+  // Load state of the job being issued, set once per job: uniform bases of its column block and
+  // per-lane offsets (weight rows past the matrix repeat its last row). Destinations are 32-bit
+  // LDS addresses: this wave's part of stage 0, plus the stage and load offsets.
+  const uint32_t lbase = lds_addr(lds);
+  const uint32_t lds_c = lbase + wave * 4096;
+  const uint32_t lds_a = lbase + 2 * kPairCodeStageBytes + wave * 1024;
+  const uint32_t lds_s = lbase + 2 * kPairCodeStageBytes + AS * kAS +
+                         (PAIRED ? 512 * (wave >> 1) + 256 * (wave & 1) : 1024 * (wave >> 1) + 512 * (wave & 1));
+  const uint8_t* cjb;
+  uint32_t coq[4];  // codes: row offset + swizzled chunk
+  auto setup_codes = [&](int j) __attribute__((always_inline)) {
     const int n0 = (nb0 + j) * cols;
-    const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
-    const uint32_t valid = (uint32_t)(ldc - 128 * ss);  // code bytes of the pair (32 .. 128)
-    uint8_t* cdst = Lc(st) + wave * 4096;
-    const uint8_t* cb = wc + (mrow + n0) * (size_t)ldc + 128 * ss;
+    const int lim = nrows_w - 1 - n0;
+    cjb = wc + (mrow + n0) * (size_t)ldc;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t q = cq16[t];
-      if (q + 16u > valid) q &= 16u;  // chunks past K re-read the pair's first group
-      dma16(cb, (uint32_t)min(crow[t], lim) * (uint32_t)ldc + q, cdst + 1024 * t);
+    for (int t = 0; t < 4; ++t) coq[t] = (uint32_t)min(crow[t], lim) * (uint32_t)ldc + cq16[t];
+  };
+  const uint16_t* sjb;
+  uint32_t so[2];  // scale/bias offsets in bytes
+  auto setup_sb = [&](int j) __attribute__((always_inline)) {
+    const int n0 = (nb0 + j) * cols;
+    const int lim = nrows_w - 1 - n0;
+    sjb = sb_arr + (mrow + n0) * (size_t)ldg;
+    if (PAIRED) {
+      so[0] = (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) so[t] = ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + (uint32_t)(lane & 1)) * 2u;
     }
   };
-  // issue the A and scale/bias loads of pipeline position (job j, step s) into stage st; the
-  // padding step (s == S) re-reads step S - 1
-  auto issue = [&](int j, int s, int st) __attribute__((always_inline)) {
-    s = min(s, S - 1);
-    const int n0 = (nb0 + j) * cols;
-    const int lim = nrows_w - 1 - n0;  // weight rows past the matrix repeat its last row
-    const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
-    if (PAIRED) {
-      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
-      dma4(sbb, (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg), Lsb(st) + 128 * (wave >> 1) + 64 * (wave & 1));
-    } else {
-      const uint16_t* sbb = sb_arr + (mrow + n0) * (size_t)ldg + 2 * s;
+  uint32_t aq[MT];  // A: row offset + swizzled chunk
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t g = tail ? 0u : (uint32_t)(lane & 1);
-        dma2(sbb, ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + g) * 2u,
-             Lsb(st) + 256 * (wave >> 1) + 128 * (wave & 1) + 64 * t);
+  for (int t = 0; t < MT; ++t) aq[t] = aoff[t] + achk[t];
+  const uint32_t vlast = (uint32_t)(ldc - 128 * (SP - 1));  // code bytes of a job's last pair (32 .. 128)
+
+  // issue the code loads of pair ss of the current code job into code stage st
+  auto issue_codes = [&](int ss, int st) __attribute__((always_inline)) {
+    const uint8_t* cb = cjb + 128 * ss;
+    const uint32_t dst = lds_c + st * kPairCodeStageBytes;
+    if (ss == SP - 1 && vlast < 128u) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t q = cq16[t];
+        if (q + 16u > vlast) q &= 16u;  // chunks past K re-read the pair's first group
+        dma16(cb, coq[t] - cq16[t] + q, dst + 1024 * t);
       }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dma16(cb, coq[t], dst + 1024 * t);
+    }
+  };
+  // issue the A and scale/bias loads of step s of the current job into stage st; the padding
+  // step (s == S) re-reads step S - 1
+  auto issue = [&](int s, int st) __attribute__((always_inline)) {
+    s = min(s, S - 1);
+    const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
+    const uint32_t sdst = lds_s + st * kSbBytes;
+    if (PAIRED) {
+      dma4(sjb + 2 * s, so[0], sdst);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) dma2(sjb + 2 * s, tail ? so[t] - 2u * (uint32_t)(lane & 1) : so[t], sdst + 256 * t);
     }
     const uint16_t* ab = abase + 128 * s;
+    const uint32_t adst = lds_a + st * kAS;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint32_t ch = tail ? (achk[t] & 127u) : achk[t];  // chunks past K re-read the first half
-      dma16(ab, aoff[t] + ch, La(st) + 1024 * (wave + 4 * t));
-    }
+    for (int t = 0; t < MT; ++t)  // chunks past K re-read the first half
+      dma16(ab, tail ? aoff[t] + (achk[t] & 127u) : aq[t], adst + 4096 * t);
   };
 
   const int n = lane & 15, kb = lane >> 4;
@@ -390,20 +423,19 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   // A stage is overwritten only after the barrier that follows its last read.
   constexpr int kOpsA = (PAIRED ? 1 : 2) + MT;  // A and scale/bias loads one wave issues per position
   constexpr int kOpsC = 4;                      // code loads one wave issues per pair
-  const int S2 = (S + 1) & ~1;
-  const int SP = S2 / 2;                        // code pairs per job
   const int P2 = njobs * S2;
   int ij = 0, is = 0;    // position being issued (job, step); stays at the last position
   int icj = 0, ics = 0;  // code pair being issued (job, pair); stays at the last pair
   int cj = 0, cs = 0;    // position being computed
   int kc = 0;            // code pairs issued so far (its parity picks the stage)
-  issue_codes(0, 0, 0);
+  setup_codes(0);
+  setup_sb(0);
+  issue_codes(0, 0);
   kc = 1;
-  issue(0, 0, 0);
+  issue(0, 0);
   if (AS == 3) {
-    ij = S2 > 1 ? 0 : 1;
-    is = S2 > 1 ? 1 : 0;
-    issue(ij, is, 1);
+    is = 1;  // S2 >= 2
+    issue(1, 1);
   }
   constexpr int kWaitEven = AS == 3 ? kOpsA : 0, kWaitOdd = kWaitEven + kOpsC;
   for (int p = 0; p < P2; p += 2 * AS) {
@@ -414,21 +446,21 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
           step_barrier<kWaitOdd>();
         else
           step_barrier<kWaitEven>();
-        if (ij < njobs - 1 || is < S2 - 1) {
-          if (++is == S2) {
-            is = 0;
-            ++ij;
-          }
+        if (is < S2 - 1) {
+          ++is;
+        } else if (R > 1 && ij < njobs - 1) {
+          is = 0;
+          setup_sb(++ij);
         }
-        issue(ij, is, (q + AS - 1) % AS);
+        issue(is, (q + AS - 1) % AS);
         if ((q & 1) == 0) {
-          if (icj < njobs - 1 || ics < SP - 1) {
-            if (++ics == SP) {
-              ics = 0;
-              ++icj;
-            }
+          if (ics < SP - 1) {
+            ++ics;
+          } else if (R > 1 && icj < njobs - 1) {
+            ics = 0;
+            setup_codes(++icj);
           }
-          issue_codes(icj, ics, kc & 1);
+          issue_codes(ics, kc & 1);
           ++kc;
         }
         if (cs < S) compute(q % AS, (cj * SP + (cs >> 1)) & 1, cs & 1, !PAIRED && cs == S - 1 && (ldg & 1));
