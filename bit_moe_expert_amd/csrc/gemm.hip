@@ -320,8 +320,15 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   // this lane's two weight rows in the block (subtiles 0 and 1)
   const int wrow0 = GU ? 16 * wave + n : 32 * wave + n;
   const int wrow1 = GU ? kGuCols + 16 * wave + n : 32 * wave + 16 + n;
-  const int cread0 = wrow0 * 128 + 8 * (kb & 1), cread1 = wrow1 * 128 + 8 * (kb & 1);
-  const int cswz0 = code_swz8(wrow0), cswz1 = code_swz8(wrow1);
+  // code read offsets within a pair stage for (second step of the pair h, group gg): row, the
+  // 8-byte half kb & 1 of the 16-byte chunk 4 h + 2 gg + (kb >> 1), XOR-swizzled by row
+  uint32_t crd[2][4];
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) {
+    const int q = 2 * hg + (kb >> 1);
+    crd[0][hg] = wrow0 * 128 + 8 * (kb & 1) + 16 * (q ^ code_swz8(wrow0));
+    crd[1][hg] = wrow1 * 128 + 8 * (kb & 1) + 16 * (q ^ code_swz8(wrow1));
+  }
   f32x4_t acc[2][MT];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -336,9 +343,8 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     const uint8_t* as = La(st);
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
-      const int q = 4 * h + 2 * gg + (kb >> 1);
-      const uint2 w0 = *reinterpret_cast<const uint2*>(cs + cread0 + 16 * (q ^ cswz0));
-      const uint2 w1 = *reinterpret_cast<const uint2*>(cs + cread1 + 16 * (q ^ cswz1));
+      const uint2 w0 = *reinterpret_cast<const uint2*>(cs + crd[0][2 * h + gg]);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(cs + crd[1][2 * h + gg]);
       f32x4_t tmp[2][MT], xs[MT];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -427,20 +433,21 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   int ij = 0, is = 0;    // position being issued (job, step); stays at the last position
   int icj = 0, ics = 0;  // code pair being issued (job, pair); stays at the last pair
   int cj = 0, cs = 0;    // position being computed
-  int kc = 0;            // code pairs issued so far (its parity picks the stage)
   setup_codes(0);
   setup_sb(0);
   issue_codes(0, 0);
-  kc = 1;
   issue(0, 0);
   if (AS == 3) {
     is = 1;  // S2 >= 2
     issue(1, 1);
   }
   constexpr int kWaitEven = AS == 3 ? kOpsA : 0, kWaitOdd = kWaitEven + kOpsC;
-  for (int p = 0; p < P2; p += 2 * AS) {
+  // kUnroll positions per iteration, a multiple of 2 AS (A stage q % AS) and of 4 (code stage
+  // (q >> 1) & 1: real pair i is issued as the i-th pair, into stage i & 1)
+  constexpr int kUnroll = AS == 3 ? 12 : 4;
+  for (int p = 0; p < P2; p += kUnroll) {
 #pragma unroll
-    for (int q = 0; q < 2 * AS; ++q) {
+    for (int q = 0; q < kUnroll; ++q) {
       if (q == 0 || p + q < P2) {
         if (q & 1)
           step_barrier<kWaitOdd>();
@@ -460,10 +467,9 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
             ics = 0;
             setup_codes(++icj);
           }
-          issue_codes(ics, kc & 1);
-          ++kc;
+          issue_codes(ics, ((q >> 1) + 1) & 1);  // the (pos / 2 + 1)-th pair issued
         }
-        if (cs < S) compute(q % AS, (cj * SP + (cs >> 1)) & 1, cs & 1, !PAIRED && cs == S - 1 && (ldg & 1));
+        if (cs < S) compute(q % AS, (q >> 1) & 1, q & 1, !PAIRED && cs == S - 1 && (ldg & 1));
         if (cs == S2 - 1) {
           finish(cj);
           cs = 0;
