@@ -123,8 +123,8 @@ def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
     if name == "gemv_gateup_topk":  # reads the router partials; routed slots + the shared expert's rows
         return 2 * act * per_w(I, d) + 2 * T * d + 2 * P * I + 4 * T * (d // 64) * E + \
             (2 * per_w(Is, d) + 2 * T * Is if Is else 0), 4 * d * (P * I + T * Is)
-    if name == "route_meta":
-        return 4 * P * 3 + 4 * (2 * E + 1), 0
+    if name == "route_meta":  # routing arrays; the layer's launch also rewrites x in pair order
+        return 4 * P * 3 + 4 * (2 * E + 1) + 2 * 2 * T * d, 0
     if name == "gemv_gateup":
         return 2 * (act * per_w(I, d) + (per_w(Is, d) if Is else 0)) + 2 * T * d + 2 * (P * I + T * Is), \
             4 * d * (P * I + T * Is)
