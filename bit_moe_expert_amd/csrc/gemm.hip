@@ -153,10 +153,12 @@ __device__ __forceinline__ void step_barrier() {
 // otherwise down (A = h rows, 128 weight rows of the down matrix, fp32 y_rows epilogue).
 // PAIRED: K is a multiple of 128 (whole steps; scale/bias pairs load as one dword).
 // MT: 16-row subtiles of A (1 for tiles of at most 16 rows, else 2); AS: depth of the A and
-// scale/bias ring (3 for MT = 1, 2 for MT = 2, so that both layouts fit the same LDS).
+// scale/bias ring, sized so that every layout fits the same LDS: 2 for MT = 2 (one step ahead),
+// 3 for MT = 1 with an odd group count (two steps ahead), 4 for MT = 1 with whole steps (a pair
+// of steps ahead, one barrier per pair).
 template <int MT, int AS, bool GU, bool PAIRED>
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
-  static_assert(AS == 2 || AS == 3, "A and scales run AS - 1 steps ahead");
+  static_assert(AS == 2 || AS == 3 || (AS == 4 && MT == 1 && PAIRED), "A and scale ring depth");
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
   constexpr int kAS = MT * kA16StageBytes;  // an A stage: 16 MT rows
   // code pair stage st (0, 1), and stage st of the scales and biases and of A, in the block's LDS
@@ -437,10 +439,50 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   setup_sb(0);
   issue_codes(0, 0);
   issue(0, 0);
-  if (AS == 3) {
+  if (AS >= 3) {
     is = 1;  // S2 >= 2
     issue(1, 1);
   }
+  if constexpr (AS == 4) {
+    // Positions are pairs of steps, one barrier per pair: position i computes pair i from code
+    // stage i & 1 and A/scale stages 2 (i & 1), 2 (i & 1) + 1, after issuing pair i + 1 into the
+    // other halves of the rings. Every load a position needs was issued one position earlier,
+    // and nothing younger is outstanding, so the barrier waits for all of this wave's loads.
+    is = 0;  // first step of the pair being issued
+    const int NP = njobs * SP;
+    for (int p = 0; p < NP; p += 2) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q == 0 || p + q < NP) {
+          step_barrier<0>();
+          if (is < S2 - 2) {
+            is += 2;
+          } else if (R > 1 && ij < njobs - 1) {
+            is = 0;
+            setup_sb(++ij);
+          }
+          issue(is, 2 * ((q + 1) & 1));
+          issue(is + 1, 2 * ((q + 1) & 1) + 1);
+          if (ics < SP - 1) {
+            ++ics;
+          } else if (R > 1 && icj < njobs - 1) {
+            ics = 0;
+            setup_codes(++icj);
+          }
+          issue_codes(ics, (q + 1) & 1);
+          if (cs < S) compute(2 * q, q, 0, false);
+          if (cs + 1 < S) compute(2 * q + 1, q, 1, false);
+          if (cs == S2 - 2) {
+            finish(cj);
+            cs = 0;
+            ++cj;
+          } else {
+            cs += 2;
+          }
+        }
+      }
+    }
+  } else {
   constexpr int kWaitEven = AS == 3 ? kOpsA : 0, kWaitOdd = kWaitEven + kOpsC;
   // kUnroll positions per iteration, a multiple of 2 AS (A stage q % AS) and of 4 (code stage
   // (q >> 1) & 1: real pair i is issued as the i-th pair, into stage i & 1)
@@ -480,6 +522,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
       }
     }
   }
+  }
   // the clamped loads past the end must land before the block (and its LDS) is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -487,11 +530,14 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 template <bool GU, bool PAIRED>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
-  // One LDS buffer, carved per tile height: two code pair stages, then three 16-row A stages and
-  // three scale stages (tiles of at most 16 rows) or two 32-row A stages and two scale stages.
+  // One LDS buffer, carved per tile height: two code pair stages, then four 16-row A stages and
+  // four scale stages (tiles of at most 16 rows, whole steps), three of each (at most 16 rows,
+  // K an odd number of groups), or two 32-row A stages and two scale stages.
   constexpr int kLds1 = 2 * kPairCodeStageBytes + 3 * kA16StageBytes + 3 * kSbBytes;
   constexpr int kLds2 = 2 * kPairCodeStageBytes + 2 * 2 * kA16StageBytes + 2 * kSbBytes;
-  constexpr int kLds = kLds1 > kLds2 ? kLds1 : kLds2;
+  constexpr int kLds4 = PAIRED ? 2 * kPairCodeStageBytes + 4 * kA16StageBytes + 4 * kSbBytes : 0;
+  constexpr int kLds12 = kLds1 > kLds2 ? kLds1 : kLds2;
+  constexpr int kLds = kLds12 > kLds4 ? kLds12 : kLds4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   int run, e, row0, rows;
   if (!block_tile(a, run, e, row0, rows)) return;
@@ -501,7 +547,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    run_body<1, 3, GU, PAIRED>(a, run, e, row0, rows, lds);
+    run_body<1, PAIRED ? 4 : 3, GU, PAIRED>(a, run, e, row0, rows, lds);
   else
     run_body<2, 2, GU, PAIRED>(a, run, e, row0, rows, lds);
 }
