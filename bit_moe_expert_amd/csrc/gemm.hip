@@ -102,7 +102,10 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 constexpr int kPairCodeStageBytes = 128 * 128;  // 128 weight rows x 256 inputs of codes
 constexpr int kA16StageBytes = 16 * 256;        // 16 A rows x 128 bf16
 constexpr int kRunGu = 1;                       // column blocks per gate/up work item
-constexpr int kRunDn = 2;                       // column blocks per down work item
+// column blocks per down work item: two when K is short (fewer than kRunMinSteps steps), so the
+// pipeline start is paid over more steps; one otherwise, for more blocks and a lean loop
+constexpr int kRunMinSteps = 6;
+inline int down_run(int I) { return (I + kBK - 1) / kBK < kRunMinSteps ? 2 : 1; }
 
 __device__ __forceinline__ int code_swz8(int r) { return r & 7; }
 __device__ __forceinline__ int a_swz(int r) { return r & 7; }
@@ -156,7 +159,7 @@ __device__ __forceinline__ void step_barrier() {
 // scale/bias ring, sized so that every layout fits the same LDS: 2 for MT = 2 (one step ahead),
 // 3 for MT = 1 with an odd group count (two steps ahead), 4 for MT = 1 with whole steps (a pair
 // of steps ahead, one barrier per pair).
-template <int MT, int AS, bool GU, bool PAIRED>
+template <int MT, int AS, bool GU, bool PAIRED, int R>
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
   static_assert(AS == 2 || AS == 3 || (AS == 4 && MT == 1 && PAIRED), "A and scale ring depth");
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
@@ -179,7 +182,6 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const int S = (K + kBK - 1) / kBK;
   const int cols = GU ? kGuCols : kDnCols;
   const int ncb = (nrows_w + cols - 1) / cols;  // column blocks of this matrix
-  const int R = GU ? kRunGu : kRunDn;
   const int nb0 = run * R;
   if (nb0 >= ncb) return;
   const int njobs = R == 1 ? 1 : min(R, ncb - nb0);
@@ -527,7 +529,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool GU, bool PAIRED>
+template <bool GU, bool PAIRED, int R>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
   // One LDS buffer, carved per tile height: two code pair stages, then four 16-row A stages and
@@ -547,19 +549,19 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    run_body<1, PAIRED ? 4 : 3, GU, PAIRED>(a, run, e, row0, rows, lds);
+    run_body<1, PAIRED ? 4 : 3, GU, PAIRED, R>(a, run, e, row0, rows, lds);
   else
-    run_body<2, 2, GU, PAIRED>(a, run, e, row0, rows, lds);
+    run_body<2, 2, GU, PAIRED, R>(a, run, e, row0, rows, lds);
 }
 
 template <bool PAIRED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_gemm(GemmArgs a) {
-  gemm_block<true, PAIRED>(a);
+  gemm_block<true, PAIRED, kRunGu>(a);
 }
 
-template <bool PAIRED>
+template <bool PAIRED, int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_gemm(GemmArgs a) {
-  gemm_block<false, PAIRED>(a);
+  gemm_block<false, PAIRED, R>(a);
 }
 
 static GemmArgs gemm_args(const Ctx& c, int nruns) {
@@ -604,14 +606,20 @@ hipError_t launch_gateup_gemm(const Ctx& c) {
 
 hipError_t launch_down_gemm(const Ctx& c) {
   const int ncb = (c.d + kDnCols - 1) / kDnCols;
-  const int nruns = (ncb + kRunDn - 1) / kRunDn;
+  const int R = down_run(c.I);
+  const int nruns = (ncb + R - 1) / R;
   const dim3 grid(grid_blocks(c.max_tiles, nruns));
   // both the routed and the shared matrix must be whole steps for the paired form
   const bool paired = c.I % kBK == 0 && (c.Is == 0 || c.Is % kBK == 0);
-  if (paired)
-    hipLaunchKernelGGL(k_down_gemm<true>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  const GemmArgs a = gemm_args(c, nruns);
+  if (paired && R == 1)
+    hipLaunchKernelGGL((k_down_gemm<true, 1>), grid, dim3(256), 0, c.stream, a);
+  else if (paired)
+    hipLaunchKernelGGL((k_down_gemm<true, 2>), grid, dim3(256), 0, c.stream, a);
+  else if (R == 1)
+    hipLaunchKernelGGL((k_down_gemm<false, 1>), grid, dim3(256), 0, c.stream, a);
   else
-    hipLaunchKernelGGL(k_down_gemm<false>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+    hipLaunchKernelGGL((k_down_gemm<false, 2>), grid, dim3(256), 0, c.stream, a);
   return hipGetLastError();
 }
 

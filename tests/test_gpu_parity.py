@@ -166,6 +166,9 @@ SHAPES = [
     # 1024 experts (the long top-k path), expert counts that are not a multiple of 64
     (40, 4096, 64, 8, 256, 128), (1, 4096, 64, 8, 256, 128), (3, 256, 1024, 16, 64, 64),
     (70, 256, 1024, 16, 64, 0), (64, 128, 300, 5, 192, 64), (2, 128, 300, 5, 192, 64),
+    # down reductions of 6 steps or more (one output column block per down work item): whole
+    # steps, an odd group count, and a shared size that is not whole steps
+    (64, 128, 8, 4, 1024, 1024), (40, 256, 8, 2, 832, 0), (35, 192, 4, 2, 768, 320),
 ]
 
 
