@@ -304,8 +304,7 @@ def main() -> int:
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the sharding design is described "
-              "in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.workload in gen.VOCAB_WORKLOADS:
