@@ -185,7 +185,7 @@ def test_decode_falls_back_to_grouped_gemm_when_h_is_large():
 
 
 # ------------------------------------------------------------------ composition and determinism
-@pytest.mark.parametrize("name", ["prefill", "decode", "m4", "m8"])
+@pytest.mark.parametrize("name", ["prefill", "decode", "m4", "m8", "diffusion", "long"])
 def test_route_then_expert_ffn_equals_forward_and_is_deterministic(name):
     w = gen.WORKLOADS[name]
     L = gen.layer(w, 0)
