@@ -35,41 +35,43 @@ hipError_t launch_decode_topk(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill (T >= 2) logits: a block owns 8 tokens x 64 experts (lane = expert). The block first
-// stages the 8 tokens' inputs in LDS as fp32 [input][token] (every thread issues all of its
-// loads before converting any); its 16 waves then take the 64-input chunks w, w + 16, ...: a
+// Prefill (T >= 2) logits: a block owns TOK tokens (8 or 16) x 64 experts (lane = expert). The
+// block first stages the tokens' inputs in LDS as fp32 [input][token] (every thread issues all of
+// its loads before converting any); its 16 waves then take the 64-input chunks w, w + 16, ...: a
 // wave loads the chunk's 64 router values of its expert and runs one fma chain per token over
-// ascending inputs. The chunk partials meet in LDS and one thread per (token, expert) adds them
-// in chunk order, then the bias. Up to kRpMaxD inputs are staged at once (larger d in passes).
-constexpr int kRpTok = 8;
+// ascending inputs, so each router value feeds TOK chains. The chunk partials meet in LDS and
+// one thread per (token, expert) adds them in chunk order, then the bias. 16384 / TOK inputs are
+// staged per pass (64 KB either way; larger d in passes). 16 tokens per block halve the router
+// loads per fma but also the block count, so they are used when the grid still has a block per CU.
 constexpr int kRpWaves = 16;
-constexpr int kRpMaxD = 2048;                    // inputs staged per pass
-constexpr int kRpMaxChunks = kRpMaxD / kGroup;   // 32 chunks per pass
 
+template <int TOK>
 __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, const uint16_t* __restrict__ x,
                                                          const float* __restrict__ wr, const float* __restrict__ bias,
                                                          float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) float s_x[kRpMaxD][kRpTok];           // 64 KB, [input][token]
-  __shared__ float s_parts[kRpMaxChunks][kRpTok][64];                           // 64 KB
+  constexpr int kMaxD = 16384 / TOK;              // inputs staged per pass
+  constexpr int kMaxChunks = kMaxD / kGroup;
+  __shared__ __attribute__((aligned(16))) float s_x[kMaxD][TOK];  // 64 KB, [input][token]
+  __shared__ float s_parts[kMaxChunks][TOK][64];                  // 64 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kRpTok;
+  const int t0 = blockIdx.x * TOK;
   const int e = blockIdx.y * 64 + lane;
   const int ec = e < E ? e : E - 1;  // experts past E compute a copy that is never stored
   const int nchunks = d / kGroup;
-  const int s_tok = tid >> 6, s_e = blockIdx.y * 64 + lane;  // sum phase: threads 0..511
+  const int s_tok = tid >> 6, s_e = blockIdx.y * 64 + lane;  // sum phase: threads 0 .. 64 TOK - 1
   float acc = 0.0f;
-  for (int p = 0; p < nchunks; p += kRpMaxChunks) {
-    const int npass = min(kRpMaxChunks, nchunks - p);
+  for (int p = 0; p < nchunks; p += kMaxChunks) {
+    const int npass = min(kMaxChunks, nchunks - p);
     const int nin = npass * kGroup;
-    // stage inputs p*64 .. p*64 + nin of the 8 tokens: thread i takes inputs i and i + 1024
-    constexpr int kH = kRpMaxD / 1024;
-    uint16_t v[kH][kRpTok];
+    // stage inputs p*64 .. p*64 + nin of the tokens: thread i takes inputs i, i + 1024, ...
+    constexpr int kH = kMaxD / 1024;
+    uint16_t v[kH][TOK];
 #pragma unroll
     for (int h = 0; h < kH; ++h) {
       const int i = tid + 1024 * h;
       const int ic = i < nin ? i : 0;
 #pragma unroll
-      for (int tk = 0; tk < kRpTok; ++tk) {
+      for (int tk = 0; tk < TOK; ++tk) {
         const int t = min(t0 + tk, T - 1);
         v[h][tk] = x[(size_t)t * d + (size_t)p * kGroup + ic];
       }
@@ -79,8 +81,10 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
       const int i = tid + 1024 * h;
       if (i < nin) {
         float4* dst = reinterpret_cast<float4*>(&s_x[i][0]);
-        dst[0] = make_float4(bf16_to_f32(v[h][0]), bf16_to_f32(v[h][1]), bf16_to_f32(v[h][2]), bf16_to_f32(v[h][3]));
-        dst[1] = make_float4(bf16_to_f32(v[h][4]), bf16_to_f32(v[h][5]), bf16_to_f32(v[h][6]), bf16_to_f32(v[h][7]));
+#pragma unroll
+        for (int q = 0; q < TOK / 4; ++q)
+          dst[q] = make_float4(bf16_to_f32(v[h][4 * q]), bf16_to_f32(v[h][4 * q + 1]), bf16_to_f32(v[h][4 * q + 2]),
+                               bf16_to_f32(v[h][4 * q + 3]));
       }
     }
     __syncthreads();
@@ -90,26 +94,32 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
       const float* wp = wr + (size_t)c * kGroup * E + ec;
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) wv[i] = wp[(size_t)i * E];
-      float pr[kRpTok];
+      float pr[TOK];
 #pragma unroll
-      for (int tk = 0; tk < kRpTok; ++tk) pr[tk] = 0.0f;
+      for (int tk = 0; tk < TOK; ++tk) pr[tk] = 0.0f;
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        const float4 xa = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][0]);
-        const float4 xb = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][4]);
-        const float xs[kRpTok] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        float xs[TOK];
 #pragma unroll
-        for (int tk = 0; tk < kRpTok; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
+        for (int q = 0; q < TOK / 4; ++q) {
+          const float4 xq = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][4 * q]);
+          xs[4 * q] = xq.x;
+          xs[4 * q + 1] = xq.y;
+          xs[4 * q + 2] = xq.z;
+          xs[4 * q + 3] = xq.w;
+        }
+#pragma unroll
+        for (int tk = 0; tk < TOK; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
       }
 #pragma unroll
-      for (int tk = 0; tk < kRpTok; ++tk) s_parts[cc][tk][lane] = pr[tk];
+      for (int tk = 0; tk < TOK; ++tk) s_parts[cc][tk][lane] = pr[tk];
     }
     __syncthreads();
-    if (tid < kRpTok * 64)
+    if (tid < TOK * 64)
       for (int cc = 0; cc < npass; ++cc) acc = acc + s_parts[cc][s_tok][lane];
     __syncthreads();
   }
-  if (tid < kRpTok * 64 && t0 + s_tok < T && s_e < E) {
+  if (tid < TOK * 64 && t0 + s_tok < T && s_e < E) {
     float v = acc;
     if (bias) v = v + bias[s_e];
     logits[(size_t)(t0 + s_tok) * E + s_e] = v;
@@ -117,9 +127,16 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
 }
 
 hipError_t launch_router_prefill(const Ctx& c) {
-  const dim3 grid((c.T + kRpTok - 1) / kRpTok, (c.E + 63) / 64);
-  hipLaunchKernelGGL(k_router_prefill, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router, c.logit_bias,
-                     c.logits);
+  const int ne = (c.E + 63) / 64;
+  if (((c.T + 15) / 16) * ne >= 256) {
+    const dim3 grid((c.T + 15) / 16, ne);
+    hipLaunchKernelGGL(k_router_prefill<16>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
+                       c.logit_bias, c.logits);
+  } else {
+    const dim3 grid((c.T + 7) / 8, ne);
+    hipLaunchKernelGGL(k_router_prefill<8>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
+                       c.logit_bias, c.logits);
+  }
   return hipGetLastError();
 }
 

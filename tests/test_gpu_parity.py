@@ -169,6 +169,9 @@ SHAPES = [
     # down reductions of 6 steps or more (one output column block per down work item): whole
     # steps, an odd group count, and a shared size that is not whole steps
     (64, 128, 8, 4, 1024, 1024), (40, 256, 8, 2, 832, 0), (35, 192, 4, 2, 768, 320),
+    # enough tokens for the 16-token router blocks, with a partial last token block and a
+    # partial last expert block
+    (1000, 128, 300, 5, 64, 64),
 ]
 
 
