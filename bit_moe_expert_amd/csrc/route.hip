@@ -35,14 +35,15 @@ hipError_t launch_decode_topk(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill (T >= 2) logits: a block owns TOK tokens (8 or 16) x 64 experts (lane = expert). The
+// Prefill (T >= 2) logits: a block owns TOK tokens (4, 8 or 16) x 64 experts (lane = expert). The
 // block first stages the tokens' inputs in LDS as fp32 [input][token] (every thread issues all of
 // its loads before converting any); its 16 waves then take the 64-input chunks w, w + 16, ...: a
 // wave loads the chunk's 64 router values of its expert and runs one fma chain per token over
 // ascending inputs, so each router value feeds TOK chains. The chunk partials meet in LDS and
 // one thread per (token, expert) adds them in chunk order, then the bias. 16384 / TOK inputs are
-// staged per pass (64 KB either way; larger d in passes). 16 tokens per block halve the router
-// loads per fma but also the block count, so they are used when the grid still has a block per CU.
+// staged per pass (64 KB in every case; larger d in passes). More tokens per block mean fewer
+// router loads per fma but fewer blocks: the launch takes the most tokens per block that still
+// give 256 blocks, and 4 when none does (small calls, where the block count is what matters).
 constexpr int kRpWaves = 16;
 
 template <int TOK>
@@ -132,9 +133,13 @@ hipError_t launch_router_prefill(const Ctx& c) {
     const dim3 grid((c.T + 15) / 16, ne);
     hipLaunchKernelGGL(k_router_prefill<16>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
                        c.logit_bias, c.logits);
-  } else {
+  } else if (((c.T + 7) / 8) * ne >= 256) {
     const dim3 grid((c.T + 7) / 8, ne);
     hipLaunchKernelGGL(k_router_prefill<8>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
+                       c.logit_bias, c.logits);
+  } else {
+    const dim3 grid((c.T + 3) / 4, ne);
+    hipLaunchKernelGGL(k_router_prefill<4>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
                        c.logit_bias, c.logits);
   }
   return hipGetLastError();
