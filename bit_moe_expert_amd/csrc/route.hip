@@ -306,8 +306,10 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
   }
   if (tid == 0) *n_tiles = n_routed + n_shared;
   __syncthreads();
-  // pass 2: stable ranks
+  // pass 2: stable ranks. This pass is bound by the single block's VALU issue, so each step is
+  // kept short (the token index comes from an fp32 reciprocal, not an integer division).
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
+  const float inv_k = 1.0f / (float)k;
   for (int base = p_begin; base < p_end; base += 64 * kMetaBatch) {
     int ev[kMetaBatch];
 #pragma unroll
@@ -321,6 +323,10 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
       const int p = base + lane + 64 * i;
       const int e = ev[i];
       const bool valid = (unsigned)e < (unsigned)E;
+      // p / k through the fp32 reciprocal (p < 2^21 is exact in fp32), then corrected by one
+      int tq = (int)((float)p * inv_k);
+      const int r = p - tq * k;
+      tq += r >= k ? 1 : (r < 0 ? -1 : 0);
       uint64_t peers = __ballot(valid);
       for (int b = 0; b < nbits; ++b) {
         const bool bit = (e >> b) & 1;
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
       if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
       __builtin_amdgcn_wave_barrier();
       if (valid) {
-        sorted_token[pos] = p / k;
+        sorted_token[pos] = tq;
         inv_pos[p] = pos;
       }
     }
