@@ -9,8 +9,11 @@ Also reported, on the same stream with HIP events: each kernel's average duratio
 dominant kernel's algorithmic bytes (or flops) per launch and its roofline fraction, and the
 CPU oracle timed on the host cores on a bounded sample of the same workload.
 
-Other workloads (--workload prefill|long|diffusion|tiny) exist for measurement; the one-line
-JSON contract is the same.
+The same line also carries, under "workloads", the tiny, prefill (T=512), long (4 x 1024,
+Zipf-skewed) and diffusion (T=256 x 30 layers) workloads, each with tokens/s, time per layer
+call, the whole-layer roofline fraction (HBM and matrix-core), the dominant kernel's fraction,
+per-stage times and the oracle timed beside it (--extra selects them; --workload picks the
+headline).
 
 Fail-closed: nothing is reported unless layer outputs match the CPU oracle and the graph
 replays reproduce the eager results bit for bit.
@@ -162,22 +165,37 @@ def traffic_from_profiles(workload: str, kernel: str):
 
 
 # ------------------------------------------------------------------------- CPU oracle baseline
-def cpu_baseline(w: gen.Workload, host_layers, seconds: float):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_cycle(w: gen.Workload, n_layers: int, seconds: float):
+    """The oracle on the workload's own calls, layer after layer of its cycle (each layer regenerated
+    on the host between calls, outside the timed region), until the cycle is done or `seconds` of
+    oracle time have passed. Only the oracle calls are timed."""
     from oracle import oracle
-    n_calls, tokens, t0 = 0, 0, time.perf_counter()
-    i = 0
-    while True:
-        L, x = host_layers[i % len(host_layers)]
+    spent, tokens, calls = 0.0, 0, 0
+    for li in range(n_layers):
+        L = gen.layer(w, li)
+        x = gen.tokens(w, li, li if w.calls > 1 else 0)
+        t0 = time.perf_counter()
         oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])
-        n_calls += 1
+        spent += time.perf_counter() - t0
         tokens += x.shape[0]
-        i += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
+        calls += 1
+        del L
+        if spent >= seconds:
             break
-    return {"value": tokens / el, "unit": "MoE-layer tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n_calls} layer calls of the same workload ({tokens} layer-tokens, first "
-                      f"{len(host_layers)} layers cycled), {el:.1f} s"}
+    return {"value": tokens / spent, "unit": "MoE-layer tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"{calls} layer calls of {w.chunk} tokens (layers 0..{calls - 1} of the {n_layers}-layer cycle), "
+                      f"{spent:.1f} s of oracle time"}
 
 
 # ------------------------------------------------------------------------- exact top-K of logit rows
@@ -291,71 +309,64 @@ def main_vocab(args) -> int:
     return 0
 
 
-# ------------------------------------------------------------------------- main
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=sorted(PLAN) + sorted(gen.VOCAB_WORKLOADS))
-    ap.add_argument("--stage-reps", type=int, default=200, help="timed launches per stage")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (counter scale)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
-        return 2
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
-    if args.workload in gen.VOCAB_WORKLOADS:
-        return main_vocab(args)
-    dev = torch.device("cuda:0")
-    w = gen.WORKLOADS[args.workload]
-    n_layers, calls = PLAN[args.workload]
+# ------------------------------------------------------------------------- one workload
+def layer_work(w: gen.Workload, counts: np.ndarray):
+    """(bytes, expert flops) the method itself must move / do in one layer call: the packed weights
+    of the experts with at least one row and of the shared expert, the router matrix, x and y; the
+    flops of the expert products (2 per weight per row, no padding)."""
+    d, E, k, I, Is, T = w.d, w.E, w.k, w.I, w.Is, w.chunk
+    per_w = lambda out, inn: out * inn * w.bits // 8 + 2 * 2 * out * inn // 64  # noqa: E731
+    act = int((counts > 0).sum())
+    wb = act * 3 * per_w(I, d) + (3 * per_w(Is, d) if Is else 0)
+    return wb + 4 * d * E + 2 * 2 * T * d, 2 * 3 * d * (T * k * I + T * Is)
+
+
+def run_workload(name: str, args, dev, cpu_seconds: float, headline: bool) -> dict:
+    """Parity gate, a HIP graph of one step timed with events, per-stage times, whole-layer and
+    dominant-kernel roofline fractions and the oracle beside it, for one workload."""
+    w = gen.WORKLOADS[name]
+    n_layers, calls = PLAN[name]
     T = w.chunk
 
     # ---- inputs (seeded, synthetic), resident in HBM before timing
     t0 = time.perf_counter()
-    layers, xs, host_keep = [], [], []
+    layers, xs = [], []
     for li in range(n_layers):
         L = gen.layer(w, li)
-        x = gen.tokens(w, li, li if w.calls > 1 else 0)
         layers.append(to_layer(L, w.k, dev))
-        xs.append(bf16_dev(x, dev))
-        if li < 4:
-            host_keep.append((L, x))
+        xs.append(bf16_dev(gen.tokens(w, li, li if w.calls > 1 else 0), dev))
         del L
     ys = [torch.empty_like(x) for x in xs]
     wss = [lay.workspace(T) for lay in layers]
     torch.cuda.synchronize()
-    log(f"{n_layers} layers resident on {torch.cuda.get_device_name(dev)} in {time.perf_counter() - t0:.1f} s "
+    log(f"{name}: {n_layers} layers resident in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated(dev) / 1e9:.2f} GB)")
     order = [(i % n_layers) for i in range(calls)]
 
-    # ---- eager pass + parity gate against the oracle (fail-closed)
-    for c, li in enumerate(order):
+    # ---- eager pass + parity gate against the oracle on whole calls (fail-closed); the oracle's
+    # time on these calls is the CPU baseline of the non-headline workloads
+    for li in order:
         layers[li].forward(xs[li], wss[li], ys[li])
     torch.cuda.synchronize()
     eager = [ys[li].clone() for li in range(n_layers)]
     from oracle import oracle
-    worst = 0.0
+    worst, o_time, o_tok, o_calls = 0.0, 0.0, 0, 0
     for li in range(min(2, n_layers)):
-        L, x = host_keep[li]
-        if T <= 512:
-            ref = oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])["y"]
-            got = bits_of(eager[li])
-        else:
-            sel = np.linspace(0, T - 1, 8).astype(np.int32)
-            ref = oracle.forward_tokens(x, L["w_router"], L["routed"], L["shared"], w.k, sel, L["logit_bias"])["y"]
-            got = bits_of(eager[li])[sel]
-        r, g = f32_of_bits(ref), f32_of_bits(got)
+        L = gen.layer(w, li)
+        x = gen.tokens(w, li, li if w.calls > 1 else 0)
+        t1 = time.perf_counter()
+        ref = oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])["y"]
+        o_time += time.perf_counter() - t1
+        o_tok += x.shape[0]
+        o_calls += 1
+        r, g = f32_of_bits(ref), f32_of_bits(bits_of(eager[li]))
         tol = 1e-2 * np.abs(r).max() + 1e-3
         err = float(np.abs(g - r).max())
         worst = max(worst, err / tol)
         if not err <= tol:
-            log(f"PARITY FAILED on layer {li}: max err {err} > {tol}; no throughput reported")
-            return 1
-    log(f"parity vs oracle ok (worst error {worst:.3f} of the allowance)")
+            raise RuntimeError(f"{name}: PARITY FAILED on layer {li}: max err {err} > {tol}; no throughput reported")
+        del L
+    log(f"{name}: parity vs oracle ok on {o_calls} whole calls (worst error {worst:.3f} of the allowance)")
 
     # ---- HIP graph of one step
     g = torch.cuda.CUDAGraph()
@@ -383,11 +394,13 @@ def main() -> int:
     ms_step = e0.elapsed_time(e1) / args.steps
     for li in range(n_layers):  # replays must reproduce the eager results
         if not torch.equal(ys[li].view(torch.int16), eager[li].view(torch.int16)):
-            log(f"graph replay differs from eager on layer {li}; no throughput reported")
-            return 1
+            raise RuntimeError(f"{name}: graph replay differs from eager on layer {li}; no throughput reported")
+    del g
     tokens_per_step = calls * T
     value = tokens_per_step / (ms_step / 1e3)
-    log(f"step {ms_step * 1e3:.1f} us for {calls} layer calls -> {value:,.0f} MoE-layer tokens/s")
+    us_call = ms_step * 1e3 / calls
+    log(f"{name}: step {ms_step * 1e3:.1f} us for {calls} layer calls ({us_call:.2f} us each) -> "
+        f"{value:,.0f} MoE-layer tokens/s")
 
     # ---- per-kernel durations: each stage alone, captured as a HIP graph of back-to-back launches
     # that cycle the layers (so weights stream from HBM), timed with events on the launch stream
@@ -400,7 +413,7 @@ def main() -> int:
     launch_layers = [i % n_layers for i in range(per_graph)]
     reps = max(1, args.stage_reps // per_graph)
     stages = {}
-    for s, name in enumerate(names):
+    for s, sname in enumerate(names):
         gs = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gs):
             for li in launch_layers:
@@ -414,16 +427,100 @@ def main() -> int:
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (reps * per_graph)
-        wb = float(np.mean([stage_work(w, name, counts[li])[0] for li in launch_layers]))
-        wf = float(np.mean([stage_work(w, name, counts[li])[1] for li in launch_layers]))
-        stages[name] = {"us": round(us, 3), "bytes": int(wb), "flops": int(wf),
-                        "GBps": round(wb / us / 1e3, 1), "TFLOPs": round(wf / us / 1e6, 2)}
-        log(f"  {name:18s} {us:8.2f} us  {wb / 1e6:9.3f} MB  {wb / us / 1e3:8.1f} GB/s  {wf / us / 1e6:7.2f} TFLOP/s")
+        wb = float(np.mean([stage_work(w, sname, counts[li])[0] for li in launch_layers]))
+        wf = float(np.mean([stage_work(w, sname, counts[li])[1] for li in launch_layers]))
+        stages[sname] = {"us": round(us, 3), "bytes": int(wb), "flops": int(wf),
+                         "GBps": round(wb / us / 1e3, 1), "TFLOPs": round(wf / us / 1e6, 2)}
+        log(f"  {sname:18s} {us:8.2f} us  {wb / 1e6:9.3f} MB  {wb / us / 1e3:8.1f} GB/s  {wf / us / 1e6:7.2f} TFLOP/s")
         del gs
     for li in range(n_layers):  # the stage loop leaves every layer's outputs as the eager pass did
         if not torch.equal(ys[li].view(torch.int16), eager[li].view(torch.int16)):
-            log(f"stage launches changed layer {li}'s output")
-            return 1
+            raise RuntimeError(f"{name}: stage launches changed layer {li}'s output")
+
+    # ---- whole-layer roofline: algorithmic bytes and expert flops per call against the call time
+    lw = [layer_work(w, counts[li]) for li in order]
+    lb = float(np.mean([b for b, _ in lw]))
+    lf = float(np.mean([f for _, f in lw]))
+    t_hbm = lb / (HBM_PEAK_GBS * 1e9)
+    t_mfma = lf / (MFMA_BF16_PEAK_TFS * 1e12)
+    layer = {"bytes_per_call": int(lb), "expert_flops_per_call": int(lf), "us_per_call": round(us_call, 3),
+             "hbm_frac": round(lb / (us_call * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+             "mfma_frac": round(lf / (us_call * 1e-6) / (MFMA_BF16_PEAK_TFS * 1e12), 4),
+             "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+             "floor_us": round(max(t_hbm, t_mfma) * 1e6, 3),
+             "roofline_frac": round(max(t_hbm, t_mfma) * 1e6 / us_call, 4)}
+
+    # ---- roofline of the dominant kernel (the gate/up stage of the path this call takes)
+    dom = next((s for s in (DOMINANT[name], "gemv_gateup_topk", "gateup_gemm") if s in stages), None)
+    if dom is None:
+        raise RuntimeError(f"{name}: no gate/up stage on this call's path; stages: {list(stages)}")
+    st = stages[dom]
+    k_hbm = st["bytes"] / (HBM_PEAK_GBS * 1e9)
+    k_mfma = st["flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+    if k_hbm >= k_mfma:
+        roof = {"bound": "hbm", "achieved": st["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(st["GBps"] / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": st["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(st["TFLOPs"] / MFMA_BF16_PEAK_TFS, 4)}
+    roof.update(kernel=dom, bytes_per_launch=st["bytes"], flops_per_launch=st["flops"], avg_us=st["us"],
+                hbm_frac=round(st["GBps"] / HBM_PEAK_GBS, 4), mfma_frac=round(st["TFLOPs"] / MFMA_BF16_PEAK_TFS, 4),
+                traffic=traffic_from_profiles(name, dom))
+
+    res = {"workload": DESCR[name], "tokens_per_s": round(value, 1), "ms_per_step": round(ms_step, 6),
+           "tokens_per_call": T, "layer_calls_per_step": calls, "parity_worst_of_allowance": round(worst, 4),
+           "layer": layer, "roofline": roof, "stages": stages}
+    # ---- the oracle beside it: the headline cycles its layers; the others report the oracle's
+    # time on the parity calls above (whole calls of the same workload)
+    if not args.no_cpu:
+        if headline:
+            res["cpu_baseline"] = cpu_baseline_cycle(w, n_layers, cpu_seconds)
+        else:
+            res["cpu_baseline"] = {"value": o_tok / o_time, "unit": "MoE-layer tokens/s", "cores": oracle.num_threads(),
+                                   "kind": "oracle", "cpu": cpu_model(),
+                                   "sample": f"{o_calls} whole layer calls of {T} tokens (the parity calls), "
+                                             f"{o_time:.1f} s of oracle time"}
+        log(f"{name}: cpu oracle {res['cpu_baseline']['value']:.2f} tokens/s on {res['cpu_baseline']['cores']} threads")
+    del layers, xs, ys, wss, eager
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------- main
+EXTRA_DEFAULT = "tiny,prefill,long,diffusion"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=sorted(PLAN) + sorted(gen.VOCAB_WORKLOADS))
+    ap.add_argument("--extra", default=EXTRA_DEFAULT,
+                    help="comma-separated workloads measured after the headline one and reported under "
+                         "'workloads' in the same JSON line ('' for none)")
+    ap.add_argument("--stage-reps", type=int, default=200, help="timed launches per stage")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        return 2
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.workload in gen.VOCAB_WORKLOADS:
+        return main_vocab(args)
+    dev = torch.device("cuda:0")
+    log(f"device {torch.cuda.get_device_name(dev)}; host {cpu_model()}")
+    try:
+        head = run_workload(args.workload, args, dev, args.cpu_seconds, headline=True)
+        extras = {}
+        for name in [n for n in args.extra.split(",") if n and n != args.workload]:
+            extras[name] = run_workload(name, args, dev, args.cpu_seconds, headline=False)
+    except RuntimeError as e:
+        log(str(e))
+        return 1
 
     if args.calib_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -432,39 +529,20 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
 
-    # ---- roofline of the dominant kernel
-    # the gate/up stage of whichever path this call takes (the GEMV tier's bound is a build choice)
-    dom = next((s for s in (DOMINANT[args.workload], "gemv_gateup_topk", "gateup_gemm") if s in stages), None)
-    if dom is None:
-        log(f"no gate/up stage on this call's path; stages: {list(stages)}")
-        return 1
-    st = stages[dom]
-    bound = "hbm"
-    if args.workload == "long":
-        bound = "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": st["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(st["GBps"] / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": st["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(st["TFLOPs"] / MFMA_BF16_PEAK_TFS, 4)}
-    roof["kernel"] = dom
-    roof["bytes_per_launch"] = st["bytes"]
-    roof["flops_per_launch"] = st["flops"]
-    roof["avg_us"] = st["us"]
-    roof["traffic"] = traffic_from_profiles(args.workload, dom)
-
+    w = gen.WORKLOADS[args.workload]
     out = {
-        "metric": "MoE-layer tokens/s", "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "metric": "MoE-layer tokens/s", "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded generator)",
-        "config": {"workload": DESCR[args.workload], "tokens_per_call": T, "layer_calls_per_step": calls,
-                   "parallelism": "single GPU"},
-        "roofline": roof, "stages": stages,
+        "config": {"workload": DESCR[args.workload], "tokens_per_call": w.chunk,
+                   "layer_calls_per_step": head["layer_calls_per_step"], "parallelism": "single GPU"},
+        "roofline": head["roofline"], "layer": head["layer"], "stages": head["stages"],
+        "parity_worst_of_allowance": head["parity_worst_of_allowance"],
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, host_keep, args.cpu_seconds)
-        log(f"cpu oracle: {out['cpu_baseline']['value']:.2f} tokens/s on {out['cpu_baseline']['cores']} threads")
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if extras:
+        out["workloads"] = extras
     print(json.dumps(out), flush=True)
     return 0
 

@@ -33,6 +33,8 @@ struct GemmArgs {
   uint16_t* h;
   uint16_t* hs;
   float* y_rows;
+  float* dbg_g;  // check export of the gate/up kernel: fp32 g and u, [P][I] then [T][Is]
+  float* dbg_u;
 };
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
@@ -159,7 +161,7 @@ __device__ __forceinline__ void step_barrier() {
 // scale/bias ring, sized so that every layout fits the same LDS: 2 for MT = 2 (one step ahead),
 // 3 for MT = 1 with an odd group count (two steps ahead), 4 for MT = 1 with whole steps (a pair
 // of steps ahead, one barrier per pair).
-template <int MT, int AS, bool GU, bool PAIRED, int R>
+template <int MT, int AS, bool GU, bool PAIRED, int R, bool DBG>
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
   static_assert(AS == 2 || AS == 3 || (AS == 4 && MT == 1 && PAIRED), "A and scale ring depth");
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
@@ -392,7 +394,21 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 
   auto finish = [&](int j) __attribute__((always_inline)) {
     const int n0 = (nb0 + j) * cols;
-    if (GU) {
+    if (GU && DBG) {
+      // the accumulators themselves (natural column order), before the activation
+      const size_t base = sh ? (size_t)a.P * a.I + (size_t)(row0 - a.P) * Ie : (size_t)row0 * Ie;
+      const int col = n0 + 16 * wave + n;
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mm + 4 * kb + r;
+          if (row < rows) {
+            a.dbg_g[base + (size_t)row * Ie + col] = acc[0][mm][r];
+            a.dbg_u[base + (size_t)row * Ie + col] = acc[1][mm][r];
+          }
+        }
+    } else if (GU) {
       uint16_t* hout = sh ? a.hs + (size_t)(row0 - a.P) * Ie : a.h + (size_t)row0 * Ie;
       // h is stored in pair order, so that the down GEMM reads it as its A operand unchanged
       const int col = pair_pos(n0 + 16 * wave + n);
@@ -529,7 +545,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool GU, bool PAIRED, int R>
+template <bool GU, bool PAIRED, int R, bool DBG = false>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   constexpr int kSbBytes = PAIRED ? 1024 : 2048;
   // One LDS buffer, carved per tile height: two code pair stages, then four 16-row A stages and
@@ -549,14 +565,15 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    run_body<1, PAIRED ? 4 : 3, GU, PAIRED, R>(a, run, e, row0, rows, lds);
+    run_body<1, PAIRED ? 4 : 3, GU, PAIRED, R, DBG>(a, run, e, row0, rows, lds);
   else
-    run_body<2, 2, GU, PAIRED, R>(a, run, e, row0, rows, lds);
+    run_body<2, 2, GU, PAIRED, R, DBG>(a, run, e, row0, rows, lds);
 }
 
-template <bool PAIRED>
+// DBG: the check export (fp32 pre-activations instead of h)
+template <bool PAIRED, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_gemm(GemmArgs a) {
-  gemm_block<true, PAIRED, kRunGu>(a);
+  gemm_block<true, PAIRED, kRunGu, DBG>(a);
 }
 
 template <bool PAIRED, int R>
@@ -584,6 +601,8 @@ static GemmArgs gemm_args(const Ctx& c, int nruns) {
   a.h = c.h;
   a.hs = c.hs;
   a.y_rows = c.y_rows;
+  a.dbg_g = c.dbg_g;
+  a.dbg_u = c.dbg_u;
   return a;
 }
 
@@ -597,10 +616,15 @@ hipError_t launch_gateup_gemm(const Ctx& c) {
   const int ncb = (max(c.I, c.Is) + kGuCols - 1) / kGuCols;
   const int nruns = (ncb + kRunGu - 1) / kRunGu;
   const dim3 grid(grid_blocks(c.max_tiles, nruns));
-  if (c.d % kBK == 0)
-    hipLaunchKernelGGL(k_gateup_gemm<true>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  const bool dbg = c.dbg_g != nullptr;
+  if (c.d % kBK == 0 && !dbg)
+    hipLaunchKernelGGL((k_gateup_gemm<true, false>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  else if (!dbg)
+    hipLaunchKernelGGL((k_gateup_gemm<false, false>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  else if (c.d % kBK == 0)
+    hipLaunchKernelGGL((k_gateup_gemm<true, true>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
   else
-    hipLaunchKernelGGL(k_gateup_gemm<false>, grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+    hipLaunchKernelGGL((k_gateup_gemm<false, true>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
   return hipGetLastError();
 }
 

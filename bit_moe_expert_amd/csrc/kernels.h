@@ -27,6 +27,8 @@ struct Ctx {
   uint16_t* hs;           // [T][Is] bf16
   float* y_rows;          // [P + T][d] fp32, grouped order, shared rows last
   uint16_t* y;            // [T][d] bf16
+  float* dbg_g;           // when set, the gate/up GEMM writes fp32 g and u ([P][I] then [T][Is]) instead of h
+  float* dbg_u;
   hipStream_t stream;
 };
 
@@ -37,6 +39,8 @@ hipError_t launch_router_prefill(const Ctx& c);  // logits [T][E]
 hipError_t launch_topk_prefill(const Ctx& c);    // logits -> topk_ids, topk_w
 hipError_t launch_route_meta(const Ctx& c);  // + xp from x in extra blocks when c.pair_in_meta
 hipError_t launch_pair_x(const Ctx& c);      // xp from x
+// any bf16 rows (a whole number of 8-input chunks each) in pair order: dst from src, nchunks chunks
+hipError_t launch_pair_rows(const uint16_t* src, uint16_t* dst, int64_t nchunks, hipStream_t stream);
 // fused_topk: take the top-k from the router partials in every block, plus the shared expert's
 // rows in blocks of their own when its weights are set; otherwise read topk_ids and compute the
 // shared slot after each token's routed slots

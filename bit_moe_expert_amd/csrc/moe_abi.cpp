@@ -242,6 +242,8 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.w_router = nullptr;
   c.logit_bias = nullptr;
   c.y = nullptr;
+  c.dbg_g = nullptr;
+  c.dbg_u = nullptr;
   memset(&c.routed, 0, sizeof(c.routed));
   memset(&c.shared, 0, sizeof(c.shared));
 }
@@ -406,6 +408,37 @@ int moe_debug_dequant_bits(const moe_q4* w, int64_t rows, int32_t in_dim, int32_
 
 int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* out_bf16, void* stream) {
   return moe_debug_dequant_bits(w, rows, in_dim, 4, out_bf16, stream);
+}
+
+int moe_debug_grouped_gemm(const moe_dims* dims, int32_t T, int32_t which, const uint16_t* a,
+                           const moe_routing* routing, const moe_ffn_q4* routed, const moe_ffn_q4* shared, float* out,
+                           float* out2, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_dims(dims, T)) return rc;
+  if (which != 0 && which != 1) return fail(MOE_EINVAL, "which = %d must be 0 (gate/up) or 1 (down)", which);
+  if (T == 0) return MOE_OK;
+  if (bits_of(*dims) != 4) return fail(MOE_EUNSUPPORTED, "the grouped GEMM takes 4-bit codes");
+  if (int rc = check_routing(routing)) return rc;
+  // x (which = 0) or h (which = 1) stands in for x in the argument checks
+  if (int rc = check_layer_args(dims, T, a, nullptr, false, routed, shared, reinterpret_cast<const uint16_t*>(out),
+                                ws, ws_bytes))
+    return rc;
+  if (!out || !aligned(out, 16) || (which == 0 && (!out2 || !aligned(out2, 16))))
+    return fail(MOE_EINVAL, "output NULL or not 16-byte aligned");
+  Ctx c;
+  layer_ctx(c, dims, T, a, nullptr, nullptr, routed, shared, nullptr, ws, stream);
+  c.r = *routing;
+  hipError_t e;
+  if (which == 0) {
+    c.dbg_g = out;
+    c.dbg_u = out2;
+    if (int rc = run_stage(kPairX, c)) return rc;
+    return run_stage(kGemmGateup, c);
+  }
+  e = launch_pair_rows(a, c.h, (int64_t)c.P * c.I / 8, c.stream);
+  if (e == hipSuccess) e = launch_pair_rows(a + (size_t)c.P * c.I, c.hs, (int64_t)c.T * c.Is / 8, c.stream);
+  if (e != hipSuccess) return fail(MOE_EHIP, "launch of pair_rows failed: %s", hipGetErrorString(e));
+  c.y_rows = out;
+  return run_stage(kGemmDown, c);
 }
 
 size_t moe_vocab_topk_workspace_bytes(int32_t R, int32_t V, int32_t K) {

@@ -226,12 +226,14 @@ static int pair_blocks(int64_t nchunks, int threads) {
   return (int)std::min<int64_t>(kPairBlocks, (nchunks + threads - 1) / threads);
 }
 
-hipError_t launch_pair_x(const Ctx& c) {
-  const int64_t nchunks = (int64_t)c.T * c.d / 8;
-  hipLaunchKernelGGL(k_pair_x, dim3(pair_blocks(nchunks, 256)), dim3(256), 0, c.stream,
-                     reinterpret_cast<const uint4*>(c.x), reinterpret_cast<uint4*>(c.xp), nchunks);
+hipError_t launch_pair_rows(const uint16_t* src, uint16_t* dst, int64_t nchunks, hipStream_t stream) {
+  if (nchunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pair_x, dim3(pair_blocks(nchunks, 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), nchunks);
   return hipGetLastError();
 }
+
+hipError_t launch_pair_x(const Ctx& c) { return launch_pair_rows(c.x, c.xp, (int64_t)c.T * c.d / 8, c.stream); }
 
 // Blocks 1 .. gridDim.x - 1, when present, pair x instead (they need nothing from block 0).
 __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared,

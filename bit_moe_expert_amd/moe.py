@@ -66,6 +66,7 @@ def lib():
         L.moe_forward_layer.argtypes = [P(Dims), i32, vp, vp, vp, P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
         L.moe_debug_dequant.argtypes = [P(Q4), i64, i32, vp, vp]
         L.moe_debug_dequant_bits.argtypes = [P(Q4), i64, i32, i32, vp, vp]
+        L.moe_debug_grouped_gemm.argtypes = [P(Dims), i32, i32, vp, P(Routing), P(FFNQ4), P(FFNQ4), vp, vp, vp, sz, vp]
         L.moe_num_stages.argtypes = [P(Dims), i32]
         L.moe_num_stages.restype = i32
         L.moe_stage_name.argtypes = [P(Dims), i32, i32]
@@ -79,8 +80,9 @@ def lib():
         L.moe_vocab_topk_workspace_bytes.restype = sz
         L.moe_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_vocab_topk_stage.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
-        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_debug_dequant", "moe_debug_dequant_bits",
-                  "moe_launch_stage",
+        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer",
+                  "moe_debug_dequant", "moe_debug_dequant_bits",
+                  "moe_launch_stage", "moe_debug_grouped_gemm",
                   "moe_vocab_topk", "moe_vocab_topk_stage"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -250,14 +252,16 @@ class Layer:
         self._rf = routed.struct(self.dev)
         self._sf = shared.struct(self.dev) if shared is not None else None
 
-    def args(self, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor):
+    def _io(self, x: torch.Tensor, y: torch.Tensor):
         T = x.shape[0]
-        if x.shape[1] != self.dims.d_model or y.shape != x.shape:
+        if x.dim() != 2 or x.shape[1] != self.dims.d_model or y.shape != x.shape:
             raise ValueError("x / y shape mismatch")
         return (ctypes.byref(self.dims), T, _ptr(x, torch.bfloat16, "x", self.dev), self._wr, self._bias,
                 ctypes.byref(self._rf), ctypes.byref(self._sf) if self._sf is not None else None,
-                _ptr(y, torch.bfloat16, "y", self.dev), _ptr(ws, torch.uint8, "ws", self.dev), ws.numel(),
-                _stream(self.dev))
+                _ptr(y, torch.bfloat16, "y", self.dev))
+
+    def args(self, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor):
+        return self._io(x, y) + (_ptr(ws, torch.uint8, "ws", self.dev), ws.numel(), _stream(self.dev))
 
     def workspace(self, T: int) -> torch.Tensor:
         return new_workspace(self.dims, T, self.dev)
@@ -286,7 +290,8 @@ def forward_layer(x: torch.Tensor, w_router: torch.Tensor, routed: QuantFFN, sha
 
 
 def debug_dequant(p: QProj) -> torch.Tensor:
-    """moe_debug_dequant: bf16 expansion of a projection, with the grouped GEMM's own routine."""
+    """moe_debug_dequant_bits: bf16 expansion of a projection, with the GEMV kernels' unpacking of the
+    codes (seg_pairs). The grouped GEMM's own unpacking is checked through debug_grouped_gemm."""
     codes = p.codes
     in_dim = codes.shape[-1] * 8 // p.bits
     rows = codes.numel() // codes.shape[-1]
@@ -297,6 +302,40 @@ def debug_dequant(p: QProj) -> torch.Tensor:
                                       _stream(dev))
     _check(rc, "moe_debug_dequant")
     return out
+
+
+def debug_grouped_gemm(which: int, a: torch.Tensor, routing: Dict[str, torch.Tensor], routed: QuantFFN,
+                       shared: Optional[QuantFFN], ws: Optional[torch.Tensor] = None):
+    """moe_debug_grouped_gemm: one grouped-GEMM kernel alone, fp32 results before the activation.
+    which = 0: a = x [T][d]; returns (g, u), each [T*k*I + T*Is] fp32 (grouped rows, shared last).
+    which = 1: a = h [T*k*I + T*Is] bf16 (same layout); returns y rows [T*k (+ T)][d] fp32."""
+    k = routing["topk_ids"].shape[1]
+    T = routing["topk_ids"].shape[0]
+    dev = a.device
+    d = routed.d_model
+    dims = make_dims(d, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff, _bits_of(routed, shared))
+    P, I, Is = T * k, dims.d_ff, dims.d_ff_shared
+    if which == 0:
+        if tuple(a.shape) != (T, d):
+            raise ValueError("x must be [T][d]")
+        out = torch.empty(P * I + T * Is, dtype=torch.float32, device=dev)
+        out2 = torch.empty_like(out)
+    else:
+        if a.numel() != P * I + T * Is:
+            raise ValueError("h must hold T*k*d_ff + T*d_ff_shared values")
+        out = torch.empty((P + (T if Is else 0), d), dtype=torch.float32, device=dev)
+        out2 = None
+    ws = new_workspace(dims, T, dev) if ws is None else ws
+    rs = _routing_struct(routing, dev)
+    rf = routed.struct(dev)
+    sf = shared.struct(dev) if shared is not None else None
+    rc = lib().moe_debug_grouped_gemm(ctypes.byref(dims), T, which, _ptr(a, torch.bfloat16, "a", dev), ctypes.byref(rs),
+                                      ctypes.byref(rf), ctypes.byref(sf) if sf is not None else None,
+                                      _ptr(out, torch.float32, "out", dev),
+                                      _ptr(out2, torch.float32, "out2", dev) if out2 is not None else None,
+                                      _ptr(ws, torch.uint8, "ws", dev), ws.numel(), _stream(dev))
+    _check(rc, "moe_debug_grouped_gemm")
+    return (out, out2) if which == 0 else out
 
 
 def vocab_topk_workspace_bytes(R: int, V: int, K: int) -> int:

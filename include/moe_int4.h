@@ -178,6 +178,22 @@ int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* o
 int moe_debug_dequant_bits(const moe_q4* w, int64_t rows, int32_t in_dim, int32_t bits, uint16_t* out_bf16,
                            void* stream);
 
+/* Check export of the grouped GEMMs (test use): runs one of the two grouped-GEMM kernels over the
+ * block map of `routing` (as written by moe_route for these dims and T), with the same unpacking of
+ * the codes, LDS stages and scale/bias slots as moe_expert_ffn's grouped path, and writes its fp32
+ * results before any activation or rounding (4-bit codes only):
+ *   which = 0: a = x [T][d] bf16; out = g, out2 = u, each [T*k][d_ff] fp32 in grouped row order
+ *              followed by [T][d_ff_shared] for the shared expert: g = x Wg^T, u = x Wu^T.
+ *   which = 1: a = h, [T*k][d_ff] bf16 in grouped row order followed by [T][d_ff_shared];
+ *              out = [T*k + T][d] fp32 rows h Wd^T (shared rows last; [T*k][d] without a shared
+ *              expert); out2 unused (may be NULL).
+ * The products are those of the expert FFN in "Perplexity's Lily Beats MLX-LM on MacBook M5. Because
+ * It Only Runs One Model.", section "Prefill: keep routing on the GPU, dequantize in flight". `ws`
+ * as sized by moe_workspace_bytes; same validation and status codes as moe_expert_ffn. */
+int moe_debug_grouped_gemm(const moe_dims* dims, int32_t T, int32_t which, const uint16_t* a,
+                           const moe_routing* routing, const moe_ffn_q4* routed, const moe_ffn_q4* shared, float* out,
+                           float* out2, void* ws, size_t ws_bytes, void* stream);
+
 /* Profiling: moe_forward_layer runs moe_num_stages() kernels in sequence for this T; stage s
  * is named moe_stage_name(). moe_launch_stage enqueues stage s alone (same arguments as
  * moe_forward_layer); its inputs are what the earlier stages left in `ws`, so run

@@ -289,6 +289,94 @@ static void orc_ffn_row(int32_t d, int32_t I, const uint16_t* x_row, const doubl
   }
 }
 
+/* ---------------------------------------------------------------- 5a. the two grouped products alone
+ * The two products of step 5 over the grouped rows, before the activation and before any rounding
+ * of their results, so that a grouped GEMM can be checked stage by stage:
+ *   gate/up: g[r][i] = sum_c x[tok(r)][c] * Wg_e(r)[i][c] and u[r][i] likewise with Wu, in double,
+ *            c ascending; grouped row r < P = T*k belongs to the routed expert e(r) whose group
+ *            [offsets[e], offsets[e+1]) holds it and to token tok(r) = sorted_token[r]; rows
+ *            P .. P+T-1 are the shared expert's, token r - P. Outputs [P][I] then [T][Is].
+ *   down:    y[r][o] = sum_i h[r][i] * Wd_e(r)[o][i], in double, i ascending, for given bf16 h
+ *            laid out [P][I] then [T][Is]; output [P + T][d] (shared rows only when Is > 0).
+ * The weights are the bf16 dequantised values of step 4. */
+static int orc_offsets_ok(int32_t E, int64_t P, const int32_t* offsets) {
+  if (offsets[0] != 0 || offsets[E] != P) return 0;
+  for (int32_t e = 0; e < E; ++e)
+    if (offsets[e + 1] < offsets[e]) return 0;
+  return 1;
+}
+
+int oracle_gateup_preact(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, int32_t Is, const uint16_t* x,
+                         const orc_ffn* routed, const orc_ffn* shared, const int32_t* offsets,
+                         const int32_t* sorted_token, double* g, double* u) {
+  if (d % ORC_GROUP || I % ORC_GROUP || Is % ORC_GROUP || k < 1 || k > E) return 1;
+  if ((Is > 0) != (shared != NULL)) return 1;
+  const int64_t P = (int64_t)T * k;
+  if (!orc_offsets_ok(E, P, offsets)) return 1;
+  const int32_t Imax = I > Is ? I : Is;
+  double* Wg = (double*)malloc(sizeof(double) * (size_t)Imax * d);
+  double* Wu = (double*)malloc(sizeof(double) * (size_t)Imax * d);
+  for (int32_t e = 0; e <= E; ++e) {
+    const int sh = (e == E);
+    if (sh && Is == 0) break;
+    const int64_t r0 = sh ? P : offsets[e], r1 = sh ? P + T : offsets[e + 1];
+    if (r0 == r1) continue;
+    const int32_t Ie = sh ? Is : I;
+    orc_dequant_matrix(sh ? &shared->gate : &routed->gate, sh ? 0 : e, Ie, d, Wg);
+    orc_dequant_matrix(sh ? &shared->up : &routed->up, sh ? 0 : e, Ie, d, Wu);
+    double* go = sh ? g + P * I : g;
+    double* uo = sh ? u + P * I : u;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t t = sh ? r - P : sorted_token[r];
+      const int64_t orow = sh ? r - P : r;
+      for (int32_t i = 0; i < Ie; ++i) {
+        double gs = 0.0, us = 0.0;
+        for (int32_t c = 0; c < d; ++c) {
+          const double xc = orc_bf16_value(x[t * d + c]);
+          gs += xc * Wg[(int64_t)i * d + c];
+          us += xc * Wu[(int64_t)i * d + c];
+        }
+        go[orow * Ie + i] = gs;
+        uo[orow * Ie + i] = us;
+      }
+    }
+  }
+  free(Wg);
+  free(Wu);
+  return 0;
+}
+
+int oracle_down_rows(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, int32_t Is, const uint16_t* h,
+                     const orc_ffn* routed, const orc_ffn* shared, const int32_t* offsets, double* y) {
+  if (d % ORC_GROUP || I % ORC_GROUP || Is % ORC_GROUP || k < 1 || k > E) return 1;
+  if ((Is > 0) != (shared != NULL)) return 1;
+  const int64_t P = (int64_t)T * k;
+  if (!orc_offsets_ok(E, P, offsets)) return 1;
+  const int32_t Imax = I > Is ? I : Is;
+  double* Wd = (double*)malloc(sizeof(double) * (size_t)Imax * d);
+  for (int32_t e = 0; e <= E; ++e) {
+    const int sh = (e == E);
+    if (sh && Is == 0) break;
+    const int64_t r0 = sh ? P : offsets[e], r1 = sh ? P + T : offsets[e + 1];
+    if (r0 == r1) continue;
+    const int32_t Ie = sh ? Is : I;
+    orc_dequant_matrix(sh ? &shared->down : &routed->down, sh ? 0 : e, d, Ie, Wd);
+    const uint16_t* hb = sh ? h + P * I : h;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t hrow = sh ? r - P : r;
+      for (int32_t o = 0; o < d; ++o) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < Ie; ++i) acc += orc_bf16_value(hb[hrow * Ie + i]) * Wd[(int64_t)o * Ie + i];
+        y[r * d + o] = acc;
+      }
+    }
+  }
+  free(Wd);
+  return 0;
+}
+
 /* ---------------------------------------------------------------- 7. combine
  * y[t] = bf16(fp32(sum_j w[t][j] * y_pair(t,j) + y_shared(t))), j ascending, in double. */
 static uint16_t orc_combine_one(int32_t k, const float* w_t, const double* const* rows, const double* shared_row,

@@ -58,8 +58,13 @@ def lib():
         L.oracle_forward_tokens.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(_FFN),
                                             ctypes.POINTER(_FFN), i32, vp, vp, vp, vp]
         L.oracle_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.oracle_gateup_preact.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(_FFN),
+                                           ctypes.POINTER(_FFN), vp, vp, vp, vp]
+        L.oracle_down_rows.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(_FFN),
+                                       ctypes.POINTER(_FFN), vp, vp]
         for f in ("oracle_router_logits", "oracle_topk_softmax", "oracle_route_meta", "oracle_dequant",
-                  "oracle_forward_layer", "oracle_forward_tokens", "oracle_vocab_topk", "oracle_dequant_bits"):
+                  "oracle_forward_layer", "oracle_forward_tokens", "oracle_vocab_topk", "oracle_dequant_bits",
+                  "oracle_gateup_preact", "oracle_down_rows"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -230,6 +235,56 @@ def forward_tokens(x, w_router, routed: dict, shared: Optional[dict], k: int, se
     if rc:
         raise ValueError(f"oracle_forward_tokens rc={rc}")
     return {"y": y, "topk_ids": ids, "topk_w": w}
+
+
+def _dims_of(routed: dict, shared: Optional[dict], d: int):
+    E = routed["gate"]["codes"].shape[0]
+    I = routed["gate"]["codes"].shape[-2]
+    Is = 0 if shared is None else shared["gate"]["codes"].shape[-2]
+    return E, I, Is
+
+
+def gateup_preact(x, routed: dict, shared: Optional[dict], k: int, offsets, sorted_token):
+    """Gate and up products of every grouped row before the activation, in double:
+    (g, u), each [T*k][I] (grouped row order) and, with a shared expert, [T][Is] (g_s, u_s)."""
+    x = _c(x, np.uint16)
+    offsets = _c(offsets, np.int32)
+    sorted_token = _c(sorted_token, np.int32)
+    T, d = x.shape
+    E, I, Is = _dims_of(routed, shared, d)
+    P = T * k
+    r_ffn, keep_r = _ffn(routed)
+    s_ffn, keep_s = _ffn(shared)
+    g = np.empty(P * I + T * Is, np.float64)
+    u = np.empty(P * I + T * Is, np.float64)
+    rc = lib().oracle_gateup_preact(T, d, E, k, I, Is, _p(x), ctypes.byref(r_ffn),
+                                    ctypes.byref(s_ffn) if s_ffn is not None else None, _p(offsets),
+                                    _p(sorted_token), _p(g), _p(u))
+    del keep_r, keep_s
+    if rc:
+        raise ValueError(f"oracle_gateup_preact rc={rc}")
+    return (g[: P * I].reshape(P, I), u[: P * I].reshape(P, I), g[P * I:].reshape(T, Is), u[P * I:].reshape(T, Is))
+
+
+def down_rows(h, h_shared, routed: dict, shared: Optional[dict], k: int, offsets):
+    """Down products of given bf16 rows in double: h [T*k][I] (grouped order), h_shared [T][Is]
+    (or None) -> y [T*k + T][d] (shared rows last; [T*k][d] without a shared expert)."""
+    h = _c(h, np.uint16)
+    offsets = _c(offsets, np.int32)
+    P = h.shape[0]
+    T = P // k
+    d = routed["down"]["codes"].shape[-2]
+    E, I, Is = _dims_of(routed, shared, d)
+    hh = h.reshape(-1) if not Is else np.concatenate([h.reshape(-1), _c(h_shared, np.uint16).reshape(-1)])
+    r_ffn, keep_r = _ffn(routed)
+    s_ffn, keep_s = _ffn(shared)
+    y = np.empty((P + (T if Is else 0), d), np.float64)
+    rc = lib().oracle_down_rows(T, d, E, k, I, Is, _p(hh), ctypes.byref(r_ffn),
+                                ctypes.byref(s_ffn) if s_ffn is not None else None, _p(offsets), _p(y))
+    del keep_r, keep_s
+    if rc:
+        raise ValueError(f"oracle_down_rows rc={rc}")
+    return y
 
 
 def vocab_topk(logits, K: int):

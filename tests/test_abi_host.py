@@ -201,3 +201,25 @@ def test_code_bits_validation():
     q = moe.Q4(f() + 4, f(), f())
     assert L.moe_debug_dequant_bits(ctypes.byref(q), 4, 128, 5, f(), None) == moe.MOE_EUNSUPPORTED
     assert L.moe_debug_dequant_bits(ctypes.byref(q), 4, 128, 2, f(), None) == moe.MOE_EINVAL
+
+
+def test_debug_gemm_validation():
+    """The grouped-GEMM check export validates its arguments like moe_expert_ffn."""
+    f = _Fake()
+    d = _dims()
+    L = moe.lib()
+    rf = _ffn(f)
+    r = moe.Routing(*[f() for _ in range(8)])
+
+    def dg(which, **o):
+        return L.moe_debug_grouped_gemm(ctypes.byref(o.get("dims", d)), o.get("T", 16), which, o.get("a", f()),
+                                        ctypes.byref(r), ctypes.byref(rf), ctypes.byref(rf), o.get("out", f()),
+                                        o.get("out2", f()), f(), o.get("ws_bytes", 1 << 40), None)
+    assert dg(2) == moe.MOE_EINVAL
+    assert dg(0, T=0) == moe.MOE_OK
+    assert dg(0, out2=None) == moe.MOE_EINVAL
+    assert dg(0, a=f() + 2) == moe.MOE_EINVAL
+    assert dg(1, ws_bytes=100) == moe.MOE_EWORKSPACE
+    d3 = _dims()
+    d3.code_bits = 3
+    assert dg(0, dims=d3) == moe.MOE_EUNSUPPORTED

@@ -657,3 +657,95 @@ def test_vocab_topk_full_size_row_against_lexsort():
     for r in range(2):
         order = np.lexsort((np.arange(x.shape[1]), -x[r].astype(np.float64)))[:64]
         assert (ids[r] == order).all() and (vals[r] == x[r][order]).all()
+
+
+# ------------------------------------------------------------------ the two grouped products alone
+def _numpy_weights(p, mat):
+    """Independent dequantisation of an exact-arithmetic projection (numpy nibbles, float64):
+    w = s * q + b with the even input in the low nibble; exact in float64 and in bf16 here."""
+    c = p["codes"][mat].astype(np.int64)
+    q = np.empty((c.shape[0], 2 * c.shape[1]), np.int64)
+    q[:, 0::2] = c & 15
+    q[:, 1::2] = c >> 4
+    s = np.repeat(oracle.bf16_to_f32(p["scales"][mat]).astype(np.float64), 64, axis=1)
+    b = np.repeat(oracle.bf16_to_f32(p["biases"][mat]).astype(np.float64), 64, axis=1)
+    return s * q + b
+
+
+def _routing_of(L, k):
+    ids, _ = oracle.topk_softmax(oracle.router_logits(L["x"], L["w_router"], L["logit_bias"]), k)
+    return oracle.route_meta(ids, L["w_router"].shape[1], L["shared"] is not None)
+
+
+@pytest.mark.parametrize("T,d,E,k,I,Is", [(9, 192, 4, 2, 128, 64), (6, 128, 3, 3, 64, 0)])
+def test_gateup_preact_exact_against_numpy_matmul(T, d, E, k, I, Is):
+    """Exact-arithmetic inputs: the oracle's pre-activations equal a float64 matmul of numpy-made
+    weights row for row (token of each grouped row, expert of each group, gate vs up, shared last)."""
+    L = gen.exact_layer(T, d, E, k, I, Is, seed=T + d)
+    m = _routing_of(L, k)
+    g, u, gs, us = oracle.gateup_preact(L["x"], L["routed"], L["shared"], k, m["offsets"], m["sorted_token"])
+    xf = oracle.bf16_to_f32(L["x"]).astype(np.float64)
+    for e in range(E):
+        r0, r1 = m["offsets"][e], m["offsets"][e + 1]
+        xs = xf[m["sorted_token"][r0:r1]]
+        assert (g[r0:r1] == xs @ _numpy_weights(L["routed"]["gate"], e).T).all()
+        assert (u[r0:r1] == xs @ _numpy_weights(L["routed"]["up"], e).T).all()
+    if Is:
+        assert (gs == xf @ _numpy_weights(L["shared"]["gate"], 0).T).all()
+        assert (us == xf @ _numpy_weights(L["shared"]["up"], 0).T).all()
+    # every value is exactly representable in fp32 (the property the GPU comparison relies on)
+    for a in (g, u, gs, us):
+        assert (a.astype(np.float32).astype(np.float64) == a).all()
+
+
+def test_gateup_preact_gives_the_forward_layers_h():
+    """On random (inexact) inputs the pre-activations, through silu(g) * u rounded to bf16, give
+    the h of the whole-layer oracle, and they match a float64 matmul of the oracle's weights."""
+    rng = np.random.default_rng(44)
+    T, d, E, k, I, Is = 7, 128, 4, 2, 64, 128
+    x, wr, routed, shared = _random_layer(rng, T, d, E, k, I, Is)
+    out = oracle.forward_layer(x, wr, routed, shared, k, want_h=True)
+    g, u, gs, us = oracle.gateup_preact(x, routed, shared, k, out["offsets"], out["sorted_token"])
+    silu = lambda z: z / (1.0 + np.exp(-z))  # noqa: E731
+    assert (_bf16((silu(g) * u).astype(F32)) == out["h"]).all()
+    assert (_bf16((silu(gs) * us).astype(F32)) == out["h_shared"]).all()
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    for e in range(E):
+        r0, r1 = out["offsets"][e], out["offsets"][e + 1]
+        W = oracle.bf16_to_f32(oracle.dequant(routed["gate"]["codes"][e], routed["gate"]["scales"][e],
+                                              routed["gate"]["biases"][e])).astype(np.float64)
+        np.testing.assert_allclose(g[r0:r1], xf[out["sorted_token"][r0:r1]] @ W.T, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,d,E,k,I,Is", [(9, 192, 4, 2, 128, 64), (6, 128, 3, 3, 192, 0)])
+def test_down_rows_exact_against_numpy_matmul(T, d, E, k, I, Is):
+    L = gen.exact_layer(T, d, E, k, I, Is, seed=3 * T + d)
+    m = _routing_of(L, k)
+    P = T * k
+    h = gen.small_ints_bf16(gen.key(7, 0, 1), P * I).reshape(P, I)
+    hs = gen.small_ints_bf16(gen.key(7, 0, 2), T * Is).reshape(T, Is) if Is else None
+    y = oracle.down_rows(h, hs, L["routed"], L["shared"], k, m["offsets"])
+    assert y.shape == (P + (T if Is else 0), d)
+    hf = oracle.bf16_to_f32(h).astype(np.float64)
+    for e in range(E):
+        r0, r1 = m["offsets"][e], m["offsets"][e + 1]
+        assert (y[r0:r1] == hf[r0:r1] @ _numpy_weights(L["routed"]["down"], e).T).all()
+    if Is:
+        assert (y[P:] == oracle.bf16_to_f32(hs).astype(np.float64) @ _numpy_weights(L["shared"]["down"], 0).T).all()
+    assert (y.astype(np.float32).astype(np.float64) == y).all()
+
+
+def test_down_rows_combine_to_the_forward_layers_output():
+    """The whole-layer oracle's output is the combine of its own h through down_rows: y[t] =
+    bf16(sum_j w[t][j] * y_row(t, j) + y_shared(t)), j ascending."""
+    rng = np.random.default_rng(45)
+    T, d, E, k, I, Is = 6, 128, 4, 3, 64, 64
+    x, wr, routed, shared = _random_layer(rng, T, d, E, k, I, Is)
+    out = oracle.forward_layer(x, wr, routed, shared, k, want_h=True)
+    yr = oracle.down_rows(out["h"], out["h_shared"], routed, shared, k, out["offsets"])
+    P = T * k
+    acc = np.zeros((T, d), np.float64)
+    for j in range(k):
+        acc += out["topk_w"][:, j:j + 1].astype(np.float64) * yr[out["inv_pos"][:, j]]
+    acc += yr[P:]
+    assert (_bf16(acc.astype(F32)) == out["y"]).all()

@@ -36,6 +36,7 @@ T_SH_DOWN_CODES, T_SH_DOWN_SB = 12, 13
 T_PERM = 14
 T_X = 100  # + chunk index
 T_LOGITS = 1000  # + step index (logit rows of the top-K workload)
+T_EXACT = 2000  # + tensor offset: inputs whose products and sums are exact in fp32
 
 QUANT_SIGMA = 0.02
 GROUP = 64
@@ -284,4 +285,51 @@ def layer(w: Workload, layer_idx: int = 0) -> dict:
         "logit_bias": logit_bias(w),
         "routed": expert_weights(w, layer_idx),
         "shared": expert_weights(w, layer_idx, shared=True) if w.Is > 0 else None,
+    }
+
+
+# ------------------------------------------------------------------ exact-arithmetic inputs
+# Inputs on which every product and every partial sum of the expert FFN's two matrix products is
+# exactly representable in fp32, whatever the summation order: integer activations in [-4, 4]
+# (bf16), and per group a power-of-two scale 2^-m (m in 3..7) with a bias of -c * 2^-m (c in
+# 0..16). A weight s * q + b = (q - c) * 2^-m then has at most 5 significant bits (exact in
+# bf16), and a sum over d <= 4096 inputs stays below 2^24 units of 2^-7. Only bit patterns are
+# drawn here; the values follow from the bf16 format.
+def _f32_bits_to_bf16(v: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(v, np.float32).view(np.uint32)
+    assert not (b & 0xFFFF).any(), "value not exactly representable in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def small_ints_bf16(k: int, n: int, lo: int = -4, hi: int = 4, start: int = 0) -> np.ndarray:
+    """bf16 bits of integers drawn from [lo, hi] (byte of the stream modulo the range size)."""
+    r = rand_bytes(k, n, start).astype(np.int32) % (hi - lo + 1) + lo
+    return _f32_bits_to_bf16(r.astype(np.float32))
+
+
+def exact_proj(seed: int, layer: int, tensor: int, n_mat: int, out_dim: int, in_dim: int) -> dict:
+    n_sb = n_mat * out_dim * in_dim // GROUP
+    codes = rand_bytes(key(seed, layer, T_EXACT + 3 * tensor), n_mat * out_dim * in_dim // 2)
+    sb = rand_bytes(key(seed, layer, T_EXACT + 3 * tensor + 1), 2 * n_sb).reshape(n_sb, 2).astype(np.int32)
+    m = 3 + sb[:, 0] % 5
+    c = sb[:, 1] % 17
+    scale = np.ldexp(np.float32(1.0), -m).astype(np.float32)
+    return {"codes": codes.reshape(n_mat, out_dim, in_dim // 2),
+            "scales": _f32_bits_to_bf16(scale).reshape(n_mat, out_dim, in_dim // GROUP),
+            "biases": _f32_bits_to_bf16((-c * scale).astype(np.float32)).reshape(n_mat, out_dim, in_dim // GROUP)}
+
+
+def exact_layer(T: int, d: int, E: int, k: int, I: int, Is: int, seed: int = 0, layer: int = 0,
+                router_sigma: float = 0.02, zipf: bool = False) -> dict:
+    """A layer (as layer()) plus its activations "x", all with exact-arithmetic values; the router
+    is N(0, router_sigma^2) in fp32, with the skewed workload's logit bias when zipf is set."""
+    def ffn(base, n, Ie):
+        return {"gate": exact_proj(seed, layer, base, n, Ie, d), "up": exact_proj(seed, layer, base + 1, n, Ie, d),
+                "down": exact_proj(seed, layer, base + 2, n, d, Ie)}
+    return {
+        "x": small_ints_bf16(key(seed, layer, T_EXACT + 99), T * d).reshape(T, d),
+        "w_router": normal_f32(key(seed, layer, T_EXACT + 98), d * E, router_sigma).reshape(d, E),
+        "logit_bias": zipf_bias(E, 1.5) if zipf else None,
+        "routed": ffn(0, E, I),
+        "shared": ffn(3, 1, Is) if Is > 0 else None,
     }
