@@ -59,6 +59,11 @@ hipError_t launch_vocab_topk(int R, int V, int K, const float* logits, uint32_t*
                              hipStream_t stream, int stage);
 hipError_t launch_dequant(const moe_q4& w, int64_t rows, int in_dim, int bits, uint16_t* out, hipStream_t stream);
 
+// The fixed device scratch of moe_forward_layer_noalloc (noalloc.hip): its size, and its address on
+// the current device (looked up once per device).
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+hipError_t scratch_device_ptr(void** out);
+
 // Block-map tile height (rows of one expert group per tile).
 constexpr int kTileRows = 32;
 

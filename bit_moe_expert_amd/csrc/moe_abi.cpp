@@ -363,6 +363,25 @@ int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const 
   return MOE_OK;
 }
 
+int moe_forward_layer_noalloc(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+                              const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y,
+                              void* stream) {
+  if (int rc = check_dims(dims, T)) return rc;
+  if (T == 0) return MOE_OK;
+  const size_t need = layout_of(*dims, T).total;
+  if (need > kScratchBytes)
+    return fail(MOE_EWORKSPACE, "T = %d needs %zu bytes of workspace; the fixed scratch holds %zu", T, need,
+                kScratchBytes);
+  // every other argument is checked against a stand-in workspace address (never dereferenced)
+  void* fake_ws = reinterpret_cast<void*>((uintptr_t)256);
+  if (int rc = check_layer_args(dims, T, x, w_router, true, routed, shared, y, fake_ws, need)) return rc;
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(MOE_EINVAL, "logit_bias not 4-byte aligned");
+  void* ws = nullptr;
+  const hipError_t e = scratch_device_ptr(&ws);
+  if (e != hipSuccess) return fail(MOE_EHIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+  return moe_forward_layer(dims, T, x, w_router, logit_bias, routed, shared, y, ws, kScratchBytes, stream);
+}
+
 int32_t moe_num_stages(const moe_dims* dims, int32_t T) {
   if (check_dims(dims, T) || T == 0) return 0;
   Stage st[8];

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_int4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES: the fixed scratch of moe_forward_layer_noalloc
 
 
 class MoeError(RuntimeError):
@@ -64,6 +65,7 @@ def lib():
         L.moe_route.argtypes = [P(Dims), i32, vp, vp, vp, P(Routing), vp, sz, vp]
         L.moe_expert_ffn.argtypes = [P(Dims), i32, vp, P(Routing), P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
         L.moe_forward_layer.argtypes = [P(Dims), i32, vp, vp, vp, P(FFNQ4), P(FFNQ4), vp, vp, sz, vp]
+        L.moe_forward_layer_noalloc.argtypes = [P(Dims), i32, vp, vp, vp, P(FFNQ4), P(FFNQ4), vp, vp]
         L.moe_debug_dequant.argtypes = [P(Q4), i64, i32, vp, vp]
         L.moe_debug_dequant_bits.argtypes = [P(Q4), i64, i32, i32, vp, vp]
         L.moe_debug_grouped_gemm.argtypes = [P(Dims), i32, i32, vp, P(Routing), P(FFNQ4), P(FFNQ4), vp, vp, vp, sz, vp]
@@ -80,7 +82,7 @@ def lib():
         L.moe_vocab_topk_workspace_bytes.restype = sz
         L.moe_vocab_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_vocab_topk_stage.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
-        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer",
+        for f in ("moe_route", "moe_expert_ffn", "moe_forward_layer", "moe_forward_layer_noalloc",
                   "moe_debug_dequant", "moe_debug_dequant_bits",
                   "moe_launch_stage", "moe_debug_grouped_gemm",
                   "moe_vocab_topk", "moe_vocab_topk_stage"):
@@ -271,6 +273,12 @@ class Layer:
         ws = self.workspace(T) if ws is None else ws
         y = torch.empty_like(x) if y is None else y
         _check(lib().moe_forward_layer(*self.args(x, y, ws)), "moe_forward_layer")
+        return y
+
+    def forward_noalloc(self, x: torch.Tensor, y: Optional[torch.Tensor] = None):
+        """moe_forward_layer_noalloc: the layer with the library's fixed device scratch as workspace."""
+        y = torch.empty_like(x) if y is None else y
+        _check(lib().moe_forward_layer_noalloc(*self._io(x, y), _stream(self.dev)), "moe_forward_layer_noalloc")
         return y
 
     def stages(self, T: int):

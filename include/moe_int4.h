@@ -163,6 +163,19 @@ int moe_expert_ffn(const moe_dims* dims, int32_t T, const uint16_t* x, const moe
                    const moe_ffn_q4* routed, const moe_ffn_q4* shared, uint16_t* y, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): moe_forward_layer with the workspace taken from a fixed device
+ * array inside the library instead of `ws`. The array holds MOE_NOALLOC_SCRATCH_BYTES bytes on each
+ * GPU the library runs on (the current device at the call) and lives until the process ends; calls
+ * whose moe_workspace_bytes(dims, T) exceeds it return MOE_EWORKSPACE. The first call on a device
+ * looks the array's address up (hipGetSymbolAddress); no call allocates or frees memory. All calls
+ * on one GPU share the array: calls that may overlap on one GPU (unordered streams) race on it and
+ * must be ordered by the caller. Otherwise as moe_forward_layer. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_layer_noalloc(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+                              const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared,
+                              uint16_t* y, void* stream);
+
 /* moe_route followed by moe_expert_ffn, with the routing arrays carved from `ws`. On the GEMV
  * path the block-map steps are skipped (it does not read them), the top-k is taken inside the
  * gate/up kernel, and only topk_ids/topk_w of the carved routing are written. */

@@ -203,12 +203,33 @@ def test_code_bits_validation():
     assert L.moe_debug_dequant_bits(ctypes.byref(q), 4, 128, 2, f(), None) == moe.MOE_EINVAL
 
 
-def test_debug_gemm_validation():
-    """The grouped-GEMM check export validates its arguments like moe_expert_ffn."""
+def test_noalloc_and_debug_gemm_validation():
+    """moe_forward_layer_noalloc refuses calls whose workspace exceeds the fixed scratch (before any
+    HIP call), validates the other arguments like moe_forward_layer; the grouped-GEMM check export
+    validates its arguments the same way."""
     f = _Fake()
     d = _dims()
     L = moe.lib()
+    hdr = open(HEADER).read()
+    assert re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", hdr)
+    assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20
+    T = 1
+    while L.moe_workspace_bytes(ctypes.byref(d), T) <= moe.NOALLOC_SCRATCH_BYTES:
+        T += 64
     rf = _ffn(f)
+
+    def na(dims, T, **o):
+        return L.moe_forward_layer_noalloc(ctypes.byref(dims), T, o.get("x", f()), o.get("wr", f()), None,
+                                           ctypes.byref(rf), ctypes.byref(o.get("sh", rf)) if o.get("sh", rf) else None,
+                                           o.get("y", f()), None)
+    assert na(d, T) == moe.MOE_EWORKSPACE
+    assert "fixed scratch" in L.moe_last_error().decode()
+    assert na(d, 0) == moe.MOE_OK
+    assert na(d, -3) == moe.MOE_EINVAL
+    assert na(d, 8, x=None) == moe.MOE_EINVAL
+    assert na(d, 8, y=f() + 2) == moe.MOE_EINVAL
+    assert na(d, 8, sh=None) == moe.MOE_EINVAL
+    assert na(_dims(g=32), 8) == moe.MOE_EUNSUPPORTED
     r = moe.Routing(*[f() for _ in range(8)])
 
     def dg(which, **o):
