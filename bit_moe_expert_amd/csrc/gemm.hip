@@ -33,6 +33,9 @@ struct GemmArgs {
   uint16_t* h;
   uint16_t* hs;
   float* y_rows;
+  const float* xsum;  // [T][d/64] group sums of x (the bias term's factor on the gate/up side)
+  float* hsum;        // [P][I/64] group sums of h (written by the gate/up epilogue, read by down)
+  float* hsum_sh;     // [T][Is/64] the same for the shared expert's h
   float* dbg_g;  // check export of the gate/up kernel: fp32 g and u, [P][I] then [T][Is]
   float* dbg_u;
 };
@@ -68,10 +71,18 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 // The matrix cores take the 4-bit codes themselves. Over one 64-input group with scale s and bias b,
 //   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * X_g,   X_g = sum_k x_k,
 // and "128 + q" is an exact bf16 made from the code bits with one and-or per pair. So each group
-// runs its two MFMA K-steps into a fresh accumulator, then two FMAs fold the group's scale and
-// bias into the running sum; X_g comes from one more MFMA of the same A rows against ones. The
-// weight enters as s * q + b evaluated in fp32 without rounding the weight itself to bf16 first
-// (a difference of at most half a bf16 ulp per weight).
+// runs its two MFMA K-steps into a fresh accumulator and one FMA folds the group's scale into the
+// running sum; the K loop needs the scales only. The bias terms of all groups form one small
+// product per job, sum_g X[row][g] C[g][col] with C = b - 128 s, which the block runs on the matrix
+// cores before its K loop: its operands (X from group sums computed once per row, for x by the pass
+// that pairs it and for h by the gate/up epilogue; the scales and biases of the job's columns) are
+// register loads issued ahead of the pipeline's first loads, so their latency hides under the
+// pipeline's start. X and C are each split into a high and a low bf16 part (X_hi C_hi + X_hi C_lo +
+// X_lo C_hi, 32 groups per v_mfma_f32_16x16x32_bf16): the dropped X_lo C_lo and the split leave a
+// relative error near 2^-16 of the bias term, and none when X and C are bf16 values, as on
+// exact-arithmetic inputs. The weight enters
+// as s * q + b without rounding the weight itself to bf16 first (a difference of at most half a
+// bf16 ulp per weight).
 //
 // Work item: one tile and a run of consecutive column blocks (gate/up: 64 h columns = 64 gate +
 // 64 up weight rows; down: 128 output columns). The block streams the run's column blocks
@@ -85,9 +96,9 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 //     next pair; each row's eight 16-byte chunks are XOR-swizzled by row so the MFMA-side 8-byte
 //     reads spread over the banks. A job's steps are padded to an even count: the padding step
 //     loads in-bounds stand-in data and multiplies nothing;
-//   - scales and biases, per step: with an even number of groups per row, one 4-byte load per
-//     weight row and array (the step's two groups); otherwise one 2-byte load per (row, group),
-//     each landing zero-extended in its own dword;
+//   - scales, per step: with an even number of groups per row, one 4-byte load per weight row
+//     (the step's two groups); otherwise one 2-byte load per (row, group), each landing
+//     zero-extended in its own dword;
 //   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes per step; the 16-byte chunks of
 //     a row are XOR-swizzled by row. A rows past the tile's rows repeat its last row and only
 //     reach accumulator rows that are never written out. Both x (paired once per call, before
@@ -97,7 +108,7 @@ __device__ __forceinline__ bool block_tile(const GemmArgs& a, int& run, int& e, 
 // A and the scales run in a ring of AS stages, AS - 1 steps ahead.
 // Addresses are a scalar base that advances per step plus a per-lane offset fixed for the run.
 // When K is an odd number of groups, the last step's second group reads in-bounds stand-in data
-// and is given scale and bias 0 when it is multiplied. Weight rows past the down matrix repeat
+// and is given scale 0 when it is multiplied. Weight rows past the down matrix repeat
 // its last row; their outputs are not written. Loads complete in issue order, so before each
 // barrier a wave waits until only the loads younger than the ones the step needs are
 // outstanding: its part of the stages the step reads has then landed.
@@ -158,20 +169,22 @@ __device__ __forceinline__ void step_barrier() {
 // otherwise down (A = h rows, 128 weight rows of the down matrix, fp32 y_rows epilogue).
 // PAIRED: K is a multiple of 128 (whole steps; scale/bias pairs load as one dword).
 // MT: 16-row subtiles of A (1 for tiles of at most 16 rows, else 2); AS: depth of the A and
-// scale/bias ring, sized so that every layout fits the same LDS: 2 for MT = 2 (one step ahead),
+// scale ring, sized so that every layout fits the same LDS: 2 for MT = 2 (one step ahead),
 // 3 for MT = 1 with an odd group count (two steps ahead), 4 for MT = 1 with whole steps (a pair
 // of steps ahead, one barrier per pair).
-template <int MT, int AS, bool GU, bool PAIRED, int R, bool DBG>
+template <int MT, int AS, bool GU, bool PAIRED, int R, bool DBG, bool VEC8>
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
   static_assert(AS == 2 || AS == 3 || (AS == 4 && MT == 1 && PAIRED), "A and scale ring depth");
-  constexpr int kSbBytes = PAIRED ? 1024 : 2048;
+  static_assert(!VEC8 || PAIRED, "a multiple of 8 groups is whole steps");
+  constexpr int kSbBytes = PAIRED ? 512 : 1024;
   constexpr int kAS = MT * kA16StageBytes;  // an A stage: 16 MT rows
-  // code pair stage st (0, 1), and stage st of the scales and biases and of A, in the block's LDS
+  // code pair stage st (0, 1), and stage st of the scales and of A, in the block's LDS
   const auto Lc = [lds](int st) { return lds + st * kPairCodeStageBytes; };
   const auto La = [lds](int st) { return lds + 2 * kPairCodeStageBytes + st * kAS; };
   const auto Lsb = [lds](int st) {
     return reinterpret_cast<uint32_t*>(lds + 2 * kPairCodeStageBytes + AS * kAS + st * kSbBytes);
   };
+
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool sh = (e == a.E);
   const int Ie = sh ? a.Is : a.I;
@@ -190,22 +203,18 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 
   // ---- weight matrices (for GU, waves 0, 1 load gate rows and waves 2, 3 up rows)
   const uint8_t* wc;
-  const uint16_t *ws, *wb;  // scale / bias arrays of this wave's direct loads
-  const uint16_t* sb_arr;
+  const uint16_t* sb_arr;  // the scales this wave's direct loads read
   if (GU) {
     const bool upw = wave >= 2;
     wc = sh ? (upw ? a.shared.up.codes : a.shared.gate.codes) : (upw ? a.routed.up.codes : a.routed.gate.codes);
-    // scale/bias loads: wave w loads array (w >> 1) for block rows 64 (w & 1) .. +63, which are
-    // gate rows for w & 1 == 0 and up rows for w & 1 == 1
+    // scale loads: wave w loads block rows 64 (w & 1) .. +63, which are gate rows for w & 1 == 0
+    // and up rows for w & 1 == 1 (waves 2, 3 repeat the loads of waves 0, 1 into the same slots)
     const bool ups = (wave & 1) != 0;
-    ws = sh ? (ups ? a.shared.up.scales : a.shared.gate.scales) : (ups ? a.routed.up.scales : a.routed.gate.scales);
-    wb = sh ? (ups ? a.shared.up.biases : a.shared.gate.biases) : (ups ? a.routed.up.biases : a.routed.gate.biases);
+    sb_arr = sh ? (ups ? a.shared.up.scales : a.shared.gate.scales) : (ups ? a.routed.up.scales : a.routed.gate.scales);
   } else {
     wc = sh ? a.shared.down.codes : a.routed.down.codes;
-    ws = sh ? a.shared.down.scales : a.routed.down.scales;
-    wb = sh ? a.shared.down.biases : a.routed.down.biases;
+    sb_arr = sh ? a.shared.down.scales : a.routed.down.scales;
   }
-  sb_arr = (wave >> 1) ? wb : ws;
   const size_t mrow = (size_t)mat * nrows_w;  // first row of this expert's matrix
 
   // ---- per-lane fixed offsets
@@ -218,7 +227,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     crow[t] = GU ? (r & (kGuCols - 1)) : r;  // row within the column block's weight rows
     cq16[t] = 16 * ((lane & 7) ^ code_swz8(r));
   }
-  // scale/bias: PAIRED: block row 64 (wave & 1) + lane; else (row, group) = (p >> 1, p & 1) for
+  // scales: PAIRED: block row 64 (wave & 1) + lane; else (row, group) = (p >> 1, p & 1) for
   // p = 64 (2 (wave & 1) + t) + lane
   int srow[2];
 #pragma unroll
@@ -258,8 +267,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const uint32_t lbase = lds_addr(lds);
   const uint32_t lds_c = lbase + wave * 4096;
   const uint32_t lds_a = lbase + 2 * kPairCodeStageBytes + wave * 1024;
-  const uint32_t lds_s = lbase + 2 * kPairCodeStageBytes + AS * kAS +
-                         (PAIRED ? 512 * (wave >> 1) + 256 * (wave & 1) : 1024 * (wave >> 1) + 512 * (wave & 1));
+  const uint32_t lds_s = lbase + 2 * kPairCodeStageBytes + AS * kAS + (PAIRED ? 256 : 512) * (wave & 1);
   const uint8_t* cjb;
   uint32_t coq[4];  // codes: row offset + swizzled chunk
   auto setup_codes = [&](int j) __attribute__((always_inline)) {
@@ -270,7 +278,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     for (int t = 0; t < 4; ++t) coq[t] = (uint32_t)min(crow[t], lim) * (uint32_t)ldc + cq16[t];
   };
   const uint16_t* sjb;
-  uint32_t so[2];  // scale/bias offsets in bytes
+  uint32_t so[2];  // scale offsets in bytes
   auto setup_sb = [&](int j) __attribute__((always_inline)) {
     const int n0 = (nb0 + j) * cols;
     const int lim = nrows_w - 1 - n0;
@@ -303,8 +311,8 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
       for (int t = 0; t < 4; ++t) dma16(cb, coq[t], dst + 1024 * t);
     }
   };
-  // issue the A and scale/bias loads of step s of the current job into stage st; the padding
-  // step (s == S) re-reads step S - 1
+  // issue the A and scale loads of step s of the current job into stage st; the padding step
+  // (s == S) re-reads step S - 1
   auto issue = [&](int s, int st) __attribute__((always_inline)) {
     s = min(s, S - 1);
     const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
@@ -340,7 +348,6 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   // step of A/scale stage st, codes from stage cst, second step of its pair when h
   auto compute = [&](int st, int cst, int h, bool half) __attribute__((always_inline)) {
@@ -351,7 +358,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     for (int gg = 0; gg < 2; ++gg) {
       const uint2 w0 = *reinterpret_cast<const uint2*>(cs + crd[0][2 * h + gg]);
       const uint2 w1 = *reinterpret_cast<const uint2*>(cs + crd[1][2 * h + gg]);
-      f32x4_t tmp[2][MT], xs[MT];
+      f32x4_t tmp[2][MT];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const uint32_t c0 = kk ? w0.y : w0.x, c1 = kk ? w1.y : w1.x;
@@ -364,34 +371,169 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
           const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
           tmp[0][mm] = mfma16x16x32(av, b0, kk == 0 ? z : tmp[0][mm]);
           tmp[1][mm] = mfma16x16x32(av, b1, kk == 0 ? z : tmp[1][mm]);
-          xs[mm] = mfma16x16x32(av, ones, kk == 0 ? z : xs[mm]);
         }
       }
-      float s0, b0v, s1, b1v;
+      float s0, s1;
       if (PAIRED) {
-        const uint32_t sc0 = sb[wrow0], bi0 = sb[128 + wrow0], sc1 = sb[wrow1], bi1 = sb[128 + wrow1];
+        const uint32_t sc0 = sb[wrow0], sc1 = sb[wrow1];
         s0 = gg ? bf16hi(sc0) : bf16lo(sc0);
-        b0v = gg ? bf16hi(bi0) : bf16lo(bi0);
         s1 = gg ? bf16hi(sc1) : bf16lo(sc1);
-        b1v = gg ? bf16hi(bi1) : bf16lo(bi1);
       } else {
         s0 = bf16lo(sb[2 * wrow0 + gg]);
-        b0v = bf16lo(sb[256 + 2 * wrow0 + gg]);
         s1 = bf16lo(sb[2 * wrow1 + gg]);
-        b1v = bf16lo(sb[256 + 2 * wrow1 + gg]);
-        if (gg == 1 && half) s0 = b0v = s1 = b1v = 0.0f;  // the group past K adds nothing
+        if (gg == 1 && half) s0 = s1 = 0.0f;  // the group past K adds nothing
       }
-      const float c0 = fmaf(-128.0f, s0, b0v), c1 = fmaf(-128.0f, s1, b1v);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          acc[0][mm][r] = fmaf(c0, xs[mm][r], fmaf(s0, tmp[0][mm][r], acc[0][mm][r]));
-          acc[1][mm][r] = fmaf(c1, xs[mm][r], fmaf(s1, tmp[1][mm][r], acc[1][mm][r]));
+          acc[0][mm][r] = fmaf(s0, tmp[0][mm][r], acc[0][mm][r]);
+          acc[1][mm][r] = fmaf(s1, tmp[1][mm][r], acc[1][mm][r]);
         }
     }
   };
 
+  // ---- bias terms: acc += X C for the job's columns, as split-bf16 products (see above). Lane
+  // (n, kb) holds groups 8 kb .. 8 kb + 7 (of a chunk of 32) of tile row 16 mm + n (X, A operand)
+  // and of the column n of each of its two subtiles (C, B operand).
+  const float* xs_row[MT];  // group sums of the tile rows of the lane's A fragments
+#pragma unroll
+  for (int mm = 0; mm < MT; ++mm) {
+    const int r = min(16 * mm + n, rows - 1);
+    if (GU) {
+      int tok = sh ? (row0 - a.P + r) : a.sorted_token[row0 + r];
+      tok = min(max(tok, 0), a.T - 1);
+      xs_row[mm] = a.xsum + (size_t)tok * (size_t)ldg;
+    } else {
+      xs_row[mm] = sh ? a.hsum_sh + (size_t)(row0 - a.P + r) * (size_t)ldg : a.hsum + (size_t)(row0 + r) * (size_t)ldg;
+    }
+  }
+  // scales and biases of the two column subtiles (gate/up: the gate and the up matrix)
+  const uint16_t* const bsc0 = GU ? (sh ? a.shared.gate.scales : a.routed.gate.scales)
+                                  : (sh ? a.shared.down.scales : a.routed.down.scales);
+  const uint16_t* const bbi0 = GU ? (sh ? a.shared.gate.biases : a.routed.gate.biases)
+                                  : (sh ? a.shared.down.biases : a.routed.down.biases);
+  const uint16_t* const bsc1 = GU ? (sh ? a.shared.up.scales : a.routed.up.scales) : bsc0;
+  const uint16_t* const bbi1 = GU ? (sh ? a.shared.up.biases : a.routed.up.biases) : bbi0;
+  // Groups gl .. gl + 7 (gl a multiple of 8) of a row of ldg values, those past the row 0, without
+  // branches (a branch would make the compiler drain the loads at its join): every load reads an
+  // in-bounds address, clamped to the row, and a select zeroes what lies past it. VEC8 (ldg a
+  // multiple of 8): the 8 values are one aligned 16-byte load (two for fp32); whole K steps (ldg
+  // even): 4-byte pairs; otherwise single values.
+  const auto load8 = [&](const uint16_t* rowp, int gl) __attribute__((always_inline)) -> uint4 {
+    if constexpr (VEC8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(rowp + min(gl, ldg - 8));
+      const bool in = gl < ldg;
+      return make_uint4(in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u);
+    }
+    uint32_t w[4];
+    if constexpr (PAIRED) {
+      const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rowp);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = gl + 2 * q;
+        const uint32_t v = r32[min(g, ldg - 2) >> 1];
+        w[q] = g < ldg ? v : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = gl + 2 * q;
+        const uint32_t lo = rowp[min(g, ldg - 1)], hi = rowp[min(g + 1, ldg - 1)];
+        w[q] = (g < ldg ? lo : 0u) | ((g + 1 < ldg ? hi : 0u) << 16);
+      }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  struct BiasOps {
+    float x[MT][8];      // group sums of the lane's rows
+    uint4 sc[2], bi[2];  // scales and biases of the lane's two columns (bf16)
+  };
+  const auto bias_load = [&](BiasOps& o, int j, int g0, bool want_x) __attribute__((always_inline)) {
+    const int gl = g0 + 8 * kb;
+    const int n0 = (nb0 + j) * cols;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int wr = t ? wrow1 : wrow0;
+      const int rm = GU ? (wr & (kGuCols - 1)) : wr;  // row within the column block of its matrix
+      const size_t row = mrow + (size_t)min(n0 + rm, nrows_w - 1);
+      o.sc[t] = load8((t ? bsc1 : bsc0) + row * (size_t)ldg, gl);
+      o.bi[t] = load8((t ? bbi1 : bbi0) + row * (size_t)ldg, gl);
+    }
+    if (want_x) {
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) {
+        if constexpr (VEC8) {
+          const float* xp8 = xs_row[mm] + min(gl, ldg - 8);
+          const float4 v0 = reinterpret_cast<const float4*>(xp8)[0], v1 = reinterpret_cast<const float4*>(xp8)[1];
+          const bool in = gl < ldg;
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o.x[mm][i] = in ? v[i] : 0.0f;
+        } else if constexpr (PAIRED) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int g = gl + 2 * q;
+            const float2 v = *reinterpret_cast<const float2*>(xs_row[mm] + min(g, ldg - 2));
+            o.x[mm][2 * q] = g < ldg ? v.x : 0.0f;
+            o.x[mm][2 * q + 1] = g < ldg ? v.y : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = xs_row[mm][min(gl + i, ldg - 1)];
+            o.x[mm][i] = gl + i < ldg ? v : 0.0f;
+          }
+        }
+      }
+    }
+  };
+  // X (this lane's rows) split once per chunk, then the products for the columns of `o` into dst
+  const auto bias_mfma = [&](const BiasOps& o, const BiasOps& xo, f32x4_t (&dst)[2][MT]) __attribute__((always_inline)) {
+    uint4 chi[2], clo[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t sv[4] = {o.sc[t].x, o.sc[t].y, o.sc[t].z, o.sc[t].w};
+      const uint32_t bv[4] = {o.bi[t].x, o.bi[t].y, o.bi[t].z, o.bi[t].w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float c0 = fmaf(-128.0f, bf16lo(sv[q]), bf16lo(bv[q]));
+        const float c1 = fmaf(-128.0f, bf16hi(sv[q]), bf16hi(bv[q]));
+        hi[q] = pack_bf16x2(c0, c1);
+        lo[q] = pack_bf16x2(c0 - bf16lo(hi[q]), c1 - bf16hi(hi[q]));
+      }
+      chi[t] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      clo[t] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      const float* v = xo.x[mm];
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hi[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+        lo[q] = pack_bf16x2(v[2 * q] - bf16lo(hi[q]), v[2 * q + 1] - bf16hi(hi[q]));
+      }
+      const uint4 xhi = make_uint4(hi[0], hi[1], hi[2], hi[3]), xlo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        dst[t][mm] = mfma16x16x32(xhi, chi[t], dst[t][mm]);
+        dst[t][mm] = mfma16x16x32(xhi, clo[t], dst[t][mm]);
+        dst[t][mm] = mfma16x16x32(xlo, chi[t], dst[t][mm]);
+      }
+    }
+  };
+
+  // gate/up: the sums of this wave's 16 h columns for each accumulator row of the lane (the same in
+  // all 16 lanes of a DPP row), combined across the 4 waves after the loop into hsum
+  float hpart[MT][4];
+  // with two jobs (down), the bias terms of the second one, added when it starts
+  f32x4_t bnext[2][MT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) bnext[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto finish = [&](int j) __attribute__((always_inline)) {
     const int n0 = (nb0 + j) * cols;
     if (GU && DBG) {
@@ -417,7 +559,15 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * mm + 4 * kb + r;
-          if (row < rows) hout[(size_t)row * Ie + col] = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
+          const uint16_t hb = f32_to_bf16(silu_mul(acc[0][mm][r], acc[1][mm][r]));
+          if (row < rows) hout[(size_t)row * Ie + col] = hb;
+          // the rounded value enters the down product, so it is what the group sum adds
+          float v = bf16_to_f32(hb);
+          v += dpp_f32<0xB1>(v);
+          v += dpp_f32<0x4E>(v);
+          v += dpp_f32<0x124>(v);
+          v += dpp_f32<0x128>(v);
+          hpart[mm][r] = v;
         }
     } else {
 #pragma unroll
@@ -436,7 +586,10 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) acc[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mm = 0; mm < MT; ++mm) {
+        acc[t][mm] = R > 1 ? bnext[t][mm] : f32x4_t{0.f, 0.f, 0.f, 0.f};  // the next job starts from its bias terms
+        if (R > 1) bnext[t][mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
   };
 
   // Positions run over (job, step) with each job's steps padded to an even count S2, so every
@@ -447,12 +600,17 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   // needs are one position's A/scales at an even position, and those plus one pair's codes at an
   // odd one; with AS = 2 they are nothing at an even position and one pair's codes at an odd one.
   // A stage is overwritten only after the barrier that follows its last read.
-  constexpr int kOpsA = (PAIRED ? 1 : 2) + MT;  // A and scale/bias loads one wave issues per position
+  constexpr int kOpsA = (PAIRED ? 1 : 2) + MT;  // A and scale loads one wave issues per position
   constexpr int kOpsC = 4;                      // code loads one wave issues per pair
   const int P2 = njobs * S2;
   int ij = 0, is = 0;    // position being issued (job, step); stays at the last position
   int icj = 0, ics = 0;  // code pair being issued (job, pair); stays at the last pair
   int cj = 0, cs = 0;    // position being computed
+  // the first chunk of bias operands goes out before the pipeline's first loads; the products run
+  // once those operands are in (the stage loads stay in flight meanwhile)
+  BiasOps bo0, bo1;
+  bias_load(bo0, 0, 0, true);
+  if (R > 1 && njobs > 1) bias_load(bo1, 1, 0, false);
   setup_codes(0);
   setup_sb(0);
   issue_codes(0, 0);
@@ -460,6 +618,18 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   if (AS >= 3) {
     is = 1;  // S2 >= 2
     issue(1, 1);
+  }
+  // keep the products (and the wait for their operands) after the pipeline's first loads
+  __builtin_amdgcn_sched_barrier(0);
+  bias_mfma(bo0, bo0, acc);
+  if (R > 1 && njobs > 1) bias_mfma(bo1, bo0, bnext);
+  for (int g0 = 32; g0 < ldg; g0 += 32) {  // more than 32 groups: the further chunks in turn
+    bias_load(bo0, 0, g0, true);
+    bias_mfma(bo0, bo0, acc);
+    if (R > 1 && njobs > 1) {
+      bias_load(bo1, 1, g0, false);
+      bias_mfma(bo1, bo0, bnext);
+    }
   }
   if constexpr (AS == 4) {
     // Positions are pairs of steps, one barrier per pair: position i computes pair i from code
@@ -543,17 +713,39 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   }
   // the clamped loads past the end must land before the block (and its LDS) is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (GU && !DBG) {
+    // group sums of h: the block's 64 h columns are one group of the down product's reduction;
+    // the 4 waves' partial sums meet in LDS (every load has landed and every read is done after
+    // the barrier) and are added in wave order
+    __syncthreads();
+    float* s_part = reinterpret_cast<float*>(lds);  // [4 waves][16 MT rows]
+    if (n == 0) {
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_part[wave * 16 * MT + 16 * mm + 4 * kb + r] = hpart[mm][r];
+    }
+    __syncthreads();
+    if (tid < 16 * MT && tid < rows) {
+      const float v = ((s_part[tid] + s_part[16 * MT + tid]) + s_part[32 * MT + tid]) + s_part[48 * MT + tid];
+      const int grp = nb0;  // column block = group of 64 h columns (one job per gate/up block)
+      if (sh)
+        a.hsum_sh[(size_t)(row0 - a.P + tid) * (size_t)(Ie / kGroup) + grp] = v;
+      else
+        a.hsum[(size_t)(row0 + tid) * (size_t)(Ie / kGroup) + grp] = v;
+    }
+  }
 }
 
-template <bool GU, bool PAIRED, int R, bool DBG = false>
+template <bool GU, bool PAIRED, int R, bool DBG, bool VEC8>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
-  constexpr int kSbBytes = PAIRED ? 1024 : 2048;
+  constexpr int kSbBytes = PAIRED ? 512 : 1024;
   // One LDS buffer, carved per tile height: two code pair stages, then four 16-row A stages and
   // four scale stages (tiles of at most 16 rows, whole steps), three of each (at most 16 rows,
   // K an odd number of groups), or two 32-row A stages and two scale stages.
-  constexpr int kLds1 = 2 * kPairCodeStageBytes + 3 * kA16StageBytes + 3 * kSbBytes;
-  constexpr int kLds2 = 2 * kPairCodeStageBytes + 2 * 2 * kA16StageBytes + 2 * kSbBytes;
-  constexpr int kLds4 = PAIRED ? 2 * kPairCodeStageBytes + 4 * kA16StageBytes + 4 * kSbBytes : 0;
+  constexpr int kLds1 = 2 * kPairCodeStageBytes + 3 * (kA16StageBytes + kSbBytes);
+  constexpr int kLds2 = 2 * kPairCodeStageBytes + 2 * (2 * kA16StageBytes + kSbBytes);
+  constexpr int kLds4 = PAIRED ? 2 * kPairCodeStageBytes + 4 * (kA16StageBytes + kSbBytes) : 0;
   constexpr int kLds12 = kLds1 > kLds2 ? kLds1 : kLds2;
   constexpr int kLds = kLds12 > kLds4 ? kLds12 : kLds4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
@@ -565,20 +757,21 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   if (rows <= 16)
-    run_body<1, PAIRED ? 4 : 3, GU, PAIRED, R, DBG>(a, run, e, row0, rows, lds);
+    run_body<1, PAIRED ? 4 : 3, GU, PAIRED, R, DBG, VEC8>(a, run, e, row0, rows, lds);
   else
-    run_body<2, 2, GU, PAIRED, R, DBG>(a, run, e, row0, rows, lds);
+    run_body<2, 2, GU, PAIRED, R, DBG, VEC8>(a, run, e, row0, rows, lds);
 }
 
-// DBG: the check export (fp32 pre-activations instead of h)
-template <bool PAIRED, bool DBG>
+// DBG: the check export (fp32 pre-activations instead of h). VEC8: the reduction is a multiple of
+// 8 groups (512 inputs), so the bias operands load as aligned 16-byte vectors.
+template <bool PAIRED, bool DBG, bool VEC8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_gemm(GemmArgs a) {
-  gemm_block<true, PAIRED, kRunGu, DBG>(a);
+  gemm_block<true, PAIRED, kRunGu, DBG, VEC8>(a);
 }
 
-template <bool PAIRED, int R>
+template <bool PAIRED, int R, bool VEC8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_gemm(GemmArgs a) {
-  gemm_block<false, PAIRED, R>(a);
+  gemm_block<false, PAIRED, R, false, VEC8>(a);
 }
 
 static GemmArgs gemm_args(const Ctx& c, int nruns) {
@@ -601,6 +794,9 @@ static GemmArgs gemm_args(const Ctx& c, int nruns) {
   a.h = c.h;
   a.hs = c.hs;
   a.y_rows = c.y_rows;
+  a.xsum = c.xsum;
+  a.hsum = c.hsum;
+  a.hsum_sh = c.hsum_sh;
   a.dbg_g = c.dbg_g;
   a.dbg_u = c.dbg_u;
   return a;
@@ -617,14 +813,14 @@ hipError_t launch_gateup_gemm(const Ctx& c) {
   const int nruns = (ncb + kRunGu - 1) / kRunGu;
   const dim3 grid(grid_blocks(c.max_tiles, nruns));
   const bool dbg = c.dbg_g != nullptr;
-  if (c.d % kBK == 0 && !dbg)
-    hipLaunchKernelGGL((k_gateup_gemm<true, false>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
-  else if (!dbg)
-    hipLaunchKernelGGL((k_gateup_gemm<false, false>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+  const bool vec8 = c.d % (8 * kGroup) == 0;
+  const auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, c.stream, gemm_args(c, nruns)); };
+  if (vec8)
+    dbg ? go(k_gateup_gemm<true, true, true>) : go(k_gateup_gemm<true, false, true>);
   else if (c.d % kBK == 0)
-    hipLaunchKernelGGL((k_gateup_gemm<true, true>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+    dbg ? go(k_gateup_gemm<true, true, false>) : go(k_gateup_gemm<true, false, false>);
   else
-    hipLaunchKernelGGL((k_gateup_gemm<false, true>), grid, dim3(256), 0, c.stream, gemm_args(c, nruns));
+    dbg ? go(k_gateup_gemm<false, true, false>) : go(k_gateup_gemm<false, false, false>);
   return hipGetLastError();
 }
 
@@ -633,17 +829,18 @@ hipError_t launch_down_gemm(const Ctx& c) {
   const int R = down_run(c.I);
   const int nruns = (ncb + R - 1) / R;
   const dim3 grid(grid_blocks(c.max_tiles, nruns));
-  // both the routed and the shared matrix must be whole steps for the paired form
+  // both the routed and the shared matrix must be whole steps for the paired form, and multiples
+  // of 8 groups for the vector form
   const bool paired = c.I % kBK == 0 && (c.Is == 0 || c.Is % kBK == 0);
+  const bool vec8 = c.I % (8 * kGroup) == 0 && (c.Is == 0 || c.Is % (8 * kGroup) == 0);
   const GemmArgs a = gemm_args(c, nruns);
-  if (paired && R == 1)
-    hipLaunchKernelGGL((k_down_gemm<true, 1>), grid, dim3(256), 0, c.stream, a);
+  const auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, c.stream, a); };
+  if (vec8)
+    R == 1 ? go(k_down_gemm<true, 1, true>) : go(k_down_gemm<true, 2, true>);
   else if (paired)
-    hipLaunchKernelGGL((k_down_gemm<true, 2>), grid, dim3(256), 0, c.stream, a);
-  else if (R == 1)
-    hipLaunchKernelGGL((k_down_gemm<false, 1>), grid, dim3(256), 0, c.stream, a);
+    R == 1 ? go(k_down_gemm<true, 1, false>) : go(k_down_gemm<true, 2, false>);
   else
-    hipLaunchKernelGGL((k_down_gemm<false, 2>), grid, dim3(256), 0, c.stream, a);
+    R == 1 ? go(k_down_gemm<false, 1, false>) : go(k_down_gemm<false, 2, false>);
   return hipGetLastError();
 }
 

@@ -22,6 +22,9 @@ struct Ctx {
   float* router_parts;    // [T][E][d/64] router chunk partials (GEMV path, T <= kGemvMaxT)
   float* logits;          // [T][E] router logits (T >= 2)
   uint16_t* xp;           // [T][d] bf16: x with each 8-input chunk in pair order (grouped GEMM operand)
+  float* xsum;            // [T][d/64] fp32 group sums of x (written with xp)
+  float* hsum;            // [P][I/64] fp32 group sums of h (grouped GEMM path)
+  float* hsum_sh;         // [T][Is/64] fp32 group sums of the shared expert's h
   bool pair_in_meta;      // the routing-metadata launch also writes xp
   uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1); pair order on the GEMM path
   uint16_t* hs;           // [T][Is] bf16
@@ -37,10 +40,11 @@ hipError_t launch_router_decode(const Ctx& c);
 hipError_t launch_decode_topk(const Ctx& c);
 hipError_t launch_router_prefill(const Ctx& c);  // logits [T][E]
 hipError_t launch_topk_prefill(const Ctx& c);    // logits -> topk_ids, topk_w
-hipError_t launch_route_meta(const Ctx& c);  // + xp from x in extra blocks when c.pair_in_meta
-hipError_t launch_pair_x(const Ctx& c);      // xp from x
-// any bf16 rows (a whole number of 8-input chunks each) in pair order: dst from src, nchunks chunks
-hipError_t launch_pair_rows(const uint16_t* src, uint16_t* dst, int64_t nchunks, hipStream_t stream);
+hipError_t launch_route_meta(const Ctx& c);  // + xp, xsum from x in extra blocks when c.pair_in_meta
+hipError_t launch_pair_x(const Ctx& c);      // xp, xsum from x
+// bf16 rows of K inputs (K a multiple of 64) in pair order, dst from src, with their group sums
+// sums [nrows][K/64] (fp32, inputs of a group added in ascending order)
+hipError_t launch_pair_rows(const uint16_t* src, uint16_t* dst, float* sums, int64_t nrows, int K, hipStream_t stream);
 // fused_topk: take the top-k from the router partials in every block, plus the shared expert's
 // rows in blocks of their own when its weights are set; otherwise read topk_ids and compute the
 // shared slot after each token's routed slots

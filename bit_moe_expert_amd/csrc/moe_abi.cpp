@@ -74,7 +74,8 @@ bool gemv_path_ctx(const Ctx& c) {
 }
 
 struct Layout {
-  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, xp, h, hs, y_rows, total;
+  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, xp, xsum, h, hs, hsum, hsum_sh,
+      y_rows, total;
 };
 
 Layout layout_of(const moe_dims& dm, int32_t T) {
@@ -103,10 +104,16 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   o += up(4);
   L.xp = o;
   o += up((size_t)T * d * 2);
+  L.xsum = o;
+  o += up((size_t)T * (d / 64) * 4);
   L.h = o;
   o += up(P * dm.d_ff * 2);
   L.hs = o;
   o += up((size_t)T * dm.d_ff_shared * 2);
+  L.hsum = o;
+  o += up(P * (dm.d_ff / 64) * 4);
+  L.hsum_sh = o;
+  o += up((size_t)T * (dm.d_ff_shared / 64) * 4);
   L.y_rows = o;
   o += up((P + T) * d * 4);
   L.total = o;
@@ -225,6 +232,9 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.router_parts = reinterpret_cast<float*>(b + L.parts);
   c.logits = reinterpret_cast<float*>(b + L.logits);
   c.xp = reinterpret_cast<uint16_t*>(b + L.xp);
+  c.xsum = reinterpret_cast<float*>(b + L.xsum);
+  c.hsum = reinterpret_cast<float*>(b + L.hsum);
+  c.hsum_sh = reinterpret_cast<float*>(b + L.hsum_sh);
   c.pair_in_meta = false;
   c.h = reinterpret_cast<uint16_t*>(b + L.h);
   c.hs = reinterpret_cast<uint16_t*>(b + L.hs);
@@ -453,8 +463,8 @@ int moe_debug_grouped_gemm(const moe_dims* dims, int32_t T, int32_t which, const
     if (int rc = run_stage(kPairX, c)) return rc;
     return run_stage(kGemmGateup, c);
   }
-  e = launch_pair_rows(a, c.h, (int64_t)c.P * c.I / 8, c.stream);
-  if (e == hipSuccess) e = launch_pair_rows(a + (size_t)c.P * c.I, c.hs, (int64_t)c.T * c.Is / 8, c.stream);
+  e = launch_pair_rows(a, c.h, c.hsum, c.P, c.I, c.stream);
+  if (e == hipSuccess && c.Is) e = launch_pair_rows(a + (size_t)c.P * c.I, c.hs, c.hsum_sh, c.T, c.Is, c.stream);
   if (e != hipSuccess) return fail(MOE_EHIP, "launch of pair_rows failed: %s", hipGetErrorString(e));
   c.y_rows = out;
   return run_stage(kGemmDown, c);

@@ -163,14 +163,73 @@ hipError_t launch_topk_prefill(const Ctx& c) {
   return hipGetLastError();
 }
 
+// x in pair order for the grouped GEMM's A operand, with its group sums: each 16-byte chunk of 8
+// inputs is rewritten as inputs 0, 4, 1, 5, 2, 6, 3, 7, the order of the weight pairs its matrix
+// cores multiply (so the GEMM reads rows without re-pairing them for every column block), and
+// sums[row][g] = the sum of the row's inputs 64 g .. 64 g + 63 in fp32, the factor of the bias
+// term of group g: each chunk's 8 inputs in ascending order, then the 8 chunks of the group pairwise
+// (chunks 2c and 2c + 1, then pairs of those, then the two halves) across the 8 lanes that hold
+// them. Rows hold K inputs (a multiple of 64); thread i of `nthreads` takes chunks i, i + nthreads,
+// ... of the whole [rows][K] array (nthreads a multiple of 64, so a group's chunks meet in one wave).
+__device__ __forceinline__ void pair_groups(const uint4* __restrict__ x, uint4* __restrict__ xp, float* __restrict__ sums,
+                                            int64_t nchunks, int64_t i, int64_t nthreads) {
+  for (int64_t base = i & ~(int64_t)63; base < nchunks; base += nthreads, i += nthreads) {
+    const bool ok = i < nchunks;
+    const uint4 v = ok ? x[i] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t p[4];
+    repair8(w, p);
+    if (ok) xp[i] = make_uint4(p[0], p[1], p[2], p[3]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = (acc + bf16lo(w[q])) + bf16hi(w[q]);
+    acc += dpp_f32<0xB1>(acc);    // chunks (2c, 2c + 1): lane i ^ 1
+    acc += dpp_f32<0x4E>(acc);    // pairs of pairs: lane i ^ 2
+    acc += __shfl_xor(acc, 4, 64);  // the two halves of each 8-lane group: lane i ^ 4
+    if (ok && (i & 7) == 0) sums[i >> 3] = acc;
+  }
+}
+
+constexpr int kPairBlocks = 256;  // blocks that pair x (beside the metadata blocks, or alone)
+
+__global__ __launch_bounds__(256) void k_pair_rows(const uint4* __restrict__ x, uint4* __restrict__ xp,
+                                                   float* __restrict__ sums, int64_t nchunks) {
+  pair_groups(x, xp, sums, nchunks, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
+}
+
+static int pair_blocks(int64_t nchunks, int threads) {
+  return (int)std::min<int64_t>(kPairBlocks, (nchunks + threads - 1) / threads);
+}
+
+hipError_t launch_pair_rows(const uint16_t* src, uint16_t* dst, float* sums, int64_t nrows, int K,
+                            hipStream_t stream) {
+  const int64_t nchunks = nrows * (K / 8);
+  if (nchunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pair_rows, dim3(pair_blocks(nchunks, 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), sums, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_x(const Ctx& c) { return launch_pair_rows(c.x, c.xp, c.xsum, c.T, c.d, c.stream); }
+
 // ---------------------------------------------------------------------------------------------
-// Histogram, prefix scan, stable scatter and block map in one 1024-thread block.
-// Wave w owns the contiguous pair range [w*span, (w+1)*span). Pass 1 counts per wave and
-// expert in LDS (atomics only for counts). A scan over experts gives offsets; a scan over waves
-// per expert gives each wave's first row in every group. Pass 2 walks the range again in steps
-// of 64 pairs: lanes with the same expert find each other with one ballot per bit of the expert
-// id, so a lane's rank is the popcount of its lower peers; the lowest peer advances the wave's
-// cursor. Rows of an expert therefore follow pair order, i.e. ascending token.
+// Histogram, prefix scan, stable scatter and block map over several 1024-thread blocks.
+// Block b ranks the pairs [b span, (b + 1) span); every block reads all T k expert ids to count,
+// per expert, all pairs and the pairs before its slice, so no block waits for another:
+//   - counts come from wave ballots: the lanes of a wave holding the same expert find each other
+//     with one ballot per bit of the expert id, and the lowest of them adds their number (the
+//     whole-table counts with an LDS atomic, a wave's own slice counts with a plain add);
+//   - a block scan over experts gives offsets; the first row of expert e for wave w of block b is
+//     offsets[e] + (pairs of e before the block) + (pairs of e in waves 0 .. w - 1 of the block);
+//   - within a wave, a lane's rank among its peers is the popcount of its lower peers, so the rows
+//     of an expert follow pair order, i.e. ascending token.
+// Block 0 also writes counts, offsets and the block map: each non-empty group in ascending expert
+// order cut into consecutive tiles of at most kTileRows rows, then the shared expert's T rows.
+// Blocks past the metadata blocks pair x for the grouped GEMM (they need nothing from the others).
+constexpr int kMetaWaves = 16;
+constexpr int kMetaSpan = 1024;  // pairs ranked per metadata block
+constexpr int kMetaBatch = 8;    // 64-pair batches whose ids a wave loads together when counting
+
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int incl = v;
@@ -199,161 +258,150 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
   return r;
 }
 
-constexpr int kMetaBatch = 8;  // pairs per lane whose ids are loaded together
-
-// x in pair order for the grouped GEMM's A operand: each 16-byte chunk of 8 inputs is rewritten
-// as inputs 0, 4, 1, 5, 2, 6, 3, 7, the order of the weight pairs its matrix cores multiply, so
-// the GEMM reads it without re-pairing every time a column block uses the row. Thread i of
-// `nthreads` takes chunks i, i + nthreads, ...
-__device__ __forceinline__ void pair_x_chunks(const uint4* __restrict__ x, uint4* __restrict__ xp, int64_t nchunks,
-                                              int64_t i, int64_t nthreads) {
-  for (; i < nchunks; i += nthreads) {
-    const uint4 v = x[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t p[4];
-    repair8(w, p);
-    xp[i] = make_uint4(p[0], p[1], p[2], p[3]);
+// The lanes of the wave (valid ones only) holding the same expert id as this lane.
+__device__ __forceinline__ uint64_t peer_mask(int e, bool valid, int nbits) {
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    peers &= bit ? bb : ~bb;
   }
+  return valid ? peers : 0ull;
 }
 
-constexpr int kPairBlocks = 256;  // blocks that pair x (beside the metadata block, or alone)
-
-__global__ __launch_bounds__(256) void k_pair_x(const uint4* __restrict__ x, uint4* __restrict__ xp, int64_t nchunks) {
-  pair_x_chunks(x, xp, nchunks, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
-}
-
-static int pair_blocks(int64_t nchunks, int threads) {
-  return (int)std::min<int64_t>(kPairBlocks, (nchunks + threads - 1) / threads);
-}
-
-hipError_t launch_pair_rows(const uint16_t* src, uint16_t* dst, int64_t nchunks, hipStream_t stream) {
-  if (nchunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pair_x, dim3(pair_blocks(nchunks, 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), nchunks);
-  return hipGetLastError();
-}
-
-hipError_t launch_pair_x(const Ctx& c) { return launch_pair_rows(c.x, c.xp, (int64_t)c.T * c.d / 8, c.stream); }
-
-// Blocks 1 .. gridDim.x - 1, when present, pair x instead (they need nothing from block 0).
-__global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared,
+__global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared, int n_meta,
                                                      const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
                                                      int32_t* __restrict__ inv_pos, int32_t* __restrict__ tiles,
                                                      int32_t* __restrict__ n_tiles, const uint4* __restrict__ x,
-                                                     uint4* __restrict__ xp, int64_t nchunks) {
-  __shared__ int s_tab[16][kMaxExperts];  // 64 KB: per-wave counts, then per-wave cursors
+                                                     uint4* __restrict__ xp, float* __restrict__ xsum, int64_t nchunks) {
+  __shared__ int s_all[kMaxExperts];                 // pairs of each expert
+  __shared__ int s_before[kMaxExperts];              // pairs of each expert before this block's slice
+  __shared__ int s_tab[kMetaWaves][kMaxExperts];     // per-wave counts of the slice, then cursors
   __shared__ int s_wsum[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (blockIdx.x > 0) {
-    pair_x_chunks(x, xp, nchunks, (int64_t)(blockIdx.x - 1) * 1024 + tid, (int64_t)(gridDim.x - 1) * 1024);
+  if ((int)blockIdx.x >= n_meta) {
+    pair_groups(x, xp, xsum, nchunks, (int64_t)(blockIdx.x - n_meta) * 1024 + tid,
+                (int64_t)(gridDim.x - n_meta) * 1024);
     return;
   }
   const int P = T * k;
-  for (int e = tid; e < E; e += 1024)
+  const int b_begin = min(P, (int)blockIdx.x * kMetaSpan), b_end = min(P, b_begin + kMetaSpan);
+  for (int e = tid; e < E; e += 1024) {
+    s_all[e] = 0;
+    s_before[e] = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < 16; ++w2) s_tab[w2][e] = 0;
-  __syncthreads();
-  const int span = (((P + 15) / 16) + 63) & ~63;
-  const int p_begin = min(P, wave * span), p_end = min(P, p_begin + span);
-  // the wave's pairs in batches of kMetaBatch per lane, every load of a batch in flight at once
-  for (int base = p_begin; base < p_end; base += 64 * kMetaBatch) {
-    int ev[kMetaBatch];
-#pragma unroll
-    for (int i = 0; i < kMetaBatch; ++i) {
-      const int p = base + lane + 64 * i;
-      ev[i] = p < p_end ? ids[p] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < kMetaBatch; ++i)
-      if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&s_tab[wave][ev[i]], 1);
+    for (int w2 = 0; w2 < kMetaWaves; ++w2) s_tab[w2][e] = 0;
   }
   __syncthreads();
-  // this expert's 16 per-wave counts, read once (all reads in flight together)
-  int wc[16];
-#pragma unroll
-  for (int w2 = 0; w2 < 16; ++w2) wc[w2] = tid < E ? s_tab[w2][tid] : 0;
-  int cnt = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < 16; ++w2) cnt += wc[w2];
-  int total = 0;
-  const int off = block_excl_scan(tid < E ? cnt : 0, s_wsum, &total);
-  if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
-    int run = off;
-#pragma unroll
-    for (int w2 = 0; w2 < 16; ++w2) {
-      s_tab[w2][tid] = run;
-      run += wc[w2];
-    }
-  }
-  if (tid == 0) offsets[E] = total;
-  // block map: routed tiles in expert order, then the shared expert's rows
-  const int nt = tid < E ? (cnt + kTileRows - 1) / kTileRows : 0;
-  int n_routed = 0;
-  const int tfirst = block_excl_scan(nt, s_wsum, &n_routed);
-  for (int j = 0; j < nt; ++j) {
-    int32_t* tl = tiles + 3 * (size_t)(tfirst + j);
-    tl[0] = tid;
-    tl[1] = off + j * kTileRows;
-    tl[2] = min(kTileRows, cnt - j * kTileRows);
-  }
-  const int n_shared = has_shared ? (T + kTileRows - 1) / kTileRows : 0;
-  for (int j = tid; j < n_shared; j += 1024) {
-    int32_t* tl = tiles + 3 * (size_t)(n_routed + j);
-    tl[0] = E;
-    tl[1] = P + j * kTileRows;
-    tl[2] = min(kTileRows, T - j * kTileRows);
-  }
-  if (tid == 0) *n_tiles = n_routed + n_shared;
-  __syncthreads();
-  // pass 2: stable ranks. This pass is bound by the single block's VALU issue, so each step is
-  // kept short (the token index comes from an fp32 reciprocal, not an integer division).
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
-  const float inv_k = 1.0f / (float)k;
-  for (int base = p_begin; base < p_end; base += 64 * kMetaBatch) {
+  // 1. counts of all pairs and of the pairs before the slice (every block, every pair); a wave
+  //    takes 64-pair batches wave, wave + 16, ... and loads kMetaBatch of them before counting any
+  for (int base0 = wave * 64; base0 < P; base0 += 64 * kMetaWaves * kMetaBatch) {
     int ev[kMetaBatch];
 #pragma unroll
     for (int i = 0; i < kMetaBatch; ++i) {
-      const int p = base + lane + 64 * i;
-      ev[i] = p < p_end ? ids[p] : -1;
+      const int p = base0 + 64 * kMetaWaves * i + lane;
+      ev[i] = p < P ? ids[p] : -1;
     }
 #pragma unroll
     for (int i = 0; i < kMetaBatch; ++i) {
-      if (base + 64 * i >= p_end) break;  // wave-uniform
-      const int p = base + lane + 64 * i;
+      const int base = base0 + 64 * kMetaWaves * i;
+      if (base >= P) break;  // wave-uniform
       const int e = ev[i];
       const bool valid = (unsigned)e < (unsigned)E;
-      // p / k through the fp32 reciprocal (p < 2^21 is exact in fp32), then corrected by one
-      int tq = (int)((float)p * inv_k);
-      const int r = p - tq * k;
-      tq += r >= k ? 1 : (r < 0 ? -1 : 0);
-      uint64_t peers = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bb = __ballot(valid && bit);
-        peers &= bit ? bb : ~bb;
+      const uint64_t peers = peer_mask(e, valid, nbits);
+      if (valid && (peers & lanemask_lt()) == 0) {
+        atomicAdd(&s_all[e], __popcll(peers));
+        // lanes below b_begin in this batch are a prefix of it: count only those peers
+        const int nb = min(max(b_begin - base, 0), 64);
+        const uint64_t below = nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
+        if (peers & below) atomicAdd(&s_before[e], __popcll(peers & below));
       }
-      int pos = 0;
-      if (valid) pos = s_tab[wave][e] + __popcll(peers & lanemask_lt());
-      __builtin_amdgcn_wave_barrier();
-      if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
-      __builtin_amdgcn_wave_barrier();
-      if (valid) {
-        sorted_token[pos] = tq;
-        inv_pos[p] = pos;
-      }
+    }
+  }
+  // 2. per-wave counts of this block's slice: wave w owns [b_begin + w wspan, ...)
+  const int wspan = (((kMetaSpan + kMetaWaves - 1) / kMetaWaves) + 63) & ~63;
+  const int w_begin = min(b_end, b_begin + wave * wspan), w_end = min(b_end, w_begin + wspan);
+  for (int base = w_begin; base < w_end; base += 64) {
+    const int p = base + lane;
+    const int e = p < w_end ? ids[p] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    const uint64_t peers = peer_mask(e, valid, nbits);
+    if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // 3. offsets, then each wave's first row in every group
+  const int cnt = tid < E ? s_all[tid] : 0;
+  int total = 0;
+  const int off = block_excl_scan(cnt, s_wsum, &total);
+  if (tid < E) {
+    int run = off + s_before[tid];
+#pragma unroll
+    for (int w2 = 0; w2 < kMetaWaves; ++w2) {
+      const int c = s_tab[w2][tid];
+      s_tab[w2][tid] = run;
+      run += c;
+    }
+  }
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == 0) offsets[E] = total;
+    // block map: routed tiles in expert order, then the shared expert's rows
+    const int nt = tid < E ? (cnt + kTileRows - 1) / kTileRows : 0;
+    int n_routed = 0;
+    const int tfirst = block_excl_scan(nt, s_wsum, &n_routed);
+    for (int j = 0; j < nt; ++j) {
+      int32_t* tl = tiles + 3 * (size_t)(tfirst + j);
+      tl[0] = tid;
+      tl[1] = off + j * kTileRows;
+      tl[2] = min(kTileRows, cnt - j * kTileRows);
+    }
+    const int n_shared = has_shared ? (T + kTileRows - 1) / kTileRows : 0;
+    for (int j = tid; j < n_shared; j += 1024) {
+      int32_t* tl = tiles + 3 * (size_t)(n_routed + j);
+      tl[0] = E;
+      tl[1] = P + j * kTileRows;
+      tl[2] = min(kTileRows, T - j * kTileRows);
+    }
+    if (tid == 0) *n_tiles = n_routed + n_shared;
+  }
+  __syncthreads();
+  // 4. stable ranks of the slice: a lane's row is the wave's cursor plus the number of its lower
+  //    peers; the lowest peer then advances the cursor. The token index comes from an fp32
+  //    reciprocal with a one-step correction (exact for p < 2^21).
+  const float inv_k = 1.0f / (float)k;
+  for (int base = w_begin; base < w_end; base += 64) {
+    const int p = base + lane;
+    const int e = p < w_end ? ids[p] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    int tq = (int)((float)p * inv_k);
+    const int r = p - tq * k;
+    tq += r >= k ? 1 : (r < 0 ? -1 : 0);
+    const uint64_t peers = peer_mask(e, valid, nbits);
+    int pos = 0;
+    if (valid) pos = s_tab[wave][e] + __popcll(peers & lanemask_lt());
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      sorted_token[pos] = tq;
+      inv_pos[p] = pos;
     }
   }
 }
 
 hipError_t launch_route_meta(const Ctx& c) {
   const int64_t nchunks = c.pair_in_meta ? (int64_t)c.T * c.d / 8 : 0;
-  const int nblocks = 1 + (nchunks ? pair_blocks(nchunks, 1024) : 0);
-  hipLaunchKernelGGL(k_route_meta, dim3(nblocks), dim3(1024), 0, c.stream, c.T, c.E, c.k, c.Is > 0 ? 1 : 0,
+  const int n_meta = std::max(1, (c.P + kMetaSpan - 1) / kMetaSpan);
+  const int nblocks = n_meta + (nchunks ? pair_blocks(nchunks, 1024) : 0);
+  hipLaunchKernelGGL(k_route_meta, dim3(nblocks), dim3(1024), 0, c.stream, c.T, c.E, c.k, c.Is > 0 ? 1 : 0, n_meta,
                      c.r.topk_ids, c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos, c.r.tiles, c.r.n_tiles,
-                     reinterpret_cast<const uint4*>(c.x), reinterpret_cast<uint4*>(c.xp), nchunks);
+                     reinterpret_cast<const uint4*>(c.x), reinterpret_cast<uint4*>(c.xp), c.xsum, nchunks);
   return hipGetLastError();
 }
 
