@@ -216,13 +216,12 @@ hipError_t launch_pair_x(const Ctx& c) { return launch_pair_rows(c.x, c.xp, c.xs
 // Histogram, prefix scan, stable scatter and block map over several 1024-thread blocks.
 // Block b ranks the pairs [b span, (b + 1) span); every block reads all T k expert ids to count,
 // per expert, all pairs and the pairs before its slice, so no block waits for another:
-//   - counts come from wave ballots: the lanes of a wave holding the same expert find each other
-//     with one ballot per bit of the expert id, and the lowest of them adds their number (the
-//     whole-table counts with an LDS atomic, a wave's own slice counts with a plain add);
+//   - counts are LDS atomic adds, one per pair (exact integers, whatever the order of the adds);
 //   - a block scan over experts gives offsets; the first row of expert e for wave w of block b is
 //     offsets[e] + (pairs of e before the block) + (pairs of e in waves 0 .. w - 1 of the block);
-//   - within a wave, a lane's rank among its peers is the popcount of its lower peers, so the rows
-//     of an expert follow pair order, i.e. ascending token.
+//   - within a wave, the lanes holding the same expert find each other with one ballot per bit of
+//     the expert id, and a lane's rank among its peers is the popcount of its lower peers, so the
+//     rows of an expert follow pair order, i.e. ascending token.
 // Block 0 also writes counts, offsets and the block map: each non-empty group in ascending expert
 // order cut into consecutive tiles of at most kTileRows rows, then the shared expert's T rows.
 // Blocks past the metadata blocks pair x for the grouped GEMM (they need nothing from the others).
@@ -295,8 +294,9 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
   }
   __syncthreads();
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
-  // 1. counts of all pairs and of the pairs before the slice (every block, every pair); a wave
-  //    takes 64-pair batches wave, wave + 16, ... and loads kMetaBatch of them before counting any
+  // 1. counts of all pairs and of the pairs before the slice (every block, every pair): one LDS
+  //    atomic add per pair (integer counts do not depend on the order of the adds); a wave takes
+  //    64-pair batches wave, wave + 16, ... and loads kMetaBatch of them before counting any
   for (int base0 = wave * 64; base0 < P; base0 += 64 * kMetaWaves * kMetaBatch) {
     int ev[kMetaBatch];
 #pragma unroll
@@ -306,17 +306,11 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
     }
 #pragma unroll
     for (int i = 0; i < kMetaBatch; ++i) {
-      const int base = base0 + 64 * kMetaWaves * i;
-      if (base >= P) break;  // wave-uniform
+      const int p = base0 + 64 * kMetaWaves * i + lane;
       const int e = ev[i];
-      const bool valid = (unsigned)e < (unsigned)E;
-      const uint64_t peers = peer_mask(e, valid, nbits);
-      if (valid && (peers & lanemask_lt()) == 0) {
-        atomicAdd(&s_all[e], __popcll(peers));
-        // lanes below b_begin in this batch are a prefix of it: count only those peers
-        const int nb = min(max(b_begin - base, 0), 64);
-        const uint64_t below = nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
-        if (peers & below) atomicAdd(&s_before[e], __popcll(peers & below));
+      if ((unsigned)e < (unsigned)E) {
+        atomicAdd(&s_all[e], 1);
+        if (p < b_begin) atomicAdd(&s_before[e], 1);
       }
     }
   }
@@ -326,10 +320,7 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
   for (int base = w_begin; base < w_end; base += 64) {
     const int p = base + lane;
     const int e = p < w_end ? ids[p] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    const uint64_t peers = peer_mask(e, valid, nbits);
-    if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_tab[wave][e], 1);
   }
   __syncthreads();
   // 3. offsets, then each wave's first row in every group
