@@ -59,22 +59,27 @@ DESCR = {
     "m32_2": "small-M with 2-bit expert codes: T=32, decode shapes, 40 layers cycled",
     "tiny3": "tiny with 3-bit expert codes: T=8, d=256, 16 experts top-4 + shared (I=I_s=128), g64",
     "tiny2": "tiny with 2-bit expert codes: T=8, d=256, 16 experts top-4 + shared (I=I_s=128), g64",
+    "prefill3": "prefill with 3-bit expert codes: T=512, d=2048, 256 experts top-8 + shared, I=I_s=512, g64, 4 layers",
+    "diffusion3": "diffusion with 3-bit expert codes: T=256 canvas x 30 layers, d=2048, 128 experts top-8, I=768",
+    "diffusion2": "diffusion with 2-bit expert codes: T=256 canvas x 30 layers, d=2048, 128 experts top-8, I=768",
 }
 # layers held on the GPU and calls per step
 PLAN = {"tiny": (1, 1), "decode": (40, 40), "prefill": (4, 4), "long": (4, 4), "diffusion": (30, 30),
         "m2": (40, 40), "m4": (40, 40), "m8": (40, 40), "m16": (40, 40), "m32": (40, 40), "m64": (40, 40),
-        "decode3": (40, 40), "decode2": (40, 40), "m32_3": (40, 40), "m32_2": (40, 40), "tiny3": (1, 1), "tiny2": (1, 1)}
+        "decode3": (40, 40), "decode2": (40, 40), "m32_3": (40, 40), "m32_2": (40, 40), "tiny3": (1, 1), "tiny2": (1, 1),
+        "prefill3": (4, 4), "diffusion3": (30, 30), "diffusion2": (30, 30)}
 DOMINANT = {"tiny": "gateup_gemm", "decode": "gemv_gateup_topk", "prefill": "gateup_gemm", "long": "gateup_gemm",
             "diffusion": "gateup_gemm", "m2": "gemv_gateup_topk", "m4": "gemv_gateup_topk",
             "m8": "gemv_gateup_topk", "m16": "gemv_gateup_topk", "m32": "gemv_gateup_topk",
             "m64": "gateup_gemm", "decode3": "gemv_gateup_topk", "decode2": "gemv_gateup_topk",
             "m32_3": "gemv_gateup_topk", "m32_2": "gemv_gateup_topk", "tiny3": "gemv_gateup_topk",
-            "tiny2": "gemv_gateup_topk"}
+            "tiny2": "gemv_gateup_topk", "prefill3": "gateup_gemm", "diffusion3": "gateup_gemm",
+            "diffusion2": "gateup_gemm"}
 STAGE_SOURCE = {"router_decode": "gemv.hip", "router_prefill": "route.hip", "route_meta": "route.hip",
                 "gemv_gateup": "gemv.hip", "gemv_gateup_topk": "gemv.hip", "decode_topk": "route.hip",
                 "topk_prefill": "route.hip",
-                "gemv_down_combine": "gemv.hip", "gateup_gemm": "gemm.hip",
-                "down_gemm": "gemm.hip", "combine": "gemm.hip", "chunk_max": "vocab_topk.hip",
+                "gemv_down_combine": "gemv.hip", "gateup_gemm": "gemm_impl.h",
+                "down_gemm": "gemm_impl.h", "combine": "gemm.hip", "chunk_max": "vocab_topk.hip",
                 "topk_rows": "vocab_topk.hip"}
 
 
@@ -488,7 +493,7 @@ def run_workload(name: str, args, dev, cpu_seconds: float, headline: bool) -> di
 
 
 # ------------------------------------------------------------------------- main
-EXTRA_DEFAULT = "tiny,prefill,long,diffusion"
+EXTRA_DEFAULT = "tiny,prefill,long,diffusion,diffusion2"
 
 
 def main() -> int:

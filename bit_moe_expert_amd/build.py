@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_int4.so")
-SOURCES = ["moe_abi.cpp", "route.hip", "gemv.hip", "gemm.hip", "dequant.hip", "vocab_topk.hip", "noalloc.hip"]
+SOURCES = ["moe_abi.cpp", "route.hip", "gemv.hip", "gemm.hip", "gemm_b3.hip", "gemm_b2.hip", "dequant.hip", "vocab_topk.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 CXXFLAGS = [

@@ -12,7 +12,7 @@ namespace moe {
 // Everything one layer call needs, resolved to device pointers by the C-ABI layer.
 struct Ctx {
   int d, E, k, I, Is, T, P, max_tiles;
-  int bits;  // bits per expert weight code: 4, 3 or 2 (3 and 2 on the GEMV path only)
+  int bits;  // bits per expert weight code: 4, 3 or 2
   const uint16_t* x;
   const float* w_router;
   const float* logit_bias;

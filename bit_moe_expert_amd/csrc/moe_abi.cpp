@@ -51,8 +51,8 @@ int check_dims(const moe_dims* dm, int32_t T) {
 
 int bits_of(const moe_dims& dm) { return dm.code_bits == 0 ? 4 : dm.code_bits; }
 
-// 16-byte loads of 4-bit codes, 12-byte (dword) loads of 3-bit and 8-byte loads of 2-bit codes
-size_t code_align(int bits) { return bits == 4 ? 16 : bits == 3 ? 4 : 8; }
+// 16-byte loads of 4- and 2-bit codes, 12-byte (dword-aligned) loads of 3-bit codes
+size_t code_align(int bits) { return bits == 3 ? 4 : 16; }
 
 int32_t max_tiles_of(const moe_dims& dm, int32_t T) {
   const int64_t P = (int64_t)T * dm.top_k;
@@ -266,9 +266,6 @@ int check_layer_args(const moe_dims* dims, int32_t T, const uint16_t* x, const f
   if (need_router && (!w_router || !aligned(w_router, 16)))
     return fail(MOE_EINVAL, "w_router NULL or not 16-byte aligned");
   const int bits = bits_of(*dims);
-  if (bits != 4 && !gemv_path(*dims, T))
-    return fail(MOE_EUNSUPPORTED, "%d-bit codes run on the GEMV path only (1..%d tokens per call, top_k * d_ff + "
-                "d_ff_shared <= %d, d_ff and d_ff_shared <= %d); T = %d", bits, kGemvMaxT, kGemvMaxH, kGemvMaxFF, T);
   if (int rc = check_ffn(routed, "routed", bits)) return rc;
   if (dims->d_ff_shared > 0) {
     if (int rc = check_ffn(shared, "shared", bits)) return rc;
@@ -445,7 +442,6 @@ int moe_debug_grouped_gemm(const moe_dims* dims, int32_t T, int32_t which, const
   if (int rc = check_dims(dims, T)) return rc;
   if (which != 0 && which != 1) return fail(MOE_EINVAL, "which = %d must be 0 (gate/up) or 1 (down)", which);
   if (T == 0) return MOE_OK;
-  if (bits_of(*dims) != 4) return fail(MOE_EUNSUPPORTED, "the grouped GEMM takes 4-bit codes");
   if (int rc = check_routing(routing)) return rc;
   // x (which = 0) or h (which = 1) stands in for x in the argument checks
   if (int rc = check_layer_args(dims, T, a, nullptr, false, routed, shared, reinterpret_cast<const uint16_t*>(out),

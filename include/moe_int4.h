@@ -88,7 +88,8 @@ typedef struct {
   int32_t code_bits;    /* bits per expert weight code: 4 (0 also means 4), or the 3- and 2-bit variant
                            ("Squeezing a 26B diffusion LLM onto a Mac", "The physics ceiling: why 300+
                            tok/s is blocked", which names 2-3 bit experts as the lever that cuts the
-                           streamed bytes); 3 and 2 run on the GEMV path only (see moe_expert_ffn) */
+                           streamed bytes); every width runs on both the GEMV and the grouped-GEMM
+                           path */
 } moe_dims;
 
 /* One projection of every expert (n matrices [out][in]). */

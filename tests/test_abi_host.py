@@ -189,13 +189,19 @@ def test_code_bits_validation():
 
     assert _layer_call(dims(5), 4, f) == moe.MOE_EUNSUPPORTED
     assert _layer_call(dims(1), 4, f) == moe.MOE_EUNSUPPORTED
-    assert _layer_call(dims(3), 33, f) == moe.MOE_EUNSUPPORTED      # 3- and 2-bit codes: GEMV path only
-    assert "GEMV path only" in L.moe_last_error().decode()
-    assert _layer_call(dims(2, k=16, I=2048), 1, f) == moe.MOE_EUNSUPPORTED  # too much h for the GEMV path
+    # 3- and 2-bit codes on the grouped-GEMM path (T > 32, or too much h for the GEMV path): the
+    # width passes and the checks go on to y
+    assert _layer_call(dims(3), 33, f, y=None) == moe.MOE_EINVAL
+    assert "y NULL" in L.moe_last_error().decode()
+    assert _layer_call(dims(2, k=16, I=2048), 1, f, y=None) == moe.MOE_EINVAL
+    assert "y NULL" in L.moe_last_error().decode()
     bad = _ffn(f)
     bad.gate.codes = f() + 4                                         # 4-byte aligned: enough for 3-bit codes only
     assert _layer_call(dims(2), 4, f, routed=bad) == moe.MOE_EINVAL
     assert _layer_call(dims(4), 4, f, routed=bad) == moe.MOE_EINVAL
+    bad.gate.codes = f() + 8                                         # 2-bit codes move as 16-byte chunks
+    assert _layer_call(dims(2), 4, f, routed=bad) == moe.MOE_EINVAL
+    bad.gate.codes = f() + 4
     assert _layer_call(dims(3), 4, f, routed=bad, y=None) == moe.MOE_EINVAL  # the codes passed; y did not
     assert "y NULL" in L.moe_last_error().decode()
     q = moe.Q4(f() + 4, f(), f())
@@ -242,5 +248,7 @@ def test_noalloc_and_debug_gemm_validation():
     assert dg(0, a=f() + 2) == moe.MOE_EINVAL
     assert dg(1, ws_bytes=100) == moe.MOE_EWORKSPACE
     d3 = _dims()
-    d3.code_bits = 3
+    d3.code_bits = 3                                                 # 3-bit codes pass; the checks go on
+    assert dg(0, dims=d3, out2=None) == moe.MOE_EINVAL
+    d3.code_bits = 5
     assert dg(0, dims=d3) == moe.MOE_EUNSUPPORTED

@@ -9,8 +9,9 @@ layer's grouped path, with fp32 results written before the activation).
    row or shared-row offset changes at least one value.
 2. One-hot activations over the workload's own weights: the gate/up product of row e_c is the
    weight column c as the GEMM reconstructs it (scale * code + bias in fp32). For these weights
-   (bias = -8 * scale) that is exact, so rounded to bf16 it must equal the oracle's dequantised
-   weights bit for bit: the dequantisation export of the grouped path.
+   (bias = -2^(b-1) * scale) that is exact, so rounded to bf16 it must equal the oracle's
+   dequantised weights bit for bit: the dequantisation export of the grouped path, for 4-, 3- and
+   2-bit codes.
 
 Equality is of values: -0 and +0 compare equal (the sign of an exact zero depends on the order).
 """
@@ -48,29 +49,38 @@ def _assert_exact(got: np.ndarray, want: np.ndarray, what: str):
                           f"{got[tuple(np.argwhere(bad)[0])]} vs {want[tuple(np.argwhere(bad)[0])]}"
 
 
-# (T, d, E, k, I, Is, zipf): the prefill shape; a K tail (d and I = 64 mod 128) with a shared
-# expert of another size; groups of ~150 rows; the skewed long shape (groups of up to ~250 rows);
-# a down reduction of 13 groups (one output column block per work item, odd group count)
+# (T, d, E, k, I, Is, zipf, bits): the prefill shape; a K tail (d and I = 64 mod 128) with a
+# shared expert of another size; groups of ~150 rows; the skewed long shape (groups of up to ~250
+# rows); a down reduction of 13 groups (one output column block per work item, odd group count);
+# then the 3- and 2-bit codes on the prefill and diffusion shapes and on the ragged ones
 CASES = [
-    (512, 2048, 256, 8, 512, 512, False),
-    (100, 192, 8, 3, 192, 64, False),
-    (300, 256, 4, 2, 128, 128, False),
-    (256, 2048, 256, 8, 512, 512, True),
-    (40, 256, 8, 2, 832, 0, False),
+    (512, 2048, 256, 8, 512, 512, False, 4),
+    (100, 192, 8, 3, 192, 64, False, 4),
+    (300, 256, 4, 2, 128, 128, False, 4),
+    (256, 2048, 256, 8, 512, 512, True, 4),
+    (40, 256, 8, 2, 832, 0, False, 4),
+    (512, 2048, 256, 8, 512, 512, False, 3),
+    (256, 2048, 128, 8, 768, 0, False, 3),
+    (256, 2048, 128, 8, 768, 0, False, 2),
+    (100, 192, 8, 3, 192, 64, False, 3),
+    (100, 192, 8, 3, 192, 64, False, 2),
+    (300, 256, 4, 2, 128, 128, False, 2),
+    (40, 256, 8, 2, 832, 0, False, 3),
+    (40, 320, 8, 2, 832, 0, False, 2),
 ]
 
 
-def _setup(T, d, E, k, I, Is, zipf):
-    L = gen.exact_layer(T, d, E, k, I, Is, seed=T + d + I, zipf=zipf)
+def _setup(T, d, E, k, I, Is, zipf, bits):
+    L = gen.exact_layer(T, d, E, k, I, Is, seed=T + d + I, zipf=zipf, bits=bits)
     ref = _oracle_routing(L, k)
     r = moe.route(bf16_dev(L["x"]), f32_dev(L["w_router"]), k, I, Is, f32_dev(L["logit_bias"]))
     check_routing(r, ref, "exact layer routing")
     return L, ref, r
 
 
-@pytest.mark.parametrize("T,d,E,k,I,Is,zipf", CASES)
-def test_gateup_preactivations_bit_exact(T, d, E, k, I, Is, zipf):
-    L, ref, r = _setup(T, d, E, k, I, Is, zipf)
+@pytest.mark.parametrize("T,d,E,k,I,Is,zipf,bits", CASES)
+def test_gateup_preactivations_bit_exact(T, d, E, k, I, Is, zipf, bits):
+    L, ref, r = _setup(T, d, E, k, I, Is, zipf, bits)
     if zipf:
         assert ref["counts"].max() > 128, "the skewed case must hold a group of more than 128 rows"
     g, u = moe.debug_grouped_gemm(0, bf16_dev(L["x"]), r, ffn_dev(L["routed"]), ffn_dev(L["shared"]))
@@ -85,9 +95,9 @@ def test_gateup_preactivations_bit_exact(T, d, E, k, I, Is, zipf):
         _assert_exact(u[P * I:].reshape(T, Is), wus, "shared up")
 
 
-@pytest.mark.parametrize("T,d,E,k,I,Is,zipf", CASES)
-def test_down_rows_bit_exact(T, d, E, k, I, Is, zipf):
-    L, ref, r = _setup(T, d, E, k, I, Is, zipf)
+@pytest.mark.parametrize("T,d,E,k,I,Is,zipf,bits", CASES)
+def test_down_rows_bit_exact(T, d, E, k, I, Is, zipf, bits):
+    L, ref, r = _setup(T, d, E, k, I, Is, zipf, bits)
     P = T * k
     h = gen.small_ints_bf16(gen.key(T, d, 77), P * I).reshape(P, I)
     hs = gen.small_ints_bf16(gen.key(T, d, 78), T * Is).reshape(T, Is) if Is else None
@@ -114,22 +124,23 @@ def _onehot_routing(experts, rows_per_expert, E):
 
 
 def _exact_weights(p, e):
-    """s * q + b in float64 (exact here), numpy nibbles: [out][in]."""
-    c = p["codes"][e].astype(np.int64)
-    q = np.empty((c.shape[0], 2 * c.shape[1]), np.int64)
-    q[:, 0::2] = c & 15
-    q[:, 1::2] = c >> 4
+    """s * q + b in float64 (exact here), codes unpacked from each row's little-endian bit stream
+    with numpy: [out][in]."""
+    bits = p.get("bits", 4)
+    st = np.unpackbits(np.ascontiguousarray(p["codes"][e], np.uint8), axis=-1, bitorder="little").astype(np.int64)
+    q = (st.reshape(p["codes"].shape[1], -1, bits) << np.arange(bits, dtype=np.int64)).sum(axis=-1)
     s = np.repeat(oracle.bf16_to_f32(p["scales"][e]).astype(np.float64), 64, axis=1)
     b = np.repeat(oracle.bf16_to_f32(p["biases"][e]).astype(np.float64), 64, axis=1)
     return s * q + b
 
 
-def test_dequant_export_through_the_grouped_gemm():
-    """Workload weights (prefill layer 0), experts 0, 137 and 255: the GEMMs' reconstruction of every
-    gate, up and down weight, rounded to bf16, equals the oracle's dequantised weight."""
-    w = gen.WORKLOADS["prefill"]
+@pytest.mark.parametrize("wname,experts", [("prefill", [0, 137, 255]), ("prefill3", [0, 77, 255]),
+                                          ("diffusion2", [0, 64, 127])])
+def test_dequant_export_through_the_grouped_gemm(wname, experts):
+    """Workload weights (layer 0), three experts: the GEMMs' reconstruction of every gate, up and
+    down weight, rounded to bf16, equals the oracle's dequantised weight (4-, 3- and 2-bit codes)."""
+    w = gen.WORKLOADS[wname]
     W = gen.expert_weights(w, 0)
-    experts = [0, 137, 255]
     routed = ffn_dev(W)
     d, I, E = w.d, w.I, w.E
     # gate/up: token t is the one-hot row of input t % d
@@ -149,6 +160,6 @@ def test_dequant_export_through_the_grouped_gemm():
     for n, e in enumerate(experts):
         for name, got in (("gate", g[n].T), ("up", u[n].T), ("down", y[n].T)):
             p = W[name]
-            want_bits = oracle.dequant(p["codes"][e], p["scales"][e], p["biases"][e])
+            want_bits = oracle.dequant(p["codes"][e], p["scales"][e], p["biases"][e], w.bits)
             assert (oracle.round_bf16(got) == want_bits).all(), f"expert {e} {name}: bf16 weights differ"
             assert (got.astype(np.float64) == _exact_weights(p, e)).all(), f"expert {e} {name}: fp32 weights differ"

@@ -231,22 +231,28 @@ def test_lowbit_dequant_bit_exact(bits):
 
 
 @pytest.mark.parametrize("name,layer", [("tiny3", 0), ("tiny2", 0), ("decode3", 0), ("decode3", 17), ("decode2", 5),
-                                        ("m32_3", 1), ("m32_2", 3)])
+                                        ("m32_3", 1), ("m32_2", 3), ("prefill3", 0), ("diffusion3", 0),
+                                        ("diffusion3", 29), ("diffusion2", 0), ("diffusion2", 17)])
 def test_forward_lowbit_workloads(name, layer):
+    """GEMV path (up to 32 tokens) and grouped-GEMM path (prefill- and diffusion-size calls)."""
     _forward_check(gen.WORKLOADS[name], layer=layer)
 
 
 @pytest.mark.parametrize("T,d,E,k,I,Is,bits", [(1, 192, 8, 2, 192, 64, 3), (5, 256, 16, 4, 128, 128, 2),
                                                (3, 64, 4, 2, 64, 0, 3), (17, 320, 8, 3, 64, 192, 2),
                                                (32, 128, 4, 2, 256, 64, 3), (1, 2112, 4, 2, 128, 64, 2),
-                                               (2, 4096, 1024, 16, 64, 64, 3), (9, 256, 300, 16, 64, 0, 2)])
+                                               (2, 4096, 1024, 16, 64, 64, 3), (9, 256, 300, 16, 64, 0, 2),
+                                               (64, 192, 8, 3, 192, 64, 3), (100, 320, 16, 4, 128, 128, 2),
+                                               (33, 256, 8, 2, 832, 0, 3), (48, 2112, 4, 2, 128, 64, 2),
+                                               (40, 4096, 300, 16, 64, 64, 3), (200, 128, 3, 2, 320, 0, 2)])
 def test_forward_lowbit_shapes(T, d, E, k, I, Is, bits):
     """Ragged K (d = 64 mod 128), no shared expert, d above 2048 (several segments per lane), the
-    largest top-k over 1024 experts, an expert count that is not a multiple of 64."""
+    largest top-k over 1024 experts, an expert count that is not a multiple of 64; calls of more
+    than 32 tokens take the grouped GEMM (groups of more than 32 rows in the last two)."""
     _forward_check(_custom(T, d, E, k, I, Is, seed=T + d + bits, bits=bits))
 
 
-@pytest.mark.parametrize("name", ["decode3", "m32_2"])
+@pytest.mark.parametrize("name", ["decode3", "m32_2", "prefill3", "diffusion2"])
 def test_lowbit_route_then_expert_ffn_equals_forward(name):
     w = gen.WORKLOADS[name]
     L = gen.layer(w, 2)

@@ -660,13 +660,19 @@ def test_vocab_topk_full_size_row_against_lexsort():
 
 
 # ------------------------------------------------------------------ the two grouped products alone
+def _numpy_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[out][in * bits / 8] bytes -> [out][in] codes: each row a little-endian bit stream (numpy's
+    unpackbits, least significant bit first), code i = the bits [bits i, bits i + bits)."""
+    st = np.unpackbits(np.ascontiguousarray(codes, np.uint8), axis=-1, bitorder="little").astype(np.int64)
+    st = st.reshape(codes.shape[0], -1, bits)
+    return (st << np.arange(bits, dtype=np.int64)).sum(axis=-1)
+
+
 def _numpy_weights(p, mat):
-    """Independent dequantisation of an exact-arithmetic projection (numpy nibbles, float64):
-    w = s * q + b with the even input in the low nibble; exact in float64 and in bf16 here."""
-    c = p["codes"][mat].astype(np.int64)
-    q = np.empty((c.shape[0], 2 * c.shape[1]), np.int64)
-    q[:, 0::2] = c & 15
-    q[:, 1::2] = c >> 4
+    """Independent dequantisation of an exact-arithmetic projection (numpy bit unpacking, float64):
+    w = s * q + b, codes a little-endian bit stream per row (for 4 bits the even input in the low
+    nibble); exact in float64 and in bf16 here."""
+    q = _numpy_codes(p["codes"][mat], p.get("bits", 4))
     s = np.repeat(oracle.bf16_to_f32(p["scales"][mat]).astype(np.float64), 64, axis=1)
     b = np.repeat(oracle.bf16_to_f32(p["biases"][mat]).astype(np.float64), 64, axis=1)
     return s * q + b
@@ -677,11 +683,12 @@ def _routing_of(L, k):
     return oracle.route_meta(ids, L["w_router"].shape[1], L["shared"] is not None)
 
 
-@pytest.mark.parametrize("T,d,E,k,I,Is", [(9, 192, 4, 2, 128, 64), (6, 128, 3, 3, 64, 0)])
-def test_gateup_preact_exact_against_numpy_matmul(T, d, E, k, I, Is):
+@pytest.mark.parametrize("T,d,E,k,I,Is,bits", [(9, 192, 4, 2, 128, 64, 4), (6, 128, 3, 3, 64, 0, 4),
+                                               (9, 192, 4, 2, 128, 64, 3), (6, 128, 3, 3, 64, 64, 2)])
+def test_gateup_preact_exact_against_numpy_matmul(T, d, E, k, I, Is, bits):
     """Exact-arithmetic inputs: the oracle's pre-activations equal a float64 matmul of numpy-made
     weights row for row (token of each grouped row, expert of each group, gate vs up, shared last)."""
-    L = gen.exact_layer(T, d, E, k, I, Is, seed=T + d)
+    L = gen.exact_layer(T, d, E, k, I, Is, seed=T + d, bits=bits)
     m = _routing_of(L, k)
     g, u, gs, us = oracle.gateup_preact(L["x"], L["routed"], L["shared"], k, m["offsets"], m["sorted_token"])
     xf = oracle.bf16_to_f32(L["x"]).astype(np.float64)
@@ -717,9 +724,10 @@ def test_gateup_preact_gives_the_forward_layers_h():
         np.testing.assert_allclose(g[r0:r1], xf[out["sorted_token"][r0:r1]] @ W.T, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("T,d,E,k,I,Is", [(9, 192, 4, 2, 128, 64), (6, 128, 3, 3, 192, 0)])
-def test_down_rows_exact_against_numpy_matmul(T, d, E, k, I, Is):
-    L = gen.exact_layer(T, d, E, k, I, Is, seed=3 * T + d)
+@pytest.mark.parametrize("T,d,E,k,I,Is,bits", [(9, 192, 4, 2, 128, 64, 4), (6, 128, 3, 3, 192, 0, 4),
+                                               (9, 192, 4, 2, 128, 64, 2), (6, 128, 3, 3, 192, 64, 3)])
+def test_down_rows_exact_against_numpy_matmul(T, d, E, k, I, Is, bits):
+    L = gen.exact_layer(T, d, E, k, I, Is, seed=3 * T + d, bits=bits)
     m = _routing_of(L, k)
     P = T * k
     h = gen.small_ints_bf16(gen.key(7, 0, 1), P * I).reshape(P, I)

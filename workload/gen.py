@@ -160,7 +160,7 @@ class Workload:
 
     @property
     def shared_bytes(self) -> int:
-        return 3 * self.d * self.Is // 2 + 3 * 2 * 2 * self.d * self.Is // GROUP
+        return 3 * self.d * self.Is * self.bits // 8 + 3 * 2 * 2 * self.d * self.Is // GROUP
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -189,6 +189,11 @@ WORKLOADS: Dict[str, Workload] = {
     "m32_2": Workload("m32_2", 32, 2048, 256, 8, 512, 512, 0.02, 40, 32, bits=2),
     "tiny3": Workload("tiny3", 8, 256, 16, 4, 128, 128, 0.05, 1, 8, bits=3),
     "tiny2": Workload("tiny2", 8, 256, 16, 4, 128, 128, 0.05, 1, 8, bits=2),
+    # the same variants on the grouped-GEMM path: the diffusion canvas at 3 and 2 bits, and a
+    # prefill-size 3-bit call
+    "diffusion3": Workload("diffusion3", 256, 2048, 128, 8, 768, 0, 0.02, 30, 256, bits=3),
+    "diffusion2": Workload("diffusion2", 256, 2048, 128, 8, 768, 0, 0.02, 30, 256, bits=2),
+    "prefill3": Workload("prefill3", 512, 2048, 256, 8, 512, 512, 0.02, 1, 512, bits=3),
 }
 
 
@@ -307,25 +312,30 @@ def small_ints_bf16(k: int, n: int, lo: int = -4, hi: int = 4, start: int = 0) -
     return _f32_bits_to_bf16(r.astype(np.float32))
 
 
-def exact_proj(seed: int, layer: int, tensor: int, n_mat: int, out_dim: int, in_dim: int) -> dict:
+def exact_proj(seed: int, layer: int, tensor: int, n_mat: int, out_dim: int, in_dim: int, bits: int = 4) -> dict:
+    """Codes of `bits` bits (uniform random bytes of the rows' bit streams), exact scales/biases."""
     n_sb = n_mat * out_dim * in_dim // GROUP
-    codes = rand_bytes(key(seed, layer, T_EXACT + 3 * tensor), n_mat * out_dim * in_dim // 2)
+    codes = rand_bytes(key(seed, layer, T_EXACT + 3 * tensor), n_mat * out_dim * in_dim * bits // 8)
     sb = rand_bytes(key(seed, layer, T_EXACT + 3 * tensor + 1), 2 * n_sb).reshape(n_sb, 2).astype(np.int32)
     m = 3 + sb[:, 0] % 5
     c = sb[:, 1] % 17
     scale = np.ldexp(np.float32(1.0), -m).astype(np.float32)
-    return {"codes": codes.reshape(n_mat, out_dim, in_dim // 2),
-            "scales": _f32_bits_to_bf16(scale).reshape(n_mat, out_dim, in_dim // GROUP),
-            "biases": _f32_bits_to_bf16((-c * scale).astype(np.float32)).reshape(n_mat, out_dim, in_dim // GROUP)}
+    out = {"codes": codes.reshape(n_mat, out_dim, in_dim * bits // 8),
+           "scales": _f32_bits_to_bf16(scale).reshape(n_mat, out_dim, in_dim // GROUP),
+           "biases": _f32_bits_to_bf16((-c * scale).astype(np.float32)).reshape(n_mat, out_dim, in_dim // GROUP)}
+    if bits != 4:
+        out["bits"] = bits
+    return out
 
 
 def exact_layer(T: int, d: int, E: int, k: int, I: int, Is: int, seed: int = 0, layer: int = 0,
-                router_sigma: float = 0.02, zipf: bool = False) -> dict:
+                router_sigma: float = 0.02, zipf: bool = False, bits: int = 4) -> dict:
     """A layer (as layer()) plus its activations "x", all with exact-arithmetic values; the router
     is N(0, router_sigma^2) in fp32, with the skewed workload's logit bias when zipf is set."""
     def ffn(base, n, Ie):
-        return {"gate": exact_proj(seed, layer, base, n, Ie, d), "up": exact_proj(seed, layer, base + 1, n, Ie, d),
-                "down": exact_proj(seed, layer, base + 2, n, d, Ie)}
+        return {"gate": exact_proj(seed, layer, base, n, Ie, d, bits),
+                "up": exact_proj(seed, layer, base + 1, n, Ie, d, bits),
+                "down": exact_proj(seed, layer, base + 2, n, d, Ie, bits)}
     return {
         "x": small_ints_bf16(key(seed, layer, T_EXACT + 99), T * d).reshape(T, d),
         "w_router": normal_f32(key(seed, layer, T_EXACT + 98), d * E, router_sigma).reshape(d, E),
