@@ -22,10 +22,17 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES: the fixed scratch
 
 
 class MoeError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, detail: Optional[str] = None):
         L = lib()
-        super().__init__(f"{where}: {L.moe_status_str(status).decode()} ({L.moe_last_error().decode()})")
+        detail = L.moe_last_error().decode() if detail is None else detail
+        super().__init__(f"{where}: {L.moe_status_str(status).decode()} ({detail})")
         self.status = status
+
+
+def _shape_error(where: str, detail: str) -> MoeError:
+    """A shape mismatch caught before the library is called: the C ABI sees only pointers, so a
+    tensor of the wrong size would become out-of-bounds device accesses."""
+    return MoeError(MOE_EINVAL, where, detail)
 
 
 class Dims(ctypes.Structure):
@@ -158,6 +165,19 @@ class QuantFFN:
             raise ValueError("gate, up and down must use the same code width")
         return self.gate.bits
 
+    def check(self, d: int, what: str) -> None:
+        """Every array's shape against (n experts, d_ff, d_model = d, code width)."""
+        n, I, b = self.n_experts, self.d_ff, self.bits
+        for name, p, out_dim, in_dim in (("gate", self.gate, I, d), ("up", self.up, I, d), ("down", self.down, d, I)):
+            if in_dim % 64 or (in_dim * b) % 8:
+                raise _shape_error(what, f"{name}: input dimension {in_dim} is not a multiple of 64")
+            want = {"codes": (n, out_dim, in_dim * b // 8), "scales": (n, out_dim, in_dim // 64),
+                    "biases": (n, out_dim, in_dim // 64)}
+            for arr, shape in want.items():
+                got = tuple(getattr(p, arr).shape)
+                if got != shape:
+                    raise _shape_error(what, f"{name}.{arr} has shape {got}, expected {shape}")
+
 
 def _bits_of(routed: QuantFFN, shared: Optional[QuantFFN]) -> int:
     if shared is not None and shared.bits != routed.bits:
@@ -165,9 +185,30 @@ def _bits_of(routed: QuantFFN, shared: Optional[QuantFFN]) -> int:
     return routed.bits
 
 
-def _dims_for(x: torch.Tensor, routed: QuantFFN, shared: Optional[QuantFFN], k: int) -> Dims:
-    return make_dims(x.shape[1], routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff,
+def _dims_for(d: int, routed: QuantFFN, shared: Optional[QuantFFN], k: int, where: str) -> Dims:
+    """The dims of a layer of d_model = d, with every expert array's shape checked."""
+    routed.check(d, where + " (routed)")
+    if shared is not None:
+        if shared.n_experts != 1:
+            raise _shape_error(where, f"the shared expert has {shared.n_experts} matrices, expected 1")
+        shared.check(d, where + " (shared)")
+    return make_dims(d, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff,
                      _bits_of(routed, shared))
+
+
+def _check_routing(r: Dict[str, torch.Tensor], dims: Dims, T: int, where: str) -> None:
+    """Every routing array's size against (T, k, E) and the block map's bound."""
+    k, E = dims.top_k, dims.n_experts
+    want = {"topk_ids": T * k, "topk_w": T * k, "counts": E, "offsets": E + 1, "sorted_token": T * k,
+            "inv_pos": T * k, "tiles": 3 * max(max_tiles(dims, T), 1), "n_tiles": 1}
+    for name, n in want.items():
+        if name not in r:
+            raise _shape_error(where, f"routing has no {name}")
+        got = r[name].numel()
+        if got < n if name == "tiles" else got != n:
+            raise _shape_error(where, f"routing {name} holds {got} values, expected {'at least ' if name == 'tiles' else ''}{n}")
+    if tuple(r["topk_ids"].shape) != (T, k) or tuple(r["topk_w"].shape) != (T, k):
+        raise _shape_error(where, f"topk_ids / topk_w must be [{T}][{k}]")
 
 
 def max_tiles(dims: Dims, T: int) -> int:
@@ -205,8 +246,12 @@ def _routing_struct(r: Dict[str, torch.Tensor], device) -> Routing:
 def route(x: torch.Tensor, w_router: torch.Tensor, k: int, d_ff: int, d_ff_shared: int,
           logit_bias: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """moe_route: top-k, gate weights and the routing metadata of T tokens."""
+    if x.dim() != 2 or w_router.dim() != 2 or w_router.shape[0] != x.shape[1]:
+        raise _shape_error("moe_route", f"x {tuple(x.shape)} and w_router {tuple(w_router.shape)} must be [T][d] and [d][E]")
     T, d = x.shape
     dims = make_dims(d, w_router.shape[1], k, d_ff, d_ff_shared)
+    if logit_bias is not None and logit_bias.numel() != dims.n_experts:
+        raise _shape_error("moe_route", f"logit_bias holds {logit_bias.numel()} values, expected {dims.n_experts}")
     dev = x.device
     ws = new_workspace(dims, T, dev) if ws is None else ws
     r = new_routing(dims, T, dev)
@@ -221,12 +266,17 @@ def route(x: torch.Tensor, w_router: torch.Tensor, k: int, d_ff: int, d_ff_share
 def expert_ffn(x: torch.Tensor, routing: Dict[str, torch.Tensor], routed: QuantFFN, shared: Optional[QuantFFN],
                ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_expert_ffn: the expert FFN of routed tokens (GEMV path for calls of up to 32 tokens, grouped GEMM above)."""
+    if x.dim() != 2:
+        raise _shape_error("moe_expert_ffn", "x must be [T][d]")
     T, d = x.shape
-    k = routing["topk_ids"].shape[1]
-    dims = _dims_for(x, routed, shared, k)
+    k = routing["topk_ids"].shape[1] if routing["topk_ids"].dim() == 2 else -1
+    dims = _dims_for(d, routed, shared, k, "moe_expert_ffn")
+    _check_routing(routing, dims, T, "moe_expert_ffn")
     dev = x.device
     ws = new_workspace(dims, T, dev) if ws is None else ws
     y = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if y is None else y
+    if tuple(y.shape) != (T, d):
+        raise _shape_error("moe_expert_ffn", f"y has shape {tuple(y.shape)}, expected {(T, d)}")
     rs = _routing_struct(routing, dev)
     rf = routed.struct(dev)
     sf = shared.struct(dev) if shared is not None else None
@@ -245,10 +295,11 @@ class Layer:
                  logit_bias: Optional[torch.Tensor] = None):
         self.dev = w_router.device
         self.w_router, self.routed, self.shared, self.k, self.logit_bias = w_router, routed, shared, k, logit_bias
-        self.dims = make_dims(routed.d_model, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff,
-                              _bits_of(routed, shared))
+        self.dims = _dims_for(routed.d_model, routed, shared, k, "moe_forward_layer")
         if w_router.shape != (self.dims.d_model, self.dims.n_experts):
-            raise ValueError(f"w_router shape {tuple(w_router.shape)} does not match the experts")
+            raise _shape_error("moe_forward_layer", f"w_router shape {tuple(w_router.shape)} does not match the experts")
+        if logit_bias is not None and logit_bias.numel() != self.dims.n_experts:
+            raise _shape_error("moe_forward_layer", f"logit_bias holds {logit_bias.numel()} values")
         self._wr = _ptr(w_router, torch.float32, "w_router", self.dev)
         self._bias = _ptr(logit_bias, torch.float32, "logit_bias", self.dev)
         self._rf = routed.struct(self.dev)
@@ -257,7 +308,7 @@ class Layer:
     def _io(self, x: torch.Tensor, y: torch.Tensor):
         T = x.shape[0]
         if x.dim() != 2 or x.shape[1] != self.dims.d_model or y.shape != x.shape:
-            raise ValueError("x / y shape mismatch")
+            raise _shape_error("moe_forward_layer", f"x {tuple(x.shape)} / y {tuple(y.shape)} must both be [T][{self.dims.d_model}]")
         return (ctypes.byref(self.dims), T, _ptr(x, torch.bfloat16, "x", self.dev), self._wr, self._bias,
                 ctypes.byref(self._rf), ctypes.byref(self._sf) if self._sf is not None else None,
                 _ptr(y, torch.bfloat16, "y", self.dev))
@@ -303,6 +354,9 @@ def debug_dequant(p: QProj) -> torch.Tensor:
     codes = p.codes
     in_dim = codes.shape[-1] * 8 // p.bits
     rows = codes.numel() // codes.shape[-1]
+    if p.scales.shape != codes.shape[:-1] + (in_dim // 64,) or p.biases.shape != p.scales.shape:
+        raise _shape_error("moe_debug_dequant", f"scales {tuple(p.scales.shape)} / biases {tuple(p.biases.shape)} do not "
+                           f"match codes {tuple(codes.shape)}")
     dev = codes.device
     out = torch.empty(tuple(codes.shape[:-1]) + (in_dim,), dtype=torch.bfloat16, device=dev)
     q = p.struct(dev)
@@ -321,7 +375,8 @@ def debug_grouped_gemm(which: int, a: torch.Tensor, routing: Dict[str, torch.Ten
     T = routing["topk_ids"].shape[0]
     dev = a.device
     d = routed.d_model
-    dims = make_dims(d, routed.n_experts, k, routed.d_ff, 0 if shared is None else shared.d_ff, _bits_of(routed, shared))
+    dims = _dims_for(d, routed, shared, k, "moe_debug_grouped_gemm")
+    _check_routing(routing, dims, T, "moe_debug_grouped_gemm")
     P, I, Is = T * k, dims.d_ff, dims.d_ff_shared
     if which == 0:
         if tuple(a.shape) != (T, d):

@@ -31,7 +31,7 @@
  *     moe_last_error() gives a per-thread message for the last failure. Asynchronous device
  *     faults surface at the caller's next synchronisation, as for any HIP launch.
  *   - Determinism. The same inputs give bit-identical outputs on every call (atomics are
- *     used only for counts and for an arrival counter, never for floating-point sums).
+ *     used only for integer counts, never for floating-point sums).
  *   - Workspace. `ws` is device scratch of at least moe_workspace_bytes() bytes; its contents
  *     on entry do not matter.
  *   - Concurrency. No global mutable state. Calls on different streams with different
@@ -140,7 +140,11 @@ int32_t moe_max_tiles(const moe_dims* dims, int32_t T);
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t T);
 
 /*
- * Router, top-k and routing metadata (steps on the GPU, no host sync):
+ * Router, top-k and routing metadata (steps on the GPU, no host sync). The router scores every
+ * expert and keeps the top k ("Perplexity's Lily Beats MLX-LM on MacBook M5. Because It Only Runs
+ * One Model.", section "Why Qwen3.6-35B-A3B is a weird workload"); the grouped rows need a
+ * histogram, prefix scan, scatter and block map after every top-k selection, kept on the GPU with
+ * no CPU round trip (same blog, section "Prefill: keep routing on the GPU, dequantize in flight").
  *   logits[t][e] = sum_i x[t][i] * w_router[i][e] (+ logit_bias[e]), in fp32 in a fixed order:
  *   the input dimension is cut into chunks of 64, each chunk reduced by an fma chain in
  *   ascending i, the chunk partials added in ascending order, the bias added last;
@@ -152,7 +156,13 @@ int moe_route(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w
               void* stream);
 
 /*
- * Expert FFN of routed tokens given their routing (as written by moe_route):
+ * Expert FFN of routed tokens given their routing (as written by moe_route). Prefill is a grouped
+ * GEMM that reconstructs the 4-bit weights tile by tile in on-chip memory with fp32 accumulation
+ * and bf16 output, never expanding them in memory; batch-1 decode is a bandwidth-bound GEMV
+ * ("Perplexity's Lily Beats MLX-LM on MacBook M5. Because It Only Runs One Model.", sections
+ * "Prefill and decode are different problems", "Prefill: keep routing on the GPU, dequantize in
+ * flight" and "Decode: minimize bytes per token"; codes of 3 and 2 bits: "Squeezing a 26B
+ * diffusion LLM onto a Mac", section "The physics ceiling: why 300+ tok/s is blocked").
  *   y[t] = bf16( sum_j topk_w[t][j] * FFN_{topk_ids[t][j]}(x[t]) + FFN_shared(x[t]) ),
  *   FFN_e(x) = h Wd_e^T with h = bf16( silu(x Wg_e^T) * (x Wu_e^T) ), each weight taken as
  *   scale * code + bias inside the dot products (never expanded in memory), fp32 accumulation.
@@ -177,9 +187,13 @@ int moe_forward_layer_noalloc(const moe_dims* dims, int32_t T, const uint16_t* x
                               const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared,
                               uint16_t* y, void* stream);
 
-/* moe_route followed by moe_expert_ffn, with the routing arrays carved from `ws`. On the GEMV
- * path the block-map steps are skipped (it does not read them), the top-k is taken inside the
- * gate/up kernel, and only topk_ids/topk_w of the carved routing are written. */
+/* The whole routed MoE FFN layer: top-k of the routed experts plus the shared expert, weighted by
+ * the renormalised gate scores ("Perplexity's Lily Beats MLX-LM on MacBook M5. Because It Only
+ * Runs One Model.", section "Why Qwen3.6-35B-A3B is a weird workload"; "Perplexity builds a custom
+ * engine for Qwen on M5 Macs"), as moe_route followed by moe_expert_ffn, with the routing arrays
+ * carved from `ws`. On the GEMV path the block-map steps are skipped (it does not read them), the
+ * top-k is taken inside the gate/up kernel, and only topk_ids/topk_w of the carved routing are
+ * written. */
 int moe_forward_layer(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
                       const float* logit_bias, const moe_ffn_q4* routed, const moe_ffn_q4* shared,
                       uint16_t* y, void* ws, size_t ws_bytes, void* stream);

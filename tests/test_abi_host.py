@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from conftest import ROOT
 
@@ -252,3 +253,72 @@ def test_noalloc_and_debug_gemm_validation():
     assert dg(0, dims=d3, out2=None) == moe.MOE_EINVAL
     d3.code_bits = 5
     assert dg(0, dims=d3) == moe.MOE_EUNSUPPORTED
+
+
+def _cpu_ffn(n, I, d, bits=4):
+    def proj(out_dim, in_dim):
+        return moe.QProj(torch.zeros((n, out_dim, in_dim * bits // 8), dtype=torch.uint8),
+                         torch.zeros((n, out_dim, in_dim // 64), dtype=torch.bfloat16),
+                         torch.zeros((n, out_dim, in_dim // 64), dtype=torch.bfloat16), bits)
+    return moe.QuantFFN(proj(I, d), proj(I, d), proj(d, I))
+
+
+def _cpu_routing(dims, T):
+    k, E = dims.top_k, dims.n_experts
+    i32 = dict(dtype=torch.int32)
+    return {"topk_ids": torch.zeros((T, k), **i32), "topk_w": torch.zeros((T, k), dtype=torch.float32),
+            "counts": torch.zeros(E, **i32), "offsets": torch.zeros(E + 1, **i32),
+            "sorted_token": torch.zeros(T * k, **i32), "inv_pos": torch.zeros((T, k), **i32),
+            "tiles": torch.zeros((moe.max_tiles(dims, T), 3), **i32), "n_tiles": torch.zeros(1, **i32)}
+
+
+def _refused(fn, *a, **kw):
+    with pytest.raises(moe.MoeError) as ei:
+        fn(*a, **kw)
+    assert ei.value.status == moe.MOE_EINVAL
+    return str(ei.value)
+
+
+def test_binding_checks_shapes_before_the_library():
+    """moe.py refuses tensors whose shapes do not match the layer (the C ABI sees only pointers,
+    where a wrong size would turn into out-of-bounds device reads), before any pointer is taken."""
+    T, d, E, k, I, Is = 40, 128, 8, 2, 64, 128
+    routed, shared = _cpu_ffn(E, I, d), _cpu_ffn(1, Is, d)
+    dims = moe.make_dims(d, E, k, I, Is)
+    x = torch.zeros((T, d), dtype=torch.bfloat16)
+    r = _cpu_routing(dims, T)
+    # expert arrays
+    bad = _cpu_ffn(E, I, d)
+    bad.up.scales = torch.zeros((E, I, d // 64 + 1), dtype=torch.bfloat16)
+    assert "up.scales" in _refused(moe.expert_ffn, x, r, bad, shared)
+    bad = _cpu_ffn(E, I, d)
+    bad.down.codes = torch.zeros((E, d, I // 2 - 1), dtype=torch.uint8)
+    assert "down.codes" in _refused(moe.expert_ffn, x, r, bad, shared)
+    assert "shared" in _refused(moe.expert_ffn, x, r, routed, _cpu_ffn(2, Is, d))
+    assert "shared" in _refused(moe.expert_ffn, x, r, routed, _cpu_ffn(1, Is, 2 * d))
+    bad3 = _cpu_ffn(E, I, d, bits=3)
+    bad3.gate.codes = torch.zeros((E, I, d // 2), dtype=torch.uint8)  # 4-bit row length with 3-bit codes
+    assert "gate.codes" in _refused(moe.expert_ffn, x, r, bad3, None)
+    # routing arrays
+    for name, t in (("tiles", torch.zeros((moe.max_tiles(dims, T) - 1, 3), dtype=torch.int32)),
+                    ("inv_pos", torch.zeros(T * k - 1, dtype=torch.int32)),
+                    ("offsets", torch.zeros(E, dtype=torch.int32)),
+                    ("counts", torch.zeros(E + 1, dtype=torch.int32)),
+                    ("sorted_token", torch.zeros(T * k + 1, dtype=torch.int32))):
+        rr = dict(r)
+        rr[name] = t
+        assert name in _refused(moe.expert_ffn, x, rr, routed, shared)
+    rr = dict(r)
+    rr["topk_w"] = torch.zeros((T, k + 1), dtype=torch.float32)
+    assert "topk_w" in _refused(moe.expert_ffn, x, rr, routed, shared)
+    # y, the layer's router and bias
+    assert "y has shape" in _refused(moe.expert_ffn, x, r, routed, shared, y=torch.zeros((T, d + 64), dtype=torch.bfloat16))
+    assert "w_router" in _refused(moe.Layer, torch.zeros((d, E + 1)), routed, shared, k)
+    assert "logit_bias" in _refused(moe.Layer, torch.zeros((d, E)), routed, shared, k, torch.zeros(E - 1))
+    assert "w_router" in _refused(moe.route, x, torch.zeros((d + 64, E)), k, I, Is)
+    assert "logit_bias" in _refused(moe.route, x, torch.zeros((d, E)), k, I, Is, torch.zeros(E + 1))
+    p = routed.gate
+    assert "scales" in _refused(moe.debug_dequant, moe.QProj(p.codes, p.scales[:, :, :1].contiguous(), p.biases))
+    # the well-formed arguments get past every shape check (and then need a GPU tensor)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.expert_ffn(x, r, routed, shared)
