@@ -55,8 +55,7 @@
 #endif
 
 #define ORC_GROUP 64
-#define ORC_SMALL_TILE 32 /* a group of at most this many rows is one tile */
-#define ORC_BIG_TILE 64   /* a larger group is cut into tiles of this many rows */
+#define ORC_TILE_ROWS 32
 
 typedef struct {
   const uint8_t* codes;    /* [n_mat][out][in * bits / 8]: each row a little-endian bit stream */
@@ -164,24 +163,11 @@ int oracle_topk_softmax(int32_t T, int32_t E, int32_t k, const float* logits, in
  * sort of pairs by expert, so rows of one expert keep ascending token order (reading: the
  * pages do not fix the order inside a group); sorted_token[row] = token of that grouped row,
  * inv_pos[t][j] = grouped row of pair (t, j).
- * Block map (reading; the pages say that the engine sizes its compute blocks to each expert's
- * load, that 32-row tiles beat 16-row ones, and frame the tile choice around about 64 rows per
- * expert): each non-empty group, in ascending expert order, is one tile when it holds at most 32
- * rows, else it is cut into consecutive tiles of 64 rows, the last one holding what remains;
- * then, when a shared expert exists, its T rows (grouped rows T*k .. T*k+T-1, token order) are
- * cut the same way and tagged with expert index E. A tile is (expert, first grouped row, rows). */
-static int orc_cut_group(int32_t e, int32_t first, int32_t n, int32_t* tiles, int32_t cap, int32_t* count) {
-  const int32_t step = n <= ORC_SMALL_TILE ? ORC_SMALL_TILE : ORC_BIG_TILE;
-  for (int32_t r = 0; r < n; r += step) {
-    if (*count >= cap) return 2;
-    tiles[3 * *count + 0] = e;
-    tiles[3 * *count + 1] = first + r;
-    tiles[3 * *count + 2] = n - r < step ? n - r : step;
-    ++*count;
-  }
-  return 0;
-}
-
+ * Block map (reading; the pages say that block size follows each expert's load and that 32-row
+ * tiles beat 16-row ones): each non-empty group, in ascending expert order, is cut into
+ * consecutive tiles of at most 32 rows; then, when a shared expert exists, its T rows (grouped
+ * rows T*k .. T*k+T-1, token order) are cut the same way and tagged with expert index E. A tile
+ * is (expert, first grouped row, rows). */
 int oracle_route_meta(int32_t T, int32_t E, int32_t k, int32_t has_shared, const int32_t* ids,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
                       int32_t* tiles, int32_t tiles_cap, int32_t* n_tiles) {
@@ -205,9 +191,24 @@ int oracle_route_meta(int32_t T, int32_t E, int32_t k, int32_t has_shared, const
   }
   free(cursor);
   int32_t n = 0;
-  for (int32_t e = 0; e < E; ++e)
-    if (orc_cut_group(e, offsets[e], counts[e], tiles, tiles_cap, &n)) return 2;
-  if (has_shared && orc_cut_group(E, (int32_t)P, T, tiles, tiles_cap, &n)) return 2;
+  for (int32_t e = 0; e < E; ++e) {
+    for (int32_t r = 0; r < counts[e]; r += ORC_TILE_ROWS) {
+      if (n >= tiles_cap) return 2;
+      tiles[3 * n + 0] = e;
+      tiles[3 * n + 1] = offsets[e] + r;
+      tiles[3 * n + 2] = counts[e] - r < ORC_TILE_ROWS ? counts[e] - r : ORC_TILE_ROWS;
+      ++n;
+    }
+  }
+  if (has_shared) {
+    for (int32_t r = 0; r < T; r += ORC_TILE_ROWS) {
+      if (n >= tiles_cap) return 2;
+      tiles[3 * n + 0] = E;
+      tiles[3 * n + 1] = (int32_t)P + r;
+      tiles[3 * n + 2] = T - r < ORC_TILE_ROWS ? T - r : ORC_TILE_ROWS;
+      ++n;
+    }
+  }
   *n_tiles = n;
   return 0;
 }
@@ -405,7 +406,7 @@ int oracle_forward_layer(int32_t T, int32_t d, int32_t E, int32_t k, int32_t I, 
   int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
   int32_t* sorted_token = (int32_t*)malloc(sizeof(int32_t) * (size_t)(P + 1));
   int32_t* inv_pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(P + 1));
-  int32_t cap = (int32_t)(E + P / ORC_SMALL_TILE + T / ORC_SMALL_TILE + 2);
+  int32_t cap = (int32_t)(E + P / ORC_TILE_ROWS + T / ORC_TILE_ROWS + 2);
   int32_t* tiles = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)cap);
   int32_t n_tiles = 0;
   int rc = oracle_router_logits(T, d, E, x, w_router, bias, logits);

