@@ -44,6 +44,9 @@ hipError_t launch_decode_topk(const Ctx& c) {
 // staged per pass (64 KB in every case; larger d in passes). More tokens per block mean fewer
 // router loads per fma but fewer blocks: the launch takes the most tokens per block that still
 // give 256 blocks, and 4 when none does (small calls, where the block count is what matters).
+// The (token block, expert block) items are dealt to the 8 XCDs (block b runs on XCD b % 8) in
+// contiguous ranges of expert-block-major order, so each XCD's L2 fetches the router columns of
+// only the expert blocks it works on instead of the whole matrix.
 constexpr int kRpWaves = 16;
 
 template <int TOK>
@@ -55,11 +58,16 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
   __shared__ __attribute__((aligned(16))) float s_x[kMaxD][TOK];  // 64 KB, [input][token]
   __shared__ float s_parts[kMaxChunks][TOK][64];                  // 64 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * TOK;
-  const int e = blockIdx.y * 64 + lane;
+  const int nbx = (T + TOK - 1) / TOK, total = nbx * ((E + 63) / 64);
+  const int per = (total + 7) / 8;  // items per XCD
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= total) return;
+  const int by = item / nbx, bx = item - by * nbx;  // expert block, token block
+  const int t0 = bx * TOK;
+  const int e = by * 64 + lane;
   const int ec = e < E ? e : E - 1;  // experts past E compute a copy that is never stored
   const int nchunks = d / kGroup;
-  const int s_tok = tid >> 6, s_e = blockIdx.y * 64 + lane;  // sum phase: threads 0 .. 64 TOK - 1
+  const int s_tok = tid >> 6, s_e = by * 64 + lane;  // sum phase: threads 0 .. 64 TOK - 1
   float acc = 0.0f;
   for (int p = 0; p < nchunks; p += kMaxChunks) {
     const int npass = min(kMaxChunks, nchunks - p);
@@ -129,17 +137,16 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
 
 hipError_t launch_router_prefill(const Ctx& c) {
   const int ne = (c.E + 63) / 64;
+  // one block per (token block, expert block) item, the grid rounded up to whole rounds of 8 XCDs
+  const auto grid = [&](int tok) { return dim3((unsigned)(8 * ((((c.T + tok - 1) / tok) * ne + 7) / 8))); };
   if (((c.T + 15) / 16) * ne >= 256) {
-    const dim3 grid((c.T + 15) / 16, ne);
-    hipLaunchKernelGGL(k_router_prefill<16>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
+    hipLaunchKernelGGL(k_router_prefill<16>, grid(16), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
                        c.logit_bias, c.logits);
   } else if (((c.T + 7) / 8) * ne >= 256) {
-    const dim3 grid((c.T + 7) / 8, ne);
-    hipLaunchKernelGGL(k_router_prefill<8>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
+    hipLaunchKernelGGL(k_router_prefill<8>, grid(8), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
                        c.logit_bias, c.logits);
   } else {
-    const dim3 grid((c.T + 3) / 4, ne);
-    hipLaunchKernelGGL(k_router_prefill<4>, grid, dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
+    hipLaunchKernelGGL(k_router_prefill<4>, grid(4), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
                        c.logit_bias, c.logits);
   }
   return hipGetLastError();
