@@ -19,6 +19,7 @@ struct Ctx {
   moe_ffn_q4 routed;
   moe_ffn_q4 shared;  // all-null when Is == 0
   moe_routing r;      // routing arrays (caller's or carved from the workspace)
+  int32_t* meta_hist;     // [slices][E] per-slice expert counts (sliced routing metadata only)
   float* router_parts;    // [T][E][d/64] router chunk partials (GEMV path, T <= kGemvMaxT)
   float* logits;          // [T][E] router logits (T >= 2)
   uint16_t* xp;           // [T][d] bf16: x with each 8-input chunk in pair order (grouped GEMM operand)
@@ -70,6 +71,17 @@ hipError_t scratch_device_ptr(void** out);
 
 // Block-map tile height (rows of one expert group per tile).
 constexpr int kTileRows = 32;
+
+// Routing metadata of more than kMetaSlicedFrom pairs (T k) runs in three launches over at most
+// kMetaMaxSlices slices of a whole number of 1024-pair spans; smaller calls take one launch.
+constexpr int kMetaSlicedFrom = 32768;
+constexpr int kMetaMaxSlices = 256;
+inline bool meta_sliced(int64_t P) { return P > kMetaSlicedFrom; }
+inline int meta_slice_span(int64_t P) {
+  const int64_t per = (P + kMetaMaxSlices - 1) / kMetaMaxSlices;
+  return (int)((per + 1023) / 1024 * 1024);
+}
+inline int meta_slices(int64_t P) { return meta_sliced(P) ? (int)((P + meta_slice_span(P) - 1) / meta_slice_span(P)) : 0; }
 
 // Calls of up to kGemvMaxT tokens take the GEMV path (one token per wave, no grouping).
 constexpr int kGemvMaxT = 32;

@@ -74,8 +74,8 @@ bool gemv_path_ctx(const Ctx& c) {
 }
 
 struct Layout {
-  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, xp, xsum, h, hs, hsum, hsum_sh,
-      y_rows, total;
+  size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, meta_hist, xp, xsum, h, hs, hsum,
+      hsum_sh, y_rows, total;
 };
 
 Layout layout_of(const moe_dims& dm, int32_t T) {
@@ -102,6 +102,8 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   o += up((size_t)max_tiles_of(dm, T) * 12);
   L.n_tiles = o;
   o += up(4);
+  L.meta_hist = o;
+  o += up((size_t)meta_slices(P) * E * 4);
   L.xp = o;
   o += up((size_t)T * d * 2);
   L.xsum = o;
@@ -247,6 +249,7 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.r.inv_pos = reinterpret_cast<int32_t*>(b + L.inv_pos);
   c.r.tiles = reinterpret_cast<int32_t*>(b + L.tiles);
   c.r.n_tiles = reinterpret_cast<int32_t*>(b + L.n_tiles);
+  c.meta_hist = reinterpret_cast<int32_t*>(b + L.meta_hist);
   c.stream = stream;
   c.x = nullptr;
   c.w_router = nullptr;

@@ -221,19 +221,26 @@ hipError_t launch_pair_x(const Ctx& c) { return launch_pair_rows(c.x, c.xp, c.xs
 
 // ---------------------------------------------------------------------------------------------
 // Histogram, prefix scan, stable scatter and block map over several 1024-thread blocks.
-// Block b ranks the pairs [b span, (b + 1) span); every block reads all T k expert ids to count,
-// per expert, all pairs and the pairs before its slice, so no block waits for another:
+// Block b ranks the pairs of its slice [b span, (b + 1) span):
 //   - counts are LDS atomic adds, one per pair (exact integers, whatever the order of the adds);
 //   - a block scan over experts gives offsets; the first row of expert e for wave w of block b is
 //     offsets[e] + (pairs of e before the block) + (pairs of e in waves 0 .. w - 1 of the block);
 //   - within a wave, the lanes holding the same expert find each other with one ballot per bit of
 //     the expert id, and a lane's rank among its peers is the popcount of its lower peers, so the
 //     rows of an expert follow pair order, i.e. ascending token.
-// Block 0 also writes counts, offsets and the block map: each non-empty group in ascending expert
-// order cut into consecutive tiles of at most kTileRows rows, then the shared expert's T rows.
-// Blocks past the metadata blocks pair x for the grouped GEMM (they need nothing from the others).
+// Two ways to get the pairs of each expert before a slice:
+//   - up to kMetaSlicedFrom pairs, one launch: every block counts all T k pairs (and those before
+//     its slice) itself, so no block waits for another; block 0 also writes counts, offsets and
+//     the block map;
+//   - beyond that, the repeated count would grow with the square of T k, so three launches: each
+//     slice's histogram; per-expert exclusive prefixes of the histograms over the slices (in
+//     place) and the counts; then, in every slice block, offsets from a block scan of the counts
+//     and the ranks of its slice (block 0 also writes offsets and the block map).
+// The block map: each non-empty group in ascending expert order cut into consecutive tiles of at
+// most kTileRows rows, then the shared expert's T rows. Blocks past the metadata blocks of the
+// (last) launch pair x for the grouped GEMM (they need nothing from the others).
 constexpr int kMetaWaves = 16;
-constexpr int kMetaSpan = 1024;  // pairs ranked per metadata block
+constexpr int kMetaSpan = 1024;  // pairs ranked per metadata block (single launch)
 constexpr int kMetaBatch = 8;    // 64-pair batches whose ids a wave loads together when counting
 
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
@@ -275,6 +282,111 @@ __device__ __forceinline__ uint64_t peer_mask(int e, bool valid, int nbits) {
   return valid ? peers : 0ull;
 }
 
+__device__ __forceinline__ int expert_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// This wave's part of the slice [b_begin, b_end): pairs [w_begin, w_end), 64-aligned lengths.
+__device__ __forceinline__ void wave_part(int b_begin, int b_end, int& w_begin, int& w_end) {
+  const int span = b_end - b_begin;
+  const int wspan = (((span + kMetaWaves - 1) / kMetaWaves) + 63) & ~63;
+  w_begin = min(b_end, b_begin + (int)(threadIdx.x >> 6) * wspan);
+  w_end = min(b_end, w_begin + wspan);
+}
+
+// Pairs of each expert in this wave's part, into s_tab[wave][.] (zeroed by the caller); the ids of
+// kMetaBatch 64-pair batches are loaded before any is counted.
+__device__ __forceinline__ void wave_counts(const int32_t* __restrict__ ids, int E, int w_begin, int w_end,
+                                            int* s_row) {
+  const int lane = threadIdx.x & 63;
+  for (int base = w_begin; base < w_end; base += 64 * kMetaBatch) {
+    int ev[kMetaBatch];
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i) {
+      const int p = base + 64 * i + lane;
+      ev[i] = p < w_end ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i)
+      if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&s_row[ev[i]], 1);
+  }
+}
+
+// Thread e (< E) turns the per-wave counts of expert e into each wave's first row of e, from the
+// slice's first row `first` of e.
+__device__ __forceinline__ void wave_cursors(int E, int first, int (*s_tab)[kMaxExperts]) {
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    int run = first;
+#pragma unroll
+    for (int w2 = 0; w2 < kMetaWaves; ++w2) {
+      const int c = s_tab[w2][tid];
+      s_tab[w2][tid] = run;
+      run += c;
+    }
+  }
+}
+
+// Stable ranks of this wave's part: a lane's row is the wave's cursor plus the number of its lower
+// peers; the lowest peer then advances the cursor. The next batch's ids are loaded before the
+// current batch is ranked. The token index comes from an fp32 reciprocal with a one-step
+// correction (exact for p < 2^21).
+__device__ __forceinline__ void wave_ranks(const int32_t* __restrict__ ids, int E, int k, int w_begin, int w_end,
+                                           int* s_row, int32_t* __restrict__ sorted_token,
+                                           int32_t* __restrict__ inv_pos) {
+  const int lane = threadIdx.x & 63, nbits = expert_bits(E);
+  const float inv_k = 1.0f / (float)k;
+  int e_next = w_begin + lane < w_end ? ids[w_begin + lane] : -1;
+  for (int base = w_begin; base < w_end; base += 64) {
+    const int p = base + lane;
+    const int e = e_next;
+    e_next = p + 64 < w_end ? ids[p + 64] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    int tq = (int)((float)p * inv_k);
+    const int r = p - tq * k;
+    tq += r >= k ? 1 : (r < 0 ? -1 : 0);
+    const uint64_t peers = peer_mask(e, valid, nbits);
+    int pos = 0;
+    if (valid) pos = s_row[e] + __popcll(peers & lanemask_lt());
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & lanemask_lt()) == 0) s_row[e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      sorted_token[pos] = tq;
+      inv_pos[p] = pos;
+    }
+  }
+}
+
+// counts (when given), offsets and the block map, by one block whose thread e (< E) holds
+// cnt = counts[e] and off = offsets[e]; total = T k.
+__device__ __forceinline__ void write_block_map(int T, int E, int P, int has_shared, int cnt, int off, int total,
+                                                int* s_wsum, int32_t* __restrict__ counts,
+                                                int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
+                                                int32_t* __restrict__ n_tiles) {
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    if (counts) counts[tid] = cnt;
+    offsets[tid] = off;
+  }
+  if (tid == 0) offsets[E] = total;
+  const int nt = tid < E ? (cnt + kTileRows - 1) / kTileRows : 0;
+  int n_routed = 0;
+  const int tfirst = block_excl_scan(nt, s_wsum, &n_routed);
+  for (int j = 0; j < nt; ++j) {
+    int32_t* tl = tiles + 3 * (size_t)(tfirst + j);
+    tl[0] = tid;
+    tl[1] = off + j * kTileRows;
+    tl[2] = min(kTileRows, cnt - j * kTileRows);
+  }
+  const int n_shared = has_shared ? (T + kTileRows - 1) / kTileRows : 0;
+  for (int j = tid; j < n_shared; j += 1024) {
+    int32_t* tl = tiles + 3 * (size_t)(n_routed + j);
+    tl[0] = E;
+    tl[1] = P + j * kTileRows;
+    tl[2] = min(kTileRows, T - j * kTileRows);
+  }
+  if (tid == 0) *n_tiles = n_routed + n_shared;
+}
+
 __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int has_shared, int n_meta,
                                                      const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
@@ -300,10 +412,8 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
     for (int w2 = 0; w2 < kMetaWaves; ++w2) s_tab[w2][e] = 0;
   }
   __syncthreads();
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
-  // 1. counts of all pairs and of the pairs before the slice (every block, every pair): one LDS
-  //    atomic add per pair (integer counts do not depend on the order of the adds); a wave takes
-  //    64-pair batches wave, wave + 16, ... and loads kMetaBatch of them before counting any
+  // 1. counts of all pairs and of the pairs before the slice (every block, every pair): a wave
+  //    takes 64-pair batches wave, wave + 16, ... and loads kMetaBatch of them before counting any
   for (int base0 = wave * 64; base0 < P; base0 += 64 * kMetaWaves * kMetaBatch) {
     int ev[kMetaBatch];
 #pragma unroll
@@ -321,85 +431,134 @@ __global__ __launch_bounds__(1024) void k_route_meta(int T, int E, int k, int ha
       }
     }
   }
-  // 2. per-wave counts of this block's slice: wave w owns [b_begin + w wspan, ...)
-  const int wspan = (((kMetaSpan + kMetaWaves - 1) / kMetaWaves) + 63) & ~63;
-  const int w_begin = min(b_end, b_begin + wave * wspan), w_end = min(b_end, w_begin + wspan);
-  for (int base = w_begin; base < w_end; base += 64) {
-    const int p = base + lane;
-    const int e = p < w_end ? ids[p] : -1;
-    if ((unsigned)e < (unsigned)E) atomicAdd(&s_tab[wave][e], 1);
-  }
+  // 2. per-wave counts of this block's slice
+  int w_begin, w_end;
+  wave_part(b_begin, b_end, w_begin, w_end);
+  wave_counts(ids, E, w_begin, w_end, s_tab[wave]);
   __syncthreads();
-  // 3. offsets, then each wave's first row in every group
+  // 3. offsets, then each wave's first row in every group; block 0 writes the map
   const int cnt = tid < E ? s_all[tid] : 0;
   int total = 0;
   const int off = block_excl_scan(cnt, s_wsum, &total);
-  if (tid < E) {
-    int run = off + s_before[tid];
+  wave_cursors(E, off + (tid < E ? s_before[tid] : 0), s_tab);
+  if (blockIdx.x == 0) write_block_map(T, E, P, has_shared, cnt, off, total, s_wsum, counts, offsets, tiles, n_tiles);
+  __syncthreads();
+  // 4. stable ranks of the slice
+  wave_ranks(ids, E, k, w_begin, w_end, s_tab[wave], sorted_token, inv_pos);
+}
+
+// Sliced metadata, launch 1: hist[s][e] = pairs of expert e in slice s.
+__global__ __launch_bounds__(1024) void k_meta_hist(int P, int E, int span, const int32_t* __restrict__ ids,
+                                                    int32_t* __restrict__ hist) {
+  __shared__ int s_cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
+  __syncthreads();
+  const int b_begin = min(P, (int)blockIdx.x * span), b_end = min(P, b_begin + span);
+  for (int p0 = b_begin; p0 < b_end; p0 += 1024 * kMetaBatch) {
+    int ev[kMetaBatch];
 #pragma unroll
-    for (int w2 = 0; w2 < kMetaWaves; ++w2) {
-      const int c = s_tab[w2][tid];
-      s_tab[w2][tid] = run;
-      run += c;
+    for (int i = 0; i < kMetaBatch; ++i) {
+      const int p = p0 + 1024 * i + tid;
+      ev[i] = p < b_end ? ids[p] : -1;
     }
-  }
-  if (blockIdx.x == 0) {
-    if (tid < E) {
-      counts[tid] = cnt;
-      offsets[tid] = off;
-    }
-    if (tid == 0) offsets[E] = total;
-    // block map: routed tiles in expert order, then the shared expert's rows
-    const int nt = tid < E ? (cnt + kTileRows - 1) / kTileRows : 0;
-    int n_routed = 0;
-    const int tfirst = block_excl_scan(nt, s_wsum, &n_routed);
-    for (int j = 0; j < nt; ++j) {
-      int32_t* tl = tiles + 3 * (size_t)(tfirst + j);
-      tl[0] = tid;
-      tl[1] = off + j * kTileRows;
-      tl[2] = min(kTileRows, cnt - j * kTileRows);
-    }
-    const int n_shared = has_shared ? (T + kTileRows - 1) / kTileRows : 0;
-    for (int j = tid; j < n_shared; j += 1024) {
-      int32_t* tl = tiles + 3 * (size_t)(n_routed + j);
-      tl[0] = E;
-      tl[1] = P + j * kTileRows;
-      tl[2] = min(kTileRows, T - j * kTileRows);
-    }
-    if (tid == 0) *n_tiles = n_routed + n_shared;
+#pragma unroll
+    for (int i = 0; i < kMetaBatch; ++i)
+      if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&s_cnt[ev[i]], 1);
   }
   __syncthreads();
-  // 4. stable ranks of the slice: a lane's row is the wave's cursor plus the number of its lower
-  //    peers; the lowest peer then advances the cursor. The token index comes from an fp32
-  //    reciprocal with a one-step correction (exact for p < 2^21).
-  const float inv_k = 1.0f / (float)k;
-  for (int base = w_begin; base < w_end; base += 64) {
-    const int p = base + lane;
-    const int e = p < w_end ? ids[p] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    int tq = (int)((float)p * inv_k);
-    const int r = p - tq * k;
-    tq += r >= k ? 1 : (r < 0 ? -1 : 0);
-    const uint64_t peers = peer_mask(e, valid, nbits);
-    int pos = 0;
-    if (valid) pos = s_tab[wave][e] + __popcll(peers & lanemask_lt());
-    __builtin_amdgcn_wave_barrier();
-    if (valid && (peers & lanemask_lt()) == 0) s_tab[wave][e] += __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      sorted_token[pos] = tq;
-      inv_pos[p] = pos;
-    }
+  for (int e = tid; e < E; e += 1024) hist[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// Sliced metadata, launch 2: block b takes experts 64 b .. 64 b + 63 (lane = expert); wave w takes
+// the w-th run of kScanRun consecutive slices. hist[.][e] becomes its exclusive prefix over the
+// slices and counts[e] the total.
+constexpr int kScanRun = kMetaMaxSlices / kMetaWaves;
+__global__ __launch_bounds__(1024) void k_meta_scan(int E, int n_slices, int32_t* __restrict__ hist,
+                                                    int32_t* __restrict__ counts) {
+  __shared__ int s_run[kMetaWaves][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = (int)blockIdx.x * 64 + lane, s0 = wave * kScanRun;
+  int c[kScanRun], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kScanRun; ++i) c[i] = (e < E && s0 + i < n_slices) ? hist[(size_t)(s0 + i) * E + e] : 0;
+#pragma unroll
+  for (int i = 0; i < kScanRun; ++i) sum += c[i];
+  s_run[wave][lane] = sum;
+  __syncthreads();
+  int run = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kMetaWaves; ++w2) run += w2 < wave ? s_run[w2][lane] : 0;
+  if (e < E) {
+#pragma unroll
+    for (int i = 0; i < kScanRun; ++i)
+      if (s0 + i < n_slices) {
+        hist[(size_t)(s0 + i) * E + e] = run;
+        run += c[i];
+      }
+    if (wave == kMetaWaves - 1) counts[e] = run;
   }
+}
+
+// Sliced metadata, launch 3: every slice block scans counts into offsets (block 0 also writes
+// offsets and the block map) and ranks its slice from offsets[e] + hist[b][e]. Blocks past the
+// slices pair x for the grouped GEMM.
+__global__ __launch_bounds__(1024) void k_meta_rank(int T, int E, int k, int has_shared, int span, int n_slices,
+                                                    const int32_t* __restrict__ ids,
+                                                    const int32_t* __restrict__ hist,
+                                                    const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
+                                                    int32_t* __restrict__ inv_pos, int32_t* __restrict__ tiles,
+                                                    int32_t* __restrict__ n_tiles, const uint4* __restrict__ x,
+                                                    uint4* __restrict__ xp, float* __restrict__ xsum, int64_t nchunks) {
+  __shared__ int s_tab[kMetaWaves][kMaxExperts];
+  __shared__ int s_wsum[17];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  if ((int)blockIdx.x >= n_slices) {
+    pair_groups(x, xp, xsum, nchunks, (int64_t)(blockIdx.x - n_slices) * 1024 + tid,
+                (int64_t)(gridDim.x - n_slices) * 1024);
+    return;
+  }
+  const int P = T * k;
+  for (int e = tid; e < E; e += 1024) {
+#pragma unroll
+    for (int w2 = 0; w2 < kMetaWaves; ++w2) s_tab[w2][e] = 0;
+  }
+  const int cnt = tid < E ? counts[tid] : 0;
+  const int before = tid < E ? hist[(size_t)blockIdx.x * E + tid] : 0;
+  __syncthreads();
+  const int b_begin = min(P, (int)blockIdx.x * span), b_end = min(P, b_begin + span);
+  int w_begin, w_end;
+  wave_part(b_begin, b_end, w_begin, w_end);
+  wave_counts(ids, E, w_begin, w_end, s_tab[wave]);
+  int total = 0;
+  const int off = block_excl_scan(cnt, s_wsum, &total);  // its barriers also end the counting
+  wave_cursors(E, off + before, s_tab);
+  if (blockIdx.x == 0) write_block_map(T, E, P, has_shared, cnt, off, total, s_wsum, nullptr, offsets, tiles, n_tiles);
+  __syncthreads();
+  wave_ranks(ids, E, k, w_begin, w_end, s_tab[wave], sorted_token, inv_pos);
 }
 
 hipError_t launch_route_meta(const Ctx& c) {
   const int64_t nchunks = c.pair_in_meta ? (int64_t)c.T * c.d / 8 : 0;
-  const int n_meta = std::max(1, (c.P + kMetaSpan - 1) / kMetaSpan);
-  const int nblocks = n_meta + (nchunks ? pair_blocks(nchunks, 1024) : 0);
-  hipLaunchKernelGGL(k_route_meta, dim3(nblocks), dim3(1024), 0, c.stream, c.T, c.E, c.k, c.Is > 0 ? 1 : 0, n_meta,
-                     c.r.topk_ids, c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos, c.r.tiles, c.r.n_tiles,
-                     reinterpret_cast<const uint4*>(c.x), reinterpret_cast<uint4*>(c.xp), c.xsum, nchunks);
+  const int pair = nchunks ? pair_blocks(nchunks, 1024) : 0;
+  const int has_shared = c.Is > 0 ? 1 : 0;
+  const uint4* x = reinterpret_cast<const uint4*>(c.x);
+  uint4* xp = reinterpret_cast<uint4*>(c.xp);
+  if (!meta_sliced(c.P)) {
+    const int n_meta = std::max(1, (c.P + kMetaSpan - 1) / kMetaSpan);
+    hipLaunchKernelGGL(k_route_meta, dim3(n_meta + pair), dim3(1024), 0, c.stream, c.T, c.E, c.k, has_shared, n_meta,
+                       c.r.topk_ids, c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos, c.r.tiles, c.r.n_tiles, x,
+                       xp, c.xsum, nchunks);
+    return hipGetLastError();
+  }
+  const int span = meta_slice_span(c.P), n_slices = meta_slices(c.P);
+  hipLaunchKernelGGL(k_meta_hist, dim3(n_slices), dim3(1024), 0, c.stream, c.P, c.E, span, c.r.topk_ids, c.meta_hist);
+  hipLaunchKernelGGL(k_meta_scan, dim3((c.E + 63) / 64), dim3(1024), 0, c.stream, c.E, n_slices, c.meta_hist,
+                     c.r.counts);
+  hipLaunchKernelGGL(k_meta_rank, dim3(n_slices + pair), dim3(1024), 0, c.stream, c.T, c.E, c.k, has_shared, span,
+                     n_slices, c.r.topk_ids, c.meta_hist, c.r.counts, c.r.offsets, c.r.sorted_token, c.r.inv_pos,
+                     c.r.tiles, c.r.n_tiles, x, xp, c.xsum, nchunks);
   return hipGetLastError();
 }
 

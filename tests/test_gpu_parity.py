@@ -87,6 +87,23 @@ def test_route_small_shapes(T, E, k, Is):
     check_routing(r, _oracle_routing(x, wr, None, k, Is > 0), f"T={T} E={E} k={k} Is={Is}")
 
 
+# Calls of more than 32768 pairs take the sliced metadata (per-slice histograms, one scan block,
+# per-slice ranks); 32768 pairs and fewer take the single launch. Both sides of the switch, one
+# expert, a partial last slice and groups far longer than a slice.
+@pytest.mark.parametrize("T,E,k,Is", [(4096, 256, 8, 64), (4097, 256, 8, 64), (40000, 1, 1, 0), (33000, 300, 5, 64),
+                                      (65536, 16, 16, 0)])
+def test_route_sliced_metadata(T, E, k, Is):
+    w = _custom(T, 64, E, k, 64, Is, seed=T + E)
+    x = gen.tokens(w, 0, 0)
+    wr = gen.router(w, 0)
+    r = moe.route(bf16_dev(x), f32_dev(wr), k, 64, Is)
+    check_routing(r, _oracle_routing(x, wr, None, k, Is > 0), f"T={T} E={E} k={k} Is={Is}")
+
+
+def test_forward_sliced_metadata():
+    _forward_check(_custom(4097, 64, 16, 8, 64, 64, seed=11))
+
+
 def test_route_ties_skew_and_large_groups():
     w = _custom(300, 256, 64, 8, 64, 64, seed=3)
     x = gen.tokens(w, 0, 0)
