@@ -52,7 +52,9 @@ def _assert_exact(got: np.ndarray, want: np.ndarray, what: str):
 # (T, d, E, k, I, Is, zipf, bits): the prefill shape; a K tail (d and I = 64 mod 128) with a
 # shared expert of another size; groups of ~150 rows; the skewed long shape (groups of up to ~250
 # rows); a down reduction of 13 groups (one output column block per work item, odd group count);
-# then the 3- and 2-bit codes on the prefill and diffusion shapes and on the ragged ones
+# then the 3- and 2-bit codes on the prefill and diffusion shapes and on the ragged ones; last,
+# groups of 200-500 rows (many whole tiles per group), with a shared expert twice as wide and
+# with skewed groups
 CASES = [
     (512, 2048, 256, 8, 512, 512, False, 4),
     (100, 192, 8, 3, 192, 64, False, 4),
@@ -67,6 +69,8 @@ CASES = [
     (300, 256, 4, 2, 128, 128, False, 2),
     (40, 256, 8, 2, 832, 0, False, 3),
     (40, 320, 8, 2, 832, 0, False, 2),
+    (1024, 512, 8, 2, 512, 512, False, 4),
+    (640, 1024, 4, 2, 512, 1024, True, 4),
 ]
 
 

@@ -192,6 +192,34 @@ SHAPES = [
 ]
 
 
+# Large expert groups (hundreds of rows, many whole tiles per group): groups of ~256 rows with a
+# shared expert of 1024 rows; a shared expert twice as wide as the routed ones; no shared expert;
+# a token count that leaves ragged last tiles.
+BIG = [(1024, 512, 8, 2, 512, 512), (700, 1024, 16, 4, 512, 1024), (640, 512, 4, 2, 512, 0), (1000, 512, 8, 4, 512, 512)]
+
+
+@pytest.mark.parametrize("T,d,E,k,I,Is", BIG)
+def test_forward_large_groups(T, d, E, k, I, Is):
+    _forward_check(_custom(T, d, E, k, I, Is, seed=T + E))
+
+
+def test_forward_whole_groups():
+    """Logit biases that route every token to one expert (one group of 512 rows, the other groups
+    empty), then to one of two experts (two groups of about 256)."""
+    w = _custom(512, 512, 4, 1, 512, 512, seed=5)
+    L = gen.layer(w, 0)
+    x = gen.tokens(w, 0, 0)
+    for hot in ([2], [1, 3]):
+        bias = np.zeros(4, np.float32)
+        bias[hot] = 1e4
+        ref = oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], 1, bias)
+        if len(hot) == 1:
+            assert (ref["counts"] == np.bincount([2], minlength=4) * 512).all()
+        y = layer_dev(dict(L, logit_bias=bias), 1).forward(bf16_dev(x))
+        torch.cuda.synchronize()
+        check_y(y, ref["y"], f"experts {hot}")
+
+
 @pytest.mark.parametrize("T,d,E,k,I,Is", SHAPES)
 def test_forward_small_shapes(T, d, E, k, I, Is):
     _forward_check(_custom(T, d, E, k, I, Is, seed=T + d + E))
