@@ -136,8 +136,11 @@ __device__ __forceinline__ uint4 code_pairs8(uint32_t u) {
 //     bytes at a 16-byte stride in LDS); the chunks of a row are XOR-swizzled by row so the
 //     MFMA-side reads spread over the banks. A job's steps are padded to an even count: the
 //     padding step loads in-bounds stand-in data and multiplies nothing;
-//   - scales, per step: with an even number of groups per row, one 4-byte load per weight row
-//     (the step's two groups); otherwise one 2-byte load per (row, group), each landing
+//   - scales: when K is whole steps, per pair of steps with the codes, into two pair stages:
+//     two 4-byte loads per weight row (each a step's two groups), both lanes of a row in one
+//     cache line and each wave loading its own 32 rows (a direct load's cost follows the cache
+//     lines it touches, so one load per row and step, repeated by two waves, had cost a sixth
+//     of the kernel). Otherwise per step, one 2-byte load per (row, group), each landing
 //     zero-extended in its own dword;
 //   - A rows (up to 32 gathered x rows, or h rows) of 256 bytes per step; the 16-byte chunks of
 //     a row are XOR-swizzled by row. A rows past the tile's rows repeat its last row and only
@@ -145,7 +148,7 @@ __device__ __forceinline__ uint4 code_pairs8(uint32_t u) {
 //     the GEMMs) and h (written so by the gate/up epilogue) hold each chunk of 8 inputs in pair
 //     order 0, 4, 1, 5, 2, 6, 3, 7, the order of the "128 + q" pairs, so A goes from LDS to the
 //     matrix cores unchanged.
-// A and the scales run in a ring of AS stages, AS - 1 steps ahead.
+// A (and the per-step scales) run in a ring of AS stages, AS - 1 steps ahead.
 // Addresses are a scalar base that advances per step plus a per-lane offset fixed for the run.
 // When K is an odd number of groups, the last step's second group reads in-bounds stand-in data
 // and is given scale 0 when it is multiplied. Weight rows past the down matrix repeat
@@ -220,7 +223,8 @@ template <int BITS, int MT, int AS, bool GU, bool PAIRED, int R, bool DBG, bool 
 __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int row0, int rows, uint8_t* lds) {
   static_assert(AS == 2 || AS == 3 || (AS == 4 && MT == 1 && PAIRED), "A and scale ring depth");
   static_assert(!VEC8 || PAIRED, "a multiple of 8 groups is whole steps");
-  constexpr int kSbBytes = PAIRED ? 512 : 1024;
+  constexpr int kSbBytes = 1024;            // without PAIRED: a scale stage per step
+  constexpr int kSpBytes = 1024;            // with PAIRED: a scale stage per pair of steps
   constexpr int kAS = MT * kA16StageBytes;  // an A stage: 16 MT rows
   // codes of a pair of steps: 32 BITS bytes per weight row, kCB-byte chunks, kLPR lanes per row;
   // in LDS a chunk takes 16 bytes and a row kLRB bytes
@@ -235,7 +239,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const auto Lc = [lds](int st) { return lds + st * kPairCodeStageBytes; };
   const auto La = [lds](int st) { return lds + 2 * kPairCodeStageBytes + st * kAS; };
   const auto Lsb = [lds](int st) {
-    return reinterpret_cast<uint32_t*>(lds + 2 * kPairCodeStageBytes + AS * kAS + st * kSbBytes);
+    return reinterpret_cast<uint32_t*>(lds + 2 * kPairCodeStageBytes + AS * kAS + st * (PAIRED ? kSpBytes : kSbBytes));
   };
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -260,9 +264,10 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   if (GU) {
     const bool upw = wave >= 2;
     wc = sh ? (upw ? a.shared.up.codes : a.shared.gate.codes) : (upw ? a.routed.up.codes : a.routed.gate.codes);
-    // scale loads: wave w loads block rows 64 (w & 1) .. +63, which are gate rows for w & 1 == 0
+    // scale loads: with PAIRED wave w loads block rows 32 w .. 32 w + 31 (gate rows for w < 2, up
+    // rows for w >= 2); otherwise block rows 64 (w & 1) .. +63, which are gate rows for w & 1 == 0
     // and up rows for w & 1 == 1 (waves 2, 3 repeat the loads of waves 0, 1 into the same slots)
-    const bool ups = (wave & 1) != 0;
+    const bool ups = PAIRED ? wave >= 2 : (wave & 1) != 0;
     sb_arr = sh ? (ups ? a.shared.up.scales : a.shared.gate.scales) : (ups ? a.routed.up.scales : a.routed.gate.scales);
   } else {
     wc = sh ? a.shared.down.codes : a.routed.down.codes;
@@ -281,12 +286,12 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     crow[t] = GU ? (r & (kGuCols - 1)) : r;  // row within the column block's weight rows
     cq16[t] = kCB * ((lane % kLPR) ^ (r & (kLPR - 1)));
   }
-  // scales: PAIRED: block row 64 (wave & 1) + lane; else (row, group) = (p >> 1, p & 1) for
-  // p = 64 (2 (wave & 1) + t) + lane
+  // scales: PAIRED: block row 32 wave + (lane >> 1), step lane & 1 of a pair; else (row, group) =
+  // (p >> 1, p & 1) for p = 64 (2 (wave & 1) + t) + lane
   int srow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int r = PAIRED ? (64 * (wave & 1) + lane) : ((64 * (2 * (wave & 1) + t) + lane) >> 1);
+    const int r = PAIRED ? (32 * wave + (lane >> 1)) : ((64 * (2 * (wave & 1) + t) + lane) >> 1);
     srow[t] = GU ? (r & (kGuCols - 1)) : r;
   }
   // A: row 4 (wave + 4 t) + (lane >> 4), chunk slot lane & 15
@@ -321,15 +326,21 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   const uint32_t lbase = lds_addr(lds);
   const uint32_t lds_c = lbase + wave * (32 * kLRB);
   const uint32_t lds_a = lbase + 2 * kPairCodeStageBytes + wave * 1024;
-  const uint32_t lds_s = lbase + 2 * kPairCodeStageBytes + AS * kAS + (PAIRED ? 256 : 512) * (wave & 1);
+  const uint32_t lds_s = lbase + 2 * kPairCodeStageBytes + AS * kAS + (PAIRED ? 256 * wave : 512 * (wave & 1));
   const uint8_t* cjb;
   uint32_t coq[kNL];  // codes: row offset + swizzled chunk
+  const uint8_t* spb;  // PAIRED: the scale pairs move with the codes (base of the code job's rows)
+  uint32_t spo;        // ... and this lane's offset: its row, plus 4 bytes for a pair's second step
   auto setup_codes = [&](int j) __attribute__((always_inline)) {
     const int n0 = (nb0 + j) * cols;
     const int lim = nrows_w - 1 - n0;
     cjb = wc + (mrow + n0) * (size_t)ldc;
 #pragma unroll
     for (int t = 0; t < kNL; ++t) coq[t] = (uint32_t)min(crow[t], lim) * (uint32_t)ldc + cq16[t];
+    if (PAIRED) {
+      spb = reinterpret_cast<const uint8_t*>(sb_arr + (mrow + n0) * (size_t)ldg);
+      spo = (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg) + 4u * (uint32_t)(lane & 1);
+    }
   };
   const uint16_t* sjb;
   uint32_t so[2];  // scale offsets in bytes
@@ -337,9 +348,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     const int n0 = (nb0 + j) * cols;
     const int lim = nrows_w - 1 - n0;
     sjb = sb_arr + (mrow + n0) * (size_t)ldg;
-    if (PAIRED) {
-      so[0] = (uint32_t)min(srow[0], lim) * (uint32_t)(2 * ldg);
-    } else {
+    if (!PAIRED) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) so[t] = ((uint32_t)min(srow[t], lim) * (uint32_t)ldg + (uint32_t)(lane & 1)) * 2u;
     }
@@ -371,6 +380,12 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 #pragma unroll
       for (int t = 0; t < kNL; ++t) dma(coq[t], dst + 1024 * t);
     }
+    if (PAIRED) {
+      // the pair's scale dwords (a step's two groups each); a pair whose second step is past K
+      // reads its first step's dword twice
+      const uint32_t off = 2 * ss + 1 < S ? spo : spo - 4u * (uint32_t)(lane & 1);
+      dma4(spb + 8 * ss, off, lds_s + st * kSpBytes);
+    }
   };
   // issue the A and scale loads of step s of the current job into stage st; the padding step
   // (s == S) re-reads step S - 1
@@ -378,9 +393,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
     s = min(s, S - 1);
     const bool tail = !PAIRED && s == S - 1 && (ldg & 1);
     const uint32_t sdst = lds_s + st * kSbBytes;
-    if (PAIRED) {
-      dma4(sjb + 2 * s, so[0], sdst);
-    } else {
+    if (!PAIRED) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) dma2(sjb + 2 * s, tail ? so[t] - 2u * (uint32_t)(lane & 1) : so[t], sdst + 256 * t);
     }
@@ -417,7 +430,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   // step of A/scale stage st, codes from stage cst, second step of its pair when h
   auto compute = [&](int st, int cst, int h, bool half) __attribute__((always_inline)) {
     const uint8_t* cs = Lc(cst);
-    const uint32_t* sb = Lsb(st);
+    const uint32_t* sb = Lsb(PAIRED ? cst : st);
     const uint8_t* as = La(st);
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
@@ -440,7 +453,7 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
       }
       float s0, s1;
       if (PAIRED) {
-        const uint32_t sc0 = sb[wrow0], sc1 = sb[wrow1];
+        const uint32_t sc0 = sb[2 * wrow0 + h], sc1 = sb[2 * wrow1 + h];
         s0 = gg ? bf16hi(sc0) : bf16lo(sc0);
         s1 = gg ? bf16hi(sc1) : bf16lo(sc1);
       } else {
@@ -665,8 +678,8 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
   // needs are one position's A/scales at an even position, and those plus one pair's codes at an
   // odd one; with AS = 2 they are nothing at an even position and one pair's codes at an odd one.
   // A stage is overwritten only after the barrier that follows its last read.
-  constexpr int kOpsA = (PAIRED ? 1 : 2) + MT;  // A and scale loads one wave issues per position
-  constexpr int kOpsC = kNL;                    // code loads one wave issues per pair
+  constexpr int kOpsA = (PAIRED ? 0 : 2) + MT;  // A (and without PAIRED scale) loads one wave issues per position
+  constexpr int kOpsC = kNL + (PAIRED ? 1 : 0);  // code (and with PAIRED scale) loads one wave issues per pair
   const int P2 = njobs * S2;
   int ij = 0, is = 0;    // position being issued (job, step); stays at the last position
   int icj = 0, ics = 0;  // code pair being issued (job, pair); stays at the last pair
@@ -804,13 +817,15 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 
 template <int BITS, bool GU, bool PAIRED, int R, bool DBG, bool VEC8>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a) {
-  constexpr int kSbBytes = PAIRED ? 512 : 1024;
-  // One LDS buffer, carved per tile height: two code pair stages, then four 16-row A stages and
-  // four scale stages (tiles of at most 16 rows, whole steps), three of each (at most 16 rows,
-  // K an odd number of groups), or two 32-row A stages and two scale stages.
-  constexpr int kLds1 = 2 * kPairCodeStageBytes + 3 * (kA16StageBytes + kSbBytes);
-  constexpr int kLds2 = 2 * kPairCodeStageBytes + 2 * (2 * kA16StageBytes + kSbBytes);
-  constexpr int kLds4 = PAIRED ? 2 * kPairCodeStageBytes + 4 * (kA16StageBytes + kSbBytes) : 0;
+  constexpr int kScB = PAIRED ? 0 : 1024;  // scale stage per step (without PAIRED)
+  constexpr int kSpB = PAIRED ? 2048 : 0;  // two scale stages per pair of steps (PAIRED)
+  // One LDS buffer, carved per tile height: two code pair stages, then four 16-row A stages
+  // (tiles of at most 16 rows, whole steps), three 16-row A stages and three scale stages (at most
+  // 16 rows, K an odd number of groups), or two 32-row A stages (and two scale stages without
+  // PAIRED); with PAIRED the two scale pair stages last.
+  constexpr int kLds1 = 2 * kPairCodeStageBytes + 3 * (kA16StageBytes + kScB) + kSpB;
+  constexpr int kLds2 = 2 * kPairCodeStageBytes + 2 * (2 * kA16StageBytes + kScB) + kSpB;
+  constexpr int kLds4 = PAIRED ? 2 * kPairCodeStageBytes + 4 * kA16StageBytes + kSpB : 0;
   constexpr int kLds12 = kLds1 > kLds2 ? kLds1 : kLds2;
   constexpr int kLds = kLds12 > kLds4 ? kLds12 : kLds4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
