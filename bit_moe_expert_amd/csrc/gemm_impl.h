@@ -178,24 +178,28 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-// The LDS destination is a wave-uniform 32-bit LDS address (the m0 value).
+// The LDS destination is a wave-uniform 32-bit LDS address (the m0 value). The scalar operands come
+// from v_readfirstlane, a vector instruction writing scalar registers, which a vector memory
+// instruction may read only 5 wait states later; the compiler inserts such waits for its own
+// loads but cannot see inside an asm statement, so the statement supplies them itself: the m0
+// write and s_nop 3 (which also covers the one wait state a direct load needs after m0 is set).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(l)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma12(const void* base, uint32_t off, uint32_t l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx3 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(l)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(l)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma2(const void* base, uint32_t off, uint32_t l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(l)
                : "memory", "m0");
 }
