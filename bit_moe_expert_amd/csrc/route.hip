@@ -9,6 +9,7 @@
 // 64; a chunk partial is an fp32 fma chain over ascending inputs from +0; partials are added in
 // ascending chunk order to a +0 accumulator; the bias is added last.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -36,17 +37,24 @@ hipError_t launch_decode_topk(const Ctx& c) {
 
 // ---------------------------------------------------------------------------------------------
 // Prefill (T >= 2) logits: a block owns TOK tokens (4, 8 or 16) x 64 experts (lane = expert). The
-// block first stages the tokens' inputs in LDS as fp32 [input][token] (every thread issues all of
-// its loads before converting any); its 16 waves then take the 64-input chunks w, w + 16, ...: a
-// wave loads the chunk's 64 router values of its expert and runs one fma chain per token over
-// ascending inputs, so each router value feeds TOK chains. The chunk partials meet in LDS and
-// one thread per (token, expert) adds them in chunk order, then the bias. 16384 / TOK inputs are
-// staged per pass (64 KB in every case; larger d in passes). More tokens per block mean fewer
-// router loads per fma but fewer blocks: the launch takes the most tokens per block that still
-// give 256 blocks, and 4 when none does (small calls, where the block count is what matters).
-// The (token block, expert block) items are dealt to the 8 XCDs (block b runs on XCD b % 8) in
-// contiguous ranges of expert-block-major order, so each XCD's L2 fetches the router columns of
-// only the expert blocks it works on instead of the whole matrix.
+// block stages the tokens' inputs in LDS as fp32 [input][token]; its 16 waves take the 64-input
+// chunks w, w + 16, ...: a wave holds the chunk's 64 router values of its expert in registers and
+// runs one fma chain per token over ascending inputs, so each router value feeds TOK chains. The
+// chunk partials meet in LDS and one thread per (token, expert) adds them in chunk order, then the
+// bias. 16384 / TOK inputs are staged per pass (64 KB in every case; larger d in passes). More
+// tokens per block mean fewer router loads per fma but fewer blocks: the launch takes the most
+// tokens per block that still give 256 blocks, and 4 when none does (small calls, where the block
+// count is what matters). The (token block, expert block) items are dealt to the 8 XCDs (block b
+// runs on XCD b % 8) in contiguous ranges of expert-block-major order, so each XCD's L2 fetches the
+// router columns of only the expert blocks it works on instead of the whole matrix.
+// With 4 tokens per block (grids too small to fill the chip, where each block's load latency is
+// on the critical path) loads run ahead of their use: a wave's first router values go out with the
+// first inputs, each router value of the wave's next chunk is loaded into its register right after
+// its last fma in the current chunk, and the next pass's inputs are loaded into registers while
+// the current pass computes (1 us less at 128 blocks; with 8 or 16 tokens, where the other waves
+// of a SIMD already cover the latency, it was up to 1 us slower). Otherwise a wave loads a chunk's
+// router values when it starts the chunk, and a pass's inputs when the pass starts. Either way the
+// arithmetic and its order are those of one chunk at a time.
 constexpr int kRpWaves = 16;
 
 template <int TOK>
@@ -54,7 +62,8 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
                                                          const float* __restrict__ wr, const float* __restrict__ bias,
                                                          float* __restrict__ logits) {
   constexpr int kMaxD = 16384 / TOK;              // inputs staged per pass
-  constexpr int kMaxChunks = kMaxD / kGroup;
+  constexpr int kMaxChunks = kMaxD / kGroup;      // a multiple of kRpWaves
+  constexpr int kH = kMaxD / 1024;                // inputs per thread and pass
   __shared__ __attribute__((aligned(16))) float s_x[kMaxD][TOK];  // 64 KB, [input][token]
   __shared__ float s_parts[kMaxChunks][TOK][64];                  // 64 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -68,13 +77,10 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
   const int ec = e < E ? e : E - 1;  // experts past E compute a copy that is never stored
   const int nchunks = d / kGroup;
   const int s_tok = tid >> 6, s_e = by * 64 + lane;  // sum phase: threads 0 .. 64 TOK - 1
-  float acc = 0.0f;
-  for (int p = 0; p < nchunks; p += kMaxChunks) {
-    const int npass = min(kMaxChunks, nchunks - p);
-    const int nin = npass * kGroup;
-    // stage inputs p*64 .. p*64 + nin of the tokens: thread i takes inputs i, i + 1024, ...
-    constexpr int kH = kMaxD / 1024;
-    uint16_t v[kH][TOK];
+  // inputs p*64 .. p*64 + nin of the tokens into registers: thread i takes inputs i, i + 1024, ...
+  uint16_t v[kH][TOK];
+  const auto load_x = [&](int p) __attribute__((always_inline)) {
+    const int nin = min(kMaxChunks, nchunks - p) * kGroup;
 #pragma unroll
     for (int h = 0; h < kH; ++h) {
       const int i = tid + 1024 * h;
@@ -85,6 +91,22 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
         v[h][tk] = x[(size_t)t * d + (size_t)p * kGroup + ic];
       }
     }
+  };
+  constexpr bool kAhead = TOK == 4;
+  float wv[kGroup];  // router values of the wave's current chunk
+  const auto wcol = [&](int c) __attribute__((always_inline)) { return wr + (size_t)c * kGroup * E + ec; };
+  const auto load_w = [&](int c) __attribute__((always_inline)) {
+    const float* wp = wcol(c);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) wv[i] = wp[(size_t)i * E];
+  };
+  load_x(0);
+  if (kAhead && wave < nchunks) load_w(wave);
+  float acc = 0.0f;
+  for (int p = 0; p < nchunks; p += kMaxChunks) {
+    const int npass = min(kMaxChunks, nchunks - p);
+    const int nin = npass * kGroup;
+    if (!kAhead && p > 0) load_x(p);
 #pragma unroll
     for (int h = 0; h < kH; ++h) {
       const int i = tid + 1024 * h;
@@ -96,30 +118,39 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
                                bf16_to_f32(v[h][4 * q + 3]));
       }
     }
+    // (a barrier waits for all of the thread's loads, so the next pass's inputs go out after it)
     __syncthreads();
+    if (kAhead && p + kMaxChunks < nchunks) load_x(p + kMaxChunks);
     for (int cc = wave; cc < npass; cc += kRpWaves) {
-      const int c = p + cc;
-      float wv[kGroup];
-      const float* wp = wr + (size_t)c * kGroup * E + ec;
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) wv[i] = wp[(size_t)i * E];
+      if (!kAhead) load_w(p + cc);
+      const int cn = p + cc + kRpWaves;  // the wave's next chunk (this pass or the next)
+      const float* wn = wcol(min(cn, nchunks - 1));
       float pr[TOK];
 #pragma unroll
       for (int tk = 0; tk < TOK; ++tk) pr[tk] = 0.0f;
+      // two copies of the chunk, with and without the next chunk's loads (a per-value condition
+      // would keep both values of every register alive)
+      const auto chunk = [&](auto refill) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        float xs[TOK];
+        for (int i = 0; i < kGroup; ++i) {
+          float xs[TOK];
 #pragma unroll
-        for (int q = 0; q < TOK / 4; ++q) {
-          const float4 xq = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][4 * q]);
-          xs[4 * q] = xq.x;
-          xs[4 * q + 1] = xq.y;
-          xs[4 * q + 2] = xq.z;
-          xs[4 * q + 3] = xq.w;
+          for (int q = 0; q < TOK / 4; ++q) {
+            const float4 xq = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][4 * q]);
+            xs[4 * q] = xq.x;
+            xs[4 * q + 1] = xq.y;
+            xs[4 * q + 2] = xq.z;
+            xs[4 * q + 3] = xq.w;
+          }
+#pragma unroll
+          for (int tk = 0; tk < TOK; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
+          if constexpr (decltype(refill)::value) wv[i] = wn[(size_t)i * E];
         }
-#pragma unroll
-        for (int tk = 0; tk < TOK; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
-      }
+      };
+      if (kAhead && cn < nchunks)
+        chunk(std::true_type{});
+      else
+        chunk(std::false_type{});
 #pragma unroll
       for (int tk = 0; tk < TOK; ++tk) s_parts[cc][tk][lane] = pr[tk];
     }
