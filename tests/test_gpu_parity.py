@@ -10,7 +10,8 @@ import torch
 from oracle import oracle
 from workload import gen
 from bit_moe_expert_amd import moe
-from gpu_inputs import (DEV, bf16_dev, bits_host, check_routing, check_y, f32_dev, ffn_dev, layer_dev, proj_dev)
+from gpu_inputs import (DEV, bf16_dev, bits_host, check_routing, check_y, f32_dev, f32_of_bits, ffn_dev, layer_dev,
+                        proj_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -316,3 +317,30 @@ def test_zero_tokens_is_a_noop():
     x = torch.empty((0, w.d), dtype=torch.bfloat16, device=DEV)
     y = lay.forward(x, ws=lay.workspace(1))
     assert y.shape == (0, w.d)
+
+
+# ------------------------------------------------------------------ large magnitudes
+def _times_pow2_bf16(bits: np.ndarray, m: int) -> np.ndarray:
+    """bf16 values (as bits) times 2^m, exactly: m is added to the exponent of every nonzero value."""
+    b = np.asarray(bits, np.uint16).astype(np.int32)
+    return np.where((b & 0x7FFF) == 0, b, b + (m << 7)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("T,d,E,k,I,Is,m", [(96, 256, 16, 4, 128, 128, 13), (96, 256, 16, 4, 128, 128, 16),
+                                            (130, 320, 2, 1, 192, 64, 16), (40, 128, 8, 2, 64, 0, 15)])
+def test_grouped_rows_beyond_fp16_range(T, d, E, k, I, Is, m):
+    """Down scales and biases times 2^m (exact in bf16) put the grouped down GEMM's rows and the
+    outputs beyond the fp16 range (up to about 1e6); the layer must still match the oracle, so no
+    16-bit intermediate with fp16's range may sit between the down products and the output."""
+    w = _custom(T, d, E, k, I, Is, seed=m + T)
+    L = gen.layer(w, 0)
+    for f in (L["routed"], L["shared"]):
+        if f is not None:
+            f["down"] = dict(f["down"], scales=_times_pow2_bf16(f["down"]["scales"], m),
+                             biases=_times_pow2_bf16(f["down"]["biases"], m))
+    x = gen.tokens(w, 0, 0)
+    ref = oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], k, L["logit_bias"])
+    assert np.abs(f32_of_bits(ref["y"])).max() > 65504.0  # the rows really leave the fp16 range
+    y = layer_dev(L, k).forward(bf16_dev(x))
+    torch.cuda.synchronize()
+    check_y(y, ref["y"], f"down weights x 2^{m}")
