@@ -170,6 +170,28 @@ def traffic_from_profiles(workload: str, kernel: str):
     return float(m_b.group(1))
 
 
+def calib_mfma(dev, n: int = 8192, reps: int = 20) -> dict:
+    """A plain bf16 torch.matmul of n x n by n x n (contiguous operands, fp32 accumulate in the
+    library): the dense matrix-core rate a library GEMM reaches on this machine, beside the nominal peak."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    tfs = 2.0 * n ** 3 / (us * 1e-6) / 1e12
+    log(f"calibration: bf16 matmul {n}^3 in {us:.1f} us -> {tfs:.0f} TFLOP/s ({100 * tfs / MFMA_BF16_PEAK_TFS:.1f}% of "
+        f"the {MFMA_BF16_PEAK_TFS:.0f} TFLOP/s dense peak)")
+    return {"bf16_matmul_n": n, "us": round(us, 2), "TFLOPs": round(tfs, 1),
+            "frac_of_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+
+
 # ------------------------------------------------------------------------- CPU oracle baseline
 def cpu_model() -> str:
     try:
@@ -510,6 +532,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (counter scale)")
+    ap.add_argument("--calib-mfma", action="store_true",
+                    help="also time a large bf16 torch.matmul (8192^3): the matrix-core rate a library GEMM reaches")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -534,6 +558,7 @@ def main() -> int:
         for _ in range(5):
             b.copy_(a)
         torch.cuda.synchronize()
+    calib = calib_mfma(dev) if args.calib_mfma else None
 
     w = gen.WORKLOADS[args.workload]
     out = {
@@ -545,6 +570,8 @@ def main() -> int:
         "roofline": head["roofline"], "layer": head["layer"], "stages": head["stages"],
         "parity_worst_of_allowance": head["parity_worst_of_allowance"],
     }
+    if calib is not None:
+        out["calibration"] = calib
     if "cpu_baseline" in head:
         out["cpu_baseline"] = head["cpu_baseline"]
     if extras:
