@@ -69,10 +69,6 @@ bool gemv_path(const moe_dims& dm, int32_t T) {
          dm.d_ff_shared <= kGemvMaxFF;
 }
 
-bool gemv_path_ctx(const Ctx& c) {
-  return small_call(c.T) && c.k * c.I + c.Is <= kGemvMaxH && c.I <= kGemvMaxFF && c.Is <= kGemvMaxFF;
-}
-
 struct Layout {
   size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, meta_hist, xp, xsum, h, hs, hsum,
       hsum_sh, y_rows, total;
