@@ -10,7 +10,7 @@ import torch
 from oracle import oracle
 from workload import gen
 from bit_moe_expert_amd import moe
-from gpu_inputs import (DEV, bf16_dev, bits_host, check_routing, check_y, f32_dev, f32_of_bits, ffn_dev, layer_dev,
+from gpu_inputs import (DEV, bf16_dev, bits_host, check_routing, check_y, f32_dev, f32_of_bits, layer_dev,
                         proj_dev)
 
 pytestmark = pytest.mark.gpu

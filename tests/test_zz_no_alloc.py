@@ -2,16 +2,12 @@
 workspace) against moe_forward_layer on the same inputs: two calls in a row, the second smaller,
 each bit-identical to the workspace entry point (same kernels, deterministic); sizes past the
 fixed scratch are refused before any launch."""
-import ctypes
-
-import numpy as np
 import pytest
 import torch
 
 from oracle import oracle
 from workload import gen
-from bit_moe_expert_amd import moe
-from gpu_inputs import DEV, bf16_dev, check_y, layer_dev
+from gpu_inputs import bf16_dev, check_y, layer_dev
 
 pytestmark = pytest.mark.gpu
 
