@@ -52,7 +52,9 @@ def test_dequant_bit_exact_workload_and_exhaustive_scales():
     sf = (sbits.astype(np.uint32) << 16).view(np.float32)
     b = oracle.round_bf16(-8.0 * sf)
     rng = np.random.default_rng(5)
-    b2 = oracle.round_bf16(rng.standard_normal(n).astype(np.float32) * sf * rng.uniform(0, 20, n).astype(np.float32))
+    # random biases up to 20 scales, clipped to the finite bf16 range (large scales would overflow)
+    b2f = np.clip(rng.standard_normal(n) * sf.astype(np.float64) * rng.uniform(0, 20, n), -3.38e38, 3.38e38)
+    b2 = oracle.round_bf16(b2f.astype(np.float32))
     for bias in (b, b2):
         p = {"codes": codes, "scales": sbits.reshape(n, 1), "biases": bias.reshape(n, 1)}
         got = bits_host(moe.debug_dequant(proj_dev(p)))
