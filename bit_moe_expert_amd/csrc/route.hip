@@ -37,24 +37,20 @@ hipError_t launch_decode_topk(const Ctx& c) {
 
 // ---------------------------------------------------------------------------------------------
 // Prefill (T >= 2) logits: a block owns TOK tokens (4, 8 or 16) x 64 experts (lane = expert). The
-// block stages the tokens' inputs in LDS as fp32 [input][token]; its 16 waves take the 64-input
+// block stages the tokens' inputs in LDS as fp32 [token][input]; its 16 waves take the 64-input
 // chunks w, w + 16, ...: a wave holds the chunk's 64 router values of its expert in registers and
-// runs one fma chain per token over ascending inputs, so each router value feeds TOK chains. The
-// chunk partials meet in LDS and one thread per (token, expert) adds them in chunk order, then the
-// bias. 16384 / TOK inputs are staged per pass (64 KB in every case; larger d in passes). More
+// runs one fma chain per token over ascending inputs (on the matrix cores, below), so each router
+// value feeds TOK chains. The chunk partials meet in LDS and one thread per (token, expert) adds them
+// in chunk order, then the bias. 16384 / TOK inputs are staged per pass (64 KB in every case; larger d in passes). More
 // tokens per block mean fewer router loads per fma but fewer blocks: the launch takes the most
 // tokens per block that still give 256 blocks, and 4 when none does (small calls, where the block
 // count is what matters). The (token block, expert block) items are dealt to the 8 XCDs (block b
 // runs on XCD b % 8) in contiguous ranges of expert-block-major order, so each XCD's L2 fetches the
 // router columns of only the expert blocks it works on instead of the whole matrix.
-// With 4 tokens per block (grids too small to fill the chip, where each block's load latency is
-// on the critical path) loads run ahead of their use: a wave's first router values go out with the
-// first inputs, each router value of the wave's next chunk is loaded into its register right after
-// its last fma in the current chunk, and the next pass's inputs are loaded into registers while
-// the current pass computes (1 us less at 128 blocks; with 8 or 16 tokens, where the other waves
-// of a SIMD already cover the latency, it was up to 1 us slower). Otherwise a wave loads a chunk's
-// router values when it starts the chunk, and a pass's inputs when the pass starts. Either way the
-// arithmetic and its order are those of one chunk at a time.
+// Loads run ahead of their use: a wave's first router values go out with the first inputs, each
+// router value of the wave's next chunk is loaded into its register right after its last use in
+// the current chunk, and the next pass's inputs are loaded into registers while the current pass
+// computes. The arithmetic and its order are those of one chunk at a time.
 constexpr int kRpWaves = 16;
 
 template <int TOK>
@@ -64,7 +60,9 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
   constexpr int kMaxD = 16384 / TOK;              // inputs staged per pass
   constexpr int kMaxChunks = kMaxD / kGroup;      // a multiple of kRpWaves
   constexpr int kH = kMaxD / 1024;                // inputs per thread and pass
-  __shared__ __attribute__((aligned(16))) float s_x[kMaxD][TOK];  // 64 KB, [input][token]
+  // [token][input], each row 16 bytes longer so the 4 rows one MFMA operand read touches start in
+  // different banks
+  __shared__ __attribute__((aligned(16))) float s_x[TOK][kMaxD + 4];
   __shared__ float s_parts[kMaxChunks][TOK][64];                  // 64 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nbx = (T + TOK - 1) / TOK, total = nbx * ((E + 63) / 64);
@@ -92,7 +90,6 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
       }
     }
   };
-  constexpr bool kAhead = TOK == 4;
   float wv[kGroup];  // router values of the wave's current chunk
   const auto wcol = [&](int c) __attribute__((always_inline)) { return wr + (size_t)c * kGroup * E + ec; };
   const auto load_w = [&](int c) __attribute__((always_inline)) {
@@ -101,58 +98,64 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
     for (int i = 0; i < kGroup; ++i) wv[i] = wp[(size_t)i * E];
   };
   load_x(0);
-  if (kAhead && wave < nchunks) load_w(wave);
+  if (wave < nchunks) load_w(wave);
   float acc = 0.0f;
   for (int p = 0; p < nchunks; p += kMaxChunks) {
     const int npass = min(kMaxChunks, nchunks - p);
     const int nin = npass * kGroup;
-    if (!kAhead && p > 0) load_x(p);
 #pragma unroll
     for (int h = 0; h < kH; ++h) {
       const int i = tid + 1024 * h;
       if (i < nin) {
-        float4* dst = reinterpret_cast<float4*>(&s_x[i][0]);
 #pragma unroll
-        for (int q = 0; q < TOK / 4; ++q)
-          dst[q] = make_float4(bf16_to_f32(v[h][4 * q]), bf16_to_f32(v[h][4 * q + 1]), bf16_to_f32(v[h][4 * q + 2]),
-                               bf16_to_f32(v[h][4 * q + 3]));
+        for (int tk = 0; tk < TOK; ++tk) s_x[tk][i] = bf16_to_f32(v[h][tk]);
       }
     }
     // (a barrier waits for all of the thread's loads, so the next pass's inputs go out after it)
     __syncthreads();
-    if (kAhead && p + kMaxChunks < nchunks) load_x(p + kMaxChunks);
+    if (p + kMaxChunks < nchunks) load_x(p + kMaxChunks);
     for (int cc = wave; cc < npass; cc += kRpWaves) {
-      if (!kAhead) load_w(p + cc);
       const int cn = p + cc + kRpWaves;  // the wave's next chunk (this pass or the next)
       const float* wn = wcol(min(cn, nchunks - 1));
-      float pr[TOK];
+      // The chains run on the matrix cores: v_mfma_f32_4x4x1_16b_f32 is 16 independent 4 x 4 outer
+      // products with K = 1, and each of its outputs is one a * b + c rounded once, as fmaf (checked
+      // bit for bit on gfx950 against fmaf chains, subnormal results and signed zeros included). Lane
+      // L = 4 blk + j gives B = its expert's router value and A = the value of token 4 g + (L & 3);
+      // register r of lane L then accumulates token 4 g + r for expert L. One MFMA per input and
+      // group of 4 tokens replaces 4 fmas per lane, and the chain keeps its order: ascending inputs
+      // from +0.
+      f32x4_t pr[TOK / 4];
 #pragma unroll
-      for (int tk = 0; tk < TOK; ++tk) pr[tk] = 0.0f;
+      for (int g = 0; g < TOK / 4; ++g) pr[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       // two copies of the chunk, with and without the next chunk's loads (a per-value condition
       // would keep both values of every register alive)
       const auto chunk = [&](auto refill) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-          float xs[TOK];
+        for (int i4 = 0; i4 < kGroup / 4; ++i4) {
+          float4 xa[TOK / 4];  // inputs 4 i4 .. 4 i4 + 3 of token 4 g + (lane & 3)
 #pragma unroll
-          for (int q = 0; q < TOK / 4; ++q) {
-            const float4 xq = *reinterpret_cast<const float4*>(&s_x[cc * kGroup + i][4 * q]);
-            xs[4 * q] = xq.x;
-            xs[4 * q + 1] = xq.y;
-            xs[4 * q + 2] = xq.z;
-            xs[4 * q + 3] = xq.w;
+          for (int g = 0; g < TOK / 4; ++g)
+            xa[g] = *reinterpret_cast<const float4*>(&s_x[4 * g + (lane & 3)][cc * kGroup + 4 * i4]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 4 * i4 + q;
+#pragma unroll
+            for (int g = 0; g < TOK / 4; ++g) {
+              const float xv = q == 0 ? xa[g].x : q == 1 ? xa[g].y : q == 2 ? xa[g].z : xa[g].w;
+              pr[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(xv, wv[i], pr[g], 0, 0, 0);
+            }
+            if constexpr (decltype(refill)::value) wv[i] = wn[(size_t)i * E];
           }
-#pragma unroll
-          for (int tk = 0; tk < TOK; ++tk) pr[tk] = fmaf(xs[tk], wv[i], pr[tk]);
-          if constexpr (decltype(refill)::value) wv[i] = wn[(size_t)i * E];
         }
       };
-      if (kAhead && cn < nchunks)
+      if (cn < nchunks)
         chunk(std::true_type{});
       else
         chunk(std::false_type{});
 #pragma unroll
-      for (int tk = 0; tk < TOK; ++tk) s_parts[cc][tk][lane] = pr[tk];
+      for (int g = 0; g < TOK / 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_parts[cc][4 * g + r][lane] = pr[g][r];
     }
     __syncthreads();
     if (tid < TOK * 64)
