@@ -435,6 +435,28 @@ int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* o
   return moe_debug_dequant_bits(w, rows, in_dim, 4, out_bf16, stream);
 }
 
+int moe_debug_router_logits(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+                            const float* logit_bias, float* out, void* stream) {
+  if (int rc = check_dims(dims, T)) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16)) return fail(MOE_EINVAL, "x NULL or not 16-byte aligned");
+  if (!w_router || !aligned(w_router, 16)) return fail(MOE_EINVAL, "w_router NULL or not 16-byte aligned");
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(MOE_EINVAL, "logit_bias not 4-byte aligned");
+  if (!out || !aligned(out, 16)) return fail(MOE_EINVAL, "out NULL or not 16-byte aligned");
+  Ctx c{};  // the router kernel reads only the fields set below
+  c.T = T;
+  c.d = dims->d_model;
+  c.E = dims->n_experts;
+  c.x = x;
+  c.w_router = w_router;
+  c.logit_bias = logit_bias;
+  c.logits = out;
+  c.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = launch_router_prefill(c);
+  if (e != hipSuccess) return fail(MOE_EHIP, "launch of router_prefill failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 int moe_debug_grouped_gemm(const moe_dims* dims, int32_t T, int32_t which, const uint16_t* a,
                            const moe_routing* routing, const moe_ffn_q4* routed, const moe_ffn_q4* shared, float* out,
                            float* out2, void* ws, size_t ws_bytes, void* stream) {

@@ -76,6 +76,7 @@ def lib():
         L.moe_debug_dequant.argtypes = [P(Q4), i64, i32, vp, vp]
         L.moe_debug_dequant_bits.argtypes = [P(Q4), i64, i32, i32, vp, vp]
         L.moe_debug_grouped_gemm.argtypes = [P(Dims), i32, i32, vp, P(Routing), P(FFNQ4), P(FFNQ4), vp, vp, vp, sz, vp]
+        L.moe_debug_router_logits.argtypes = [P(Dims), i32, vp, vp, vp, vp, vp]
         L.moe_num_stages.argtypes = [P(Dims), i32]
         L.moe_num_stages.restype = i32
         L.moe_stage_name.argtypes = [P(Dims), i32, i32]
@@ -346,6 +347,28 @@ def forward_layer(x: torch.Tensor, w_router: torch.Tensor, routed: QuantFFN, sha
                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_forward_layer: route + expert FFN + combine for T tokens."""
     return Layer(w_router, routed, shared, k, logit_bias).forward(x, ws, y)
+
+
+def debug_router_logits(x: torch.Tensor, w_router: torch.Tensor,
+                        logit_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_debug_router_logits: fp32 logits [T][E] from the router kernel of calls of more than 32
+    tokens, whatever T (for bit-for-bit comparison)."""
+    if x.dim() != 2 or w_router.dim() != 2 or w_router.shape[0] != x.shape[1]:
+        raise _shape_error("moe_debug_router_logits", f"x {tuple(x.shape)} and w_router {tuple(w_router.shape)} "
+                           "must be [T][d] and [d][E]")
+    T, d = x.shape
+    E = w_router.shape[1]
+    dims = make_dims(d, E, 1, 64, 0)
+    if logit_bias is not None and logit_bias.numel() != E:
+        raise _shape_error("moe_debug_router_logits", f"logit_bias holds {logit_bias.numel()} values, expected {E}")
+    dev = x.device
+    out = torch.empty((T, E), dtype=torch.float32, device=dev)
+    rc = lib().moe_debug_router_logits(ctypes.byref(dims), T, _ptr(x, torch.bfloat16, "x", dev),
+                                       _ptr(w_router, torch.float32, "w_router", dev),
+                                       _ptr(logit_bias, torch.float32, "logit_bias", dev), _ptr(out, torch.float32, "out", dev),
+                                       _stream(dev))
+    _check(rc, "moe_debug_router_logits")
+    return out
 
 
 def debug_dequant(p: QProj) -> torch.Tensor:

@@ -206,6 +206,16 @@ int moe_debug_dequant(const moe_q4* w, int64_t rows, int32_t in_dim, uint16_t* o
 int moe_debug_dequant_bits(const moe_q4* w, int64_t rows, int32_t in_dim, int32_t bits, uint16_t* out_bf16,
                            void* stream);
 
+/* Check export of the router (test use): out = logits [T][E] fp32 of T >= 1 tokens, in the fixed
+ * order of moe_route (chunks of 64 inputs, each an fma chain in ascending i from +0, the chunk
+ * partials added in ascending order, then logit_bias), computed by the router kernel of calls of
+ * more than 32 tokens whatever T, so its logits can be compared bit for bit (the router scores every
+ * expert: "Perplexity's Lily Beats MLX-LM on MacBook M5. Because It Only Runs One Model.", section
+ * "Why Qwen3.6-35B-A3B is a weird workload"). Only d_model and n_experts of `dims` matter beyond
+ * validation. x and w_router 16-byte aligned, out 16-byte aligned; same status codes as moe_route. */
+int moe_debug_router_logits(const moe_dims* dims, int32_t T, const uint16_t* x, const float* w_router,
+                            const float* logit_bias, float* out, void* stream);
+
 /* Check export of the grouped GEMMs (test use): runs one of the two grouped-GEMM kernels over the
  * block map of `routing` (as written by moe_route for these dims and T), with the same unpacking of
  * the codes, LDS stages and scale/bias slots as moe_expert_ffn's grouped path, and writes its fp32

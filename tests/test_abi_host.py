@@ -322,3 +322,21 @@ def test_binding_checks_shapes_before_the_library():
     # the well-formed arguments get past every shape check (and then need a GPU tensor)
     with pytest.raises(ValueError, match="GPU tensor"):
         moe.expert_ffn(x, r, routed, shared)
+
+
+def test_debug_router_logits_validation():
+    """moe_debug_router_logits validates like moe_route, before any HIP call."""
+    f = _Fake()
+    d = _dims()
+    L = moe.lib()
+
+    def rl(T=8, **o):
+        return L.moe_debug_router_logits(ctypes.byref(o.get("dims", d)), T, o.get("x", f()), o.get("wr", f()),
+                                         o.get("bias", None), o.get("out", f()), None)
+    assert rl(T=0) == moe.MOE_OK
+    assert rl(T=-1) == moe.MOE_EINVAL
+    assert rl(x=None) == moe.MOE_EINVAL
+    assert rl(wr=f() + 4) == moe.MOE_EINVAL
+    assert rl(out=None) == moe.MOE_EINVAL
+    assert rl(bias=f() + 2) == moe.MOE_EINVAL
+    assert rl(dims=_dims(g=32)) == moe.MOE_EUNSUPPORTED

@@ -93,6 +93,25 @@ def test_route_small_shapes(T, E, k, Is):
 # Calls of more than 32768 pairs take the sliced metadata (per-slice histograms, one scan block,
 # per-slice ranks); 32768 pairs and fewer take the single launch. Both sides of the switch, one
 # expert, a partial last slice and groups far longer than a slice.
+# (T, d, E, Zipf bias): 4, 8 and 16 tokens per block, one to eight staging passes, ragged expert blocks
+LOGIT_CASES = [(1, 256, 16, False), (7, 512, 64, False), (64, 320, 300, False), (512, 2048, 256, False),
+               (1024, 2048, 256, True), (33, 16384, 8, False), (512, 16384, 256, False), (300, 2048, 1024, True)]
+
+
+@pytest.mark.parametrize("T,d,E,zipf", LOGIT_CASES)
+def test_router_logits_bit_exact(T, d, E, zipf):
+    """The grouped path's router logits equal the oracle's fixed-order fp32 chains bit for bit: its fma
+    chains run as K = 1 fp32 MFMAs, each step rounded once as fmaf."""
+    w = _custom(T, d, E, min(8, E), 64, 0, sigma=0.02, seed=T + d + E, zipf=zipf)
+    x = gen.tokens(w, 0, 0)
+    wr = gen.router(w, 0)
+    bias = gen.logit_bias(w)
+    got = moe.debug_router_logits(bf16_dev(x), f32_dev(wr), f32_dev(bias)).cpu().numpy()
+    ref = oracle.router_logits(x, wr, bias).astype(np.float32)
+    diff = got.view(np.uint32) != ref.view(np.uint32)
+    assert not diff.any(), f"{int(diff.sum())} of {diff.size} logits differ, first at {np.argwhere(diff)[0]}"
+
+
 @pytest.mark.parametrize("T,E,k,Is", [(4096, 256, 8, 64), (4097, 256, 8, 64), (40000, 1, 1, 0), (33000, 300, 5, 64),
                                       (65536, 16, 16, 0)])
 def test_route_sliced_metadata(T, E, k, Is):
