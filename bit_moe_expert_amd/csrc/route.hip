@@ -36,58 +36,65 @@ hipError_t launch_decode_topk(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill (T >= 2) logits: a block owns TOK tokens (4, 8 or 16) x 64 experts (lane = expert). The
-// block stages the tokens' inputs in LDS as fp32 [token][input]; its 16 waves take the 64-input
-// chunks w, w + 16, ...: a wave holds the chunk's 64 router values of its expert in registers and
-// runs one fma chain per token over ascending inputs (on the matrix cores, below), so each router
-// value feeds TOK chains. The chunk partials meet in LDS and one thread per (token, expert) adds them
-// in chunk order, then the bias. 16384 / TOK inputs are staged per pass (64 KB in every case; larger d in passes). More
-// tokens per block mean fewer router loads per fma but fewer blocks: the launch takes the most
-// tokens per block that still give 256 blocks, and 4 when none does (small calls, where the block
-// count is what matters). The (token block, expert block) items are dealt to the 8 XCDs (block b
-// runs on XCD b % 8) in contiguous ranges of expert-block-major order, so each XCD's L2 fetches the
-// router columns of only the expert blocks it works on instead of the whole matrix.
+// Prefill (T >= 2) logits: a block owns TOK tokens x EB experts (EB = 64 or 32). The block
+// stages the tokens' inputs in LDS as fp32 [token][input]; its 16 waves take the 64-input chunks
+// w, w + 16, ...: a wave holds the chunk's 64 router values of its lanes' experts in registers and
+// runs one fma chain per (token, expert) over ascending inputs (on the matrix cores, below), so each
+// router value feeds TOK chains. With EB = 32 the two halves of a wave hold the same 32 experts for
+// different tokens, so 8 tokens per block keep a whole wave busy. The chunk partials meet in LDS
+// and one thread per (token, expert) adds them in chunk order, then the bias. 16384 / TOK inputs
+// are staged per pass (64 KB in every case; larger d in passes). More tokens per block mean fewer
+// router loads per fma but fewer blocks: the launch takes 16 tokens x 64 experts when that still
+// gives 256 blocks, else 8 x 64 when that does, else 8 x 32 (small calls, where the block count is
+// what matters: the same blocks as 4 x 64, each reading half the router bytes). The (token block,
+// expert block) items are dealt to the 8 XCDs (block b runs on XCD b % 8) in contiguous ranges of
+// expert-block-major order, so each XCD's L2 fetches the router columns of only the expert blocks
+// it works on instead of the whole matrix.
 // Loads run ahead of their use: a wave's first router values go out with the first inputs, each
 // router value of the wave's next chunk is loaded into its register right after its last use in
 // the current chunk, and the next pass's inputs are loaded into registers while the current pass
 // computes. The arithmetic and its order are those of one chunk at a time.
 constexpr int kRpWaves = 16;
 
-template <int TOK>
+template <int TOK, int EB>
 __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, const uint16_t* __restrict__ x,
                                                          const float* __restrict__ wr, const float* __restrict__ bias,
                                                          float* __restrict__ logits) {
-  constexpr int kMaxD = 16384 / TOK;              // inputs staged per pass
-  constexpr int kMaxChunks = kMaxD / kGroup;      // a multiple of kRpWaves
-  constexpr int kH = kMaxD / 1024;                // inputs per thread and pass
-  // [token][input], each row 16 bytes longer so the 4 rows one MFMA operand read touches start in
+  constexpr int kMaxD = 16384 / TOK;          // inputs staged per pass
+  constexpr int kMaxChunks = kMaxD / kGroup;  // a multiple of kRpWaves
+  constexpr int kNV = TOK * kMaxD / 1024;     // staged values per thread and pass
+  constexpr int kTG = 256 / EB;               // tokens per MFMA: 4 (EB = 64) or 8 (EB = 32)
+  constexpr int kNG = TOK / kTG;              // MFMAs per input
+  static_assert((EB == 64 || EB == 32) && TOK % kTG == 0 && TOK <= 16 && kMaxChunks % kRpWaves == 0, "block shape");
+  // [token][input], each row 16 bytes longer so the rows one MFMA operand read touches start in
   // different banks
   __shared__ __attribute__((aligned(16))) float s_x[TOK][kMaxD + 4];
-  __shared__ float s_parts[kMaxChunks][TOK][64];                  // 64 KB
+  __shared__ float s_parts[kMaxChunks][TOK][EB];  // 64 KB (EB = 64) or 32 KB
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nbx = (T + TOK - 1) / TOK, total = nbx * ((E + 63) / 64);
+  const int nbx = (T + TOK - 1) / TOK, total = nbx * ((E + EB - 1) / EB);
   const int per = (total + 7) / 8;  // items per XCD
   const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (item >= total) return;
   const int by = item / nbx, bx = item - by * nbx;  // expert block, token block
   const int t0 = bx * TOK;
-  const int e = by * 64 + lane;
+  const int e = by * EB + (lane & (EB - 1));
   const int ec = e < E ? e : E - 1;  // experts past E compute a copy that is never stored
+  // lane L's tokens: kTG g + tl + (L & 3) in the A operand of group g, and kTG g + tl + r in its
+  // output register r (with EB = 32 the upper half of the wave takes the group's last 4 tokens)
+  const int tl = 4 * (lane / EB);
   const int nchunks = d / kGroup;
-  const int s_tok = tid >> 6, s_e = by * 64 + lane;  // sum phase: threads 0 .. 64 TOK - 1
-  // inputs p*64 .. p*64 + nin of the tokens into registers: thread i takes inputs i, i + 1024, ...
-  uint16_t v[kH][TOK];
+  const int s_tok = tid / EB, s_e = by * EB + (tid & (EB - 1));  // sum phase: threads 0 .. TOK EB - 1
+  // inputs p*64 .. p*64 + nin of the tokens into registers: value q of a thread is (token, input)
+  // = divmod(tid + 1024 q, kMaxD), so consecutive threads load consecutive inputs of one token
+  uint16_t v[kNV];
   const auto load_x = [&](int p) __attribute__((always_inline)) {
     const int nin = min(kMaxChunks, nchunks - p) * kGroup;
 #pragma unroll
-    for (int h = 0; h < kH; ++h) {
-      const int i = tid + 1024 * h;
+    for (int q = 0; q < kNV; ++q) {
+      const int f = tid + 1024 * q, tk = f / kMaxD, i = f % kMaxD;
       const int ic = i < nin ? i : 0;
-#pragma unroll
-      for (int tk = 0; tk < TOK; ++tk) {
-        const int t = min(t0 + tk, T - 1);
-        v[h][tk] = x[(size_t)t * d + (size_t)p * kGroup + ic];
-      }
+      const int t = min(t0 + tk, T - 1);
+      v[q] = x[(size_t)t * d + (size_t)p * kGroup + ic];
     }
   };
   float wv[kGroup];  // router values of the wave's current chunk
@@ -104,12 +111,9 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
     const int npass = min(kMaxChunks, nchunks - p);
     const int nin = npass * kGroup;
 #pragma unroll
-    for (int h = 0; h < kH; ++h) {
-      const int i = tid + 1024 * h;
-      if (i < nin) {
-#pragma unroll
-        for (int tk = 0; tk < TOK; ++tk) s_x[tk][i] = bf16_to_f32(v[h][tk]);
-      }
+    for (int q = 0; q < kNV; ++q) {
+      const int f = tid + 1024 * q, tk = f / kMaxD, i = f % kMaxD;
+      if (i < nin) s_x[tk][i] = bf16_to_f32(v[q]);
     }
     // (a barrier waits for all of the thread's loads, so the next pass's inputs go out after it)
     __syncthreads();
@@ -120,27 +124,27 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
       // The chains run on the matrix cores: v_mfma_f32_4x4x1_16b_f32 is 16 independent 4 x 4 outer
       // products with K = 1, and each of its outputs is one a * b + c rounded once, as fmaf (checked
       // bit for bit on gfx950 against fmaf chains, subnormal results and signed zeros included). Lane
-      // L = 4 blk + j gives B = its expert's router value and A = the value of token 4 g + (L & 3);
-      // register r of lane L then accumulates token 4 g + r for expert L. One MFMA per input and
-      // group of 4 tokens replaces 4 fmas per lane, and the chain keeps its order: ascending inputs
-      // from +0.
-      f32x4_t pr[TOK / 4];
+      // L = 4 blk + j gives B = its expert's router value and A = the value of its A token; register
+      // r of lane L then accumulates the lane's r-th output token for expert e. One MFMA per input
+      // and group of kTG tokens replaces kTG fmas per expert, and the chain keeps its order:
+      // ascending inputs from +0.
+      f32x4_t pr[kNG];
 #pragma unroll
-      for (int g = 0; g < TOK / 4; ++g) pr[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int g = 0; g < kNG; ++g) pr[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       // two copies of the chunk, with and without the next chunk's loads (a per-value condition
       // would keep both values of every register alive)
       const auto chunk = [&](auto refill) __attribute__((always_inline)) {
 #pragma unroll
         for (int i4 = 0; i4 < kGroup / 4; ++i4) {
-          float4 xa[TOK / 4];  // inputs 4 i4 .. 4 i4 + 3 of token 4 g + (lane & 3)
+          float4 xa[kNG];  // inputs 4 i4 .. 4 i4 + 3 of the lane's A token of each group
 #pragma unroll
-          for (int g = 0; g < TOK / 4; ++g)
-            xa[g] = *reinterpret_cast<const float4*>(&s_x[4 * g + (lane & 3)][cc * kGroup + 4 * i4]);
+          for (int g = 0; g < kNG; ++g)
+            xa[g] = *reinterpret_cast<const float4*>(&s_x[kTG * g + tl + (lane & 3)][cc * kGroup + 4 * i4]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int i = 4 * i4 + q;
 #pragma unroll
-            for (int g = 0; g < TOK / 4; ++g) {
+            for (int g = 0; g < kNG; ++g) {
               const float xv = q == 0 ? xa[g].x : q == 1 ? xa[g].y : q == 2 ? xa[g].z : xa[g].w;
               pr[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(xv, wv[i], pr[g], 0, 0, 0);
             }
@@ -153,16 +157,16 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
       else
         chunk(std::false_type{});
 #pragma unroll
-      for (int g = 0; g < TOK / 4; ++g)
+      for (int g = 0; g < kNG; ++g)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_parts[cc][4 * g + r][lane] = pr[g][r];
+        for (int r = 0; r < 4; ++r) s_parts[cc][kTG * g + tl + r][lane & (EB - 1)] = pr[g][r];
     }
     __syncthreads();
-    if (tid < TOK * 64)
-      for (int cc = 0; cc < npass; ++cc) acc = acc + s_parts[cc][s_tok][lane];
+    if (tid < TOK * EB)
+      for (int cc = 0; cc < npass; ++cc) acc = acc + s_parts[cc][s_tok][tid & (EB - 1)];
     __syncthreads();
   }
-  if (tid < TOK * 64 && t0 + s_tok < T && s_e < E) {
+  if (tid < TOK * EB && t0 + s_tok < T && s_e < E) {
     float v = acc;
     if (bias) v = v + bias[s_e];
     logits[(size_t)(t0 + s_tok) * E + s_e] = v;
@@ -170,18 +174,18 @@ __global__ __launch_bounds__(1024) void k_router_prefill(int T, int d, int E, co
 }
 
 hipError_t launch_router_prefill(const Ctx& c) {
-  const int ne = (c.E + 63) / 64;
   // one block per (token block, expert block) item, the grid rounded up to whole rounds of 8 XCDs
-  const auto grid = [&](int tok) { return dim3((unsigned)(8 * ((((c.T + tok - 1) / tok) * ne + 7) / 8))); };
-  if (((c.T + 15) / 16) * ne >= 256) {
-    hipLaunchKernelGGL(k_router_prefill<16>, grid(16), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
-                       c.logit_bias, c.logits);
-  } else if (((c.T + 7) / 8) * ne >= 256) {
-    hipLaunchKernelGGL(k_router_prefill<8>, grid(8), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
-                       c.logit_bias, c.logits);
+  const auto items = [&](int tok, int eb) { return ((c.T + tok - 1) / tok) * ((c.E + eb - 1) / eb); };
+  const auto grid = [&](int tok, int eb) { return dim3((unsigned)(8 * ((items(tok, eb) + 7) / 8))); };
+  if (items(16, 64) >= 256) {
+    hipLaunchKernelGGL((k_router_prefill<16, 64>), grid(16, 64), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x,
+                       c.w_router, c.logit_bias, c.logits);
+  } else if (items(8, 64) >= 256) {
+    hipLaunchKernelGGL((k_router_prefill<8, 64>), grid(8, 64), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x,
+                       c.w_router, c.logit_bias, c.logits);
   } else {
-    hipLaunchKernelGGL(k_router_prefill<4>, grid(4), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x, c.w_router,
-                       c.logit_bias, c.logits);
+    hipLaunchKernelGGL((k_router_prefill<8, 32>), grid(8, 32), dim3(1024), 0, c.stream, c.T, c.d, c.E, c.x,
+                       c.w_router, c.logit_bias, c.logits);
   }
   return hipGetLastError();
 }
