@@ -145,9 +145,9 @@ def stage_work(w: gen.Workload, name: str, counts: np.ndarray):
         return wb + 2 * T * d + 2 * (P * I + T * Is), 4 * d * (P * I + T * Is)
     if name == "down_gemm":
         wb = act * per_w(d, I) + (per_w(d, Is) if Is else 0)
-        return wb + 2 * (P * I + T * Is) + 4 * (P + (T if Is else 0)) * d, 2 * d * (P * I + T * Is)
-    if name == "combine":
-        return 4 * (P + (T if Is else 0)) * d + 2 * T * d + 8 * P, 2 * P * d
+        return wb + 2 * (P * I + T * Is) + (2 * d + d // 32) * (P + (T if Is else 0)), 2 * d * (P * I + T * Is)
+    if name == "combine":  # fp16 rows with one exponent byte per 32 values
+        return (2 * d + d // 32) * (P + (T if Is else 0)) + 2 * T * d + 8 * P, 2 * P * d
     raise KeyError(name)
 
 

@@ -30,6 +30,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float a) { return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu); }
 
+// Two fp32 -> packed fp16 pair (low half = a), round-to-nearest-even; and the way back.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  f32x2_t v = {a, b};
+  h2 r = __builtin_convertvector(v, h2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 // A constant the compiler must hold in a VGPR: gfx9 VOP3 encodings take no literal, so
 // (t & mask) | magic with plain constants becomes an AND and an OR; with both in registers it is
 // one v_and_or_b32. The value is loop-invariant and the asm has no side effects, so it is

@@ -20,19 +20,22 @@ hipError_t launch_down_gemm(const Ctx& c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Weighted gather back to token order: y[t] = bf16(sum_j w[t][j] * y_rows[inv_pos[t][j]] +
-// y_rows[P + t]), j ascending, in fp32. A block covers 1024 outputs of one token (one thread per
-// 4 outputs), so the token's k row indices and weights are block-uniform scalar loads.
+// Weighted gather back to token order: y[t] = bf16(sum_j w[t][j] * row(inv_pos[t][j]) + row(P + t)),
+// j ascending, in fp32, where row(i) is the down product's fp16 row i with each 32-column segment
+// multiplied back by 2^e (exact). A block covers 1024 outputs of one token (one thread per 4
+// outputs), so the token's k row indices and weights are block-uniform scalar loads.
 constexpr int kCombineThreads = 256;
 __global__ __launch_bounds__(kCombineThreads) void k_combine(int T, int d, int k, int P, int has_shared,
                                                              const int32_t* __restrict__ inv_pos,
                                                              const float* __restrict__ w,
-                                                             const float* __restrict__ y_rows, uint16_t* __restrict__ y) {
+                                                             const uint16_t* __restrict__ y_rows,
+                                                             const uint8_t* __restrict__ y_exp,
+                                                             uint16_t* __restrict__ y) {
   const int nb = (d + 4 * kCombineThreads - 1) / (4 * kCombineThreads);  // blocks per token
   const int t = blockIdx.x / nb;
   const int o = ((blockIdx.x % nb) * kCombineThreads + threadIdx.x) * 4;
   if (t >= T || o >= d) return;
-  // every index and row load is issued before the first add
+  // every index, row and exponent load is issued before the first add
   int row[kMaxTopK];
   float wj[kMaxTopK];
 #pragma unroll
@@ -40,25 +43,33 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(int T, int d, int k
     row[j] = j < k ? inv_pos[(size_t)t * k + j] : -1;
     wj[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
-  float4 v[kMaxTopK], vs = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int seg = o / 32, nseg = d / 32;
+  uint2 q[kMaxTopK], qs = make_uint2(0u, 0u);
+  int ej[kMaxTopK], es = 0;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
-    if ((unsigned)row[j] < (unsigned)P) v[j] = *reinterpret_cast<const float4*>(y_rows + (size_t)row[j] * d + o);
-  if (has_shared) vs = *reinterpret_cast<const float4*>(y_rows + (size_t)(P + t) * d + o);
+    if ((unsigned)row[j] < (unsigned)P) {
+      q[j] = *reinterpret_cast<const uint2*>(y_rows + (size_t)row[j] * d + o);
+      ej[j] = y_exp[(size_t)row[j] * nseg + seg];
+    }
+  if (has_shared) {
+    qs = *reinterpret_cast<const uint2*>(y_rows + (size_t)(P + t) * d + o);
+    es = y_exp[(size_t)(P + t) * nseg + seg];
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
     if ((unsigned)row[j] < (unsigned)P) {
-      acc.x = fmaf(wj[j], v[j].x, acc.x);
-      acc.y = fmaf(wj[j], v[j].y, acc.y);
-      acc.z = fmaf(wj[j], v[j].z, acc.z);
-      acc.w = fmaf(wj[j], v[j].w, acc.w);
+      acc.x = fmaf(wj[j], __builtin_ldexpf(f16lo(q[j].x), ej[j]), acc.x);
+      acc.y = fmaf(wj[j], __builtin_ldexpf(f16hi(q[j].x), ej[j]), acc.y);
+      acc.z = fmaf(wj[j], __builtin_ldexpf(f16lo(q[j].y), ej[j]), acc.z);
+      acc.w = fmaf(wj[j], __builtin_ldexpf(f16hi(q[j].y), ej[j]), acc.w);
     }
   if (has_shared) {
-    acc.x += vs.x;
-    acc.y += vs.y;
-    acc.z += vs.z;
-    acc.w += vs.w;
+    acc.x += __builtin_ldexpf(f16lo(qs.x), es);
+    acc.y += __builtin_ldexpf(f16hi(qs.x), es);
+    acc.z += __builtin_ldexpf(f16lo(qs.y), es);
+    acc.w += __builtin_ldexpf(f16hi(qs.y), es);
   }
   uint2 out;
   out.x = pack_bf16x2(acc.x, acc.y);
@@ -69,7 +80,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(int T, int d, int k
 hipError_t launch_combine(const Ctx& c) {
   const int nb = (c.d + 4 * kCombineThreads - 1) / (4 * kCombineThreads);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((size_t)c.T * nb)), dim3(kCombineThreads), 0, c.stream, c.T, c.d, c.k,
-                     c.P, c.Is > 0 ? 1 : 0, c.r.inv_pos, c.r.topk_w, c.y_rows, c.y);
+                     c.P, c.Is > 0 ? 1 : 0, c.r.inv_pos, c.r.topk_w, c.y_rows, c.y_exp, c.y);
   return hipGetLastError();
 }
 

@@ -19,6 +19,8 @@
 // move to LDS and become "128 + q" pairs.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,12 +40,14 @@ struct GemmArgs {
   moe_ffn_q4 routed, shared;
   uint16_t* h;
   uint16_t* hs;
-  float* y_rows;
+  uint16_t* y_rows;  // fp16 rows of the down product, each 32-column segment scaled by 2^-e ...
+  uint8_t* y_exp;    // ... e per (row, segment)
   const float* xsum;  // [T][d/64] group sums of x (the bias term's factor on the gate/up side)
   float* hsum;        // [P][I/64] group sums of h (written by the gate/up epilogue, read by down)
   float* hsum_sh;     // [T][Is/64] the same for the shared expert's h
   float* dbg_g;  // check export of the gate/up kernel: fp32 g and u, [P][I] then [T][Is]
   float* dbg_u;
+  float* dbg_y;  // check export of the down kernel: its fp32 rows, [P + T][d]
 };
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
@@ -651,7 +655,8 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
           v += dpp_f32<0x128>(v);
           hpart[mm][r] = v;
         }
-    } else {
+    } else if (DBG) {
+      // the check export: the fp32 rows themselves
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int col = n0 + 32 * wave + 16 * t + n;
@@ -661,8 +666,58 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = 16 * mm + 4 * kb + r;
-            if (row < rows) a.y_rows[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
+            if (row < rows) a.dbg_y[(size_t)(row0 + row) * d + col] = acc[t][mm][r];
           }
+      }
+    } else if (n0 + 32 * wave < d) {  // d is a multiple of 64: the wave's 32 columns are whole
+      // fp16 rows. The wave's 32 columns of a row form one segment with an exponent e >= 0 that
+      // keeps the segment's largest magnitude below 2^15; the segment is stored as
+      // fp16(v * 2^-e) (the scaling is exact), so any fp32 range survives with fp16's 11-bit
+      // precision, and e goes to y_exp. First a 4 x 4 transpose within each quad of lanes turns the
+      // MFMA layout (lane = column, register = row) into 4 consecutive columns of one row per lane
+      // (row 4 kb + (n & 3), columns 4 (n >> 2) .. + 3 of each 16-column half), so each lane
+      // stores 8 bytes per half. The lane shuffles run in every lane, outside any condition.
+      const int cw = n0 + 32 * wave;
+      const bool q0 = (n & 1) != 0, q1 = (n & 2) != 0;
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) {
+        float tv[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4_t m = acc[t][mm];
+          const float s0 = dpp_f32<0xB1>(m[0]), s1 = dpp_f32<0xB1>(m[1]);  // quad_perm 1,0,3,2
+          const float s2 = dpp_f32<0xB1>(m[2]), s3 = dpp_f32<0xB1>(m[3]);
+          const float b0 = q0 ? s1 : m[0], b1 = q0 ? m[1] : s0, b2 = q0 ? s3 : m[2], b3 = q0 ? m[3] : s2;
+          const float u0 = dpp_f32<0x4E>(b0), u1 = dpp_f32<0x4E>(b1);  // quad_perm 2,3,0,1
+          const float u2 = dpp_f32<0x4E>(b2), u3 = dpp_f32<0x4E>(b3);
+          tv[t][0] = q1 ? u2 : b0;
+          tv[t][1] = q1 ? u3 : b1;
+          tv[t][2] = q1 ? b2 : u0;
+          tv[t][3] = q1 ? b3 : u1;
+        }
+        // the row's largest magnitude (max ignores NaN): the lane's 8 values, then lanes n + 4, n + 8
+        // (mod 16), which hold the same row
+        float mx = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(tv[t][r]));
+        mx = fmaxf(mx, dpp_f32<0x124>(mx));  // row_ror 4
+        mx = fmaxf(mx, dpp_f32<0x128>(mx));  // row_ror 8
+        // mx < 2^(be - 126) for biased exponent be, so e = be - 141 brings it below 2^15
+        const int e = max(0, (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 141);
+        const int row = 16 * mm + 4 * kb + (n & 3);
+        if (row < rows) {
+          uint16_t* yr = a.y_rows + (size_t)(row0 + row) * d + cw + 4 * (n >> 2);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            uint2 hv;
+            hv.x = pack_f16x2(__builtin_ldexpf(tv[t][0], -e), __builtin_ldexpf(tv[t][1], -e));
+            hv.y = pack_f16x2(__builtin_ldexpf(tv[t][2], -e), __builtin_ldexpf(tv[t][3], -e));
+            *reinterpret_cast<uint2*>(yr + 16 * t) = hv;
+          }
+          if ((n >> 2) == 0) a.y_exp[(size_t)(row0 + row) * (d / 32) + cw / 32] = (uint8_t)e;
+        }
       }
     }
 #pragma unroll
@@ -853,9 +908,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   gemm_block<BITS, true, PAIRED, kRunGu, DBG, VEC8>(a);
 }
 
-template <int BITS, bool PAIRED, int R, bool VEC8>
+// DBG: the check export (the fp32 rows instead of fp16 rows and exponents).
+template <int BITS, bool PAIRED, int R, bool DBG, bool VEC8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_gemm(GemmArgs a) {
-  gemm_block<BITS, false, PAIRED, R, false, VEC8>(a);
+  gemm_block<BITS, false, PAIRED, R, DBG, VEC8>(a);
 }
 
 inline GemmArgs gemm_args(const Ctx& c, int nruns) {
@@ -878,6 +934,8 @@ inline GemmArgs gemm_args(const Ctx& c, int nruns) {
   a.h = c.h;
   a.hs = c.hs;
   a.y_rows = c.y_rows;
+  a.y_exp = c.y_exp;
+  a.dbg_y = c.dbg_y;
   a.xsum = c.xsum;
   a.hsum = c.hsum;
   a.hsum_sh = c.hsum_sh;
@@ -912,6 +970,7 @@ hipError_t launch_gateup_gemm_bits(const Ctx& c) {
 template <int BITS>
 hipError_t launch_down_gemm_bits(const Ctx& c) {
   const int ncb = (c.d + kDnCols - 1) / kDnCols;
+  const bool dbg = c.dbg_y != nullptr;
   const int R = down_run(c.I);
   const int nruns = (ncb + R - 1) / R;
   const dim3 grid(grid_blocks(c.max_tiles, nruns));
@@ -921,12 +980,20 @@ hipError_t launch_down_gemm_bits(const Ctx& c) {
   const bool vec8 = c.I % (8 * kGroup) == 0 && (c.Is == 0 || c.Is % (8 * kGroup) == 0);
   const GemmArgs a = gemm_args(c, nruns);
   const auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, c.stream, a); };
-  if (vec8)
-    R == 1 ? go(k_down_gemm<BITS, true, 1, true>) : go(k_down_gemm<BITS, true, 2, true>);
-  else if (paired)
-    R == 1 ? go(k_down_gemm<BITS, true, 1, false>) : go(k_down_gemm<BITS, true, 2, false>);
+  // the check export runs the same block shapes with fp32 rows out
+  const auto pick = [&](auto dbg_tag) {
+    constexpr bool D = decltype(dbg_tag)::value;
+    if (vec8)
+      R == 1 ? go(k_down_gemm<BITS, true, 1, D, true>) : go(k_down_gemm<BITS, true, 2, D, true>);
+    else if (paired)
+      R == 1 ? go(k_down_gemm<BITS, true, 1, D, false>) : go(k_down_gemm<BITS, true, 2, D, false>);
+    else
+      R == 1 ? go(k_down_gemm<BITS, false, 1, D, false>) : go(k_down_gemm<BITS, false, 2, D, false>);
+  };
+  if (dbg)
+    pick(std::true_type{});
   else
-    R == 1 ? go(k_down_gemm<BITS, false, 1, false>) : go(k_down_gemm<BITS, false, 2, false>);
+    pick(std::false_type{});
   return hipGetLastError();
 }
 

@@ -29,10 +29,13 @@ struct Ctx {
   bool pair_in_meta;      // the routing-metadata launch also writes xp
   uint16_t* h;            // [P][I] bf16, grouped order (slot order at T == 1); pair order on the GEMM path
   uint16_t* hs;           // [T][Is] bf16
-  float* y_rows;          // [P + T][d] fp32, grouped order, shared rows last
+  uint16_t* y_rows;       // [P + T][d] fp16 bits, grouped order, shared rows last; each (row, 32-column
+                          // segment) holds the values times 2^-e ...
+  uint8_t* y_exp;         // [P + T][d/32] ... with the segment's e here
   uint16_t* y;            // [T][d] bf16
   float* dbg_g;           // when set, the gate/up GEMM writes fp32 g and u ([P][I] then [T][Is]) instead of h
   float* dbg_u;
+  float* dbg_y;           // when set, the down GEMM writes its fp32 rows ([P + T][d]) here instead
   hipStream_t stream;
 };
 

@@ -71,7 +71,7 @@ bool gemv_path(const moe_dims& dm, int32_t T) {
 
 struct Layout {
   size_t parts, logits, ids, w, counts, offsets, sorted, inv_pos, tiles, n_tiles, meta_hist, xp, xsum, h, hs, hsum,
-      hsum_sh, y_rows, total;
+      hsum_sh, y_rows, y_exp, total;
 };
 
 Layout layout_of(const moe_dims& dm, int32_t T) {
@@ -113,7 +113,9 @@ Layout layout_of(const moe_dims& dm, int32_t T) {
   L.hsum_sh = o;
   o += up((size_t)T * (dm.d_ff_shared / 64) * 4);
   L.y_rows = o;
-  o += up((P + T) * d * 4);
+  o += up((P + T) * d * 2);
+  L.y_exp = o;
+  o += up((P + T) * (d / 32));
   L.total = o;
   return L;
 }
@@ -236,7 +238,8 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.pair_in_meta = false;
   c.h = reinterpret_cast<uint16_t*>(b + L.h);
   c.hs = reinterpret_cast<uint16_t*>(b + L.hs);
-  c.y_rows = reinterpret_cast<float*>(b + L.y_rows);
+  c.y_rows = reinterpret_cast<uint16_t*>(b + L.y_rows);
+  c.y_exp = reinterpret_cast<uint8_t*>(b + L.y_exp);
   c.r.topk_ids = reinterpret_cast<int32_t*>(b + L.ids);
   c.r.topk_w = reinterpret_cast<float*>(b + L.w);
   c.r.counts = reinterpret_cast<int32_t*>(b + L.counts);
@@ -253,6 +256,7 @@ void fill_ctx(Ctx& c, const moe_dims& dm, int32_t T, void* ws, hipStream_t strea
   c.y = nullptr;
   c.dbg_g = nullptr;
   c.dbg_u = nullptr;
+  c.dbg_y = nullptr;
   memset(&c.routed, 0, sizeof(c.routed));
   memset(&c.shared, 0, sizeof(c.shared));
 }
@@ -483,7 +487,7 @@ int moe_debug_grouped_gemm(const moe_dims* dims, int32_t T, int32_t which, const
   e = launch_pair_rows(a, c.h, c.hsum, c.P, c.I, c.stream);
   if (e == hipSuccess && c.Is) e = launch_pair_rows(a + (size_t)c.P * c.I, c.hs, c.hsum_sh, c.T, c.Is, c.stream);
   if (e != hipSuccess) return fail(MOE_EHIP, "launch of pair_rows failed: %s", hipGetErrorString(e));
-  c.y_rows = out;
+  c.dbg_y = out;
   return run_stage(kGemmDown, c);
 }
 

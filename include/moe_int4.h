@@ -218,8 +218,9 @@ int moe_debug_router_logits(const moe_dims* dims, int32_t T, const uint16_t* x, 
 
 /* Check export of the grouped GEMMs (test use): runs one of the two grouped-GEMM kernels over the
  * block map of `routing` (as written by moe_route for these dims and T), with the same unpacking of
- * the codes, LDS stages and scale/bias slots as moe_expert_ffn's grouped path, and writes its fp32
- * results before any activation or rounding (4-bit codes only):
+ * the codes, LDS stages and scale/bias slots as moe_expert_ffn's grouped path (codes of any width
+ * dims->code_bits allows), and writes its fp32 results before any activation or rounding (the layer
+ * itself keeps the down rows as fp16 with one power-of-two exponent per 32 columns):
  *   which = 0: a = x [T][d] bf16; out = g, out2 = u, each [T*k][d_ff] fp32 in grouped row order
  *              followed by [T][d_ff_shared] for the shared expert: g = x Wg^T, u = x Wu^T.
  *   which = 1: a = h, [T*k][d_ff] bf16 in grouped row order followed by [T][d_ff_shared];
