@@ -172,6 +172,11 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// A value from another lane of the quad (quad_perm CTRL), every lane written (no old value kept).
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);

@@ -685,36 +685,37 @@ __device__ __forceinline__ void run_body(const GemmArgs& a, int run, int e, int 
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const f32x4_t m = acc[t][mm];
-          const float s0 = dpp_f32<0xB1>(m[0]), s1 = dpp_f32<0xB1>(m[1]);  // quad_perm 1,0,3,2
-          const float s2 = dpp_f32<0xB1>(m[2]), s3 = dpp_f32<0xB1>(m[3]);
+          const float s0 = quad_swap<0xB1>(m[0]), s1 = quad_swap<0xB1>(m[1]);  // quad_perm 1,0,3,2
+          const float s2 = quad_swap<0xB1>(m[2]), s3 = quad_swap<0xB1>(m[3]);
           const float b0 = q0 ? s1 : m[0], b1 = q0 ? m[1] : s0, b2 = q0 ? s3 : m[2], b3 = q0 ? m[3] : s2;
-          const float u0 = dpp_f32<0x4E>(b0), u1 = dpp_f32<0x4E>(b1);  // quad_perm 2,3,0,1
-          const float u2 = dpp_f32<0x4E>(b2), u3 = dpp_f32<0x4E>(b3);
+          const float u0 = quad_swap<0x4E>(b0), u1 = quad_swap<0x4E>(b1);  // quad_perm 2,3,0,1
+          const float u2 = quad_swap<0x4E>(b2), u3 = quad_swap<0x4E>(b3);
           tv[t][0] = q1 ? u2 : b0;
           tv[t][1] = q1 ? u3 : b1;
           tv[t][2] = q1 ? b2 : u0;
           tv[t][3] = q1 ? b3 : u1;
         }
-        // the row's largest magnitude (max ignores NaN): the lane's 8 values, then lanes n + 4, n + 8
-        // (mod 16), which hold the same row
+        // the exponent field of the row's largest magnitude (max ignores NaN): the lane's 8 values,
+        // then lanes n + 4, n + 8 (mod 16), which hold the same row
         float mx = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(tv[t][r]));
-        mx = fmaxf(mx, dpp_f32<0x124>(mx));  // row_ror 4
-        mx = fmaxf(mx, dpp_f32<0x128>(mx));  // row_ror 8
-        // mx < 2^(be - 126) for biased exponent be, so e = be - 141 brings it below 2^15
-        const int e = max(0, (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 141);
+        uint32_t be = __float_as_uint(mx) >> 23;
+        be = max(be, dpp_u32<0x124>(be));  // row_ror 4
+        be = max(be, dpp_u32<0x128>(be));  // row_ror 8
+        // the largest magnitude is below 2^(be - 126), so e = be - 141 brings it below 2^15
+        const int e = max(0, (int)be - 141);
         const int row = 16 * mm + 4 * kb + (n & 3);
         if (row < rows) {
           uint16_t* yr = a.y_rows + (size_t)(row0 + row) * d + cw + 4 * (n >> 2);
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            uint2 hv;
-            hv.x = pack_f16x2(__builtin_ldexpf(tv[t][0], -e), __builtin_ldexpf(tv[t][1], -e));
-            hv.y = pack_f16x2(__builtin_ldexpf(tv[t][2], -e), __builtin_ldexpf(tv[t][3], -e));
-            *reinterpret_cast<uint2*>(yr + 16 * t) = hv;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = __builtin_ldexpf(tv[t][r], -e);
+            *reinterpret_cast<uint2*>(yr + 16 * t) = make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
           }
           if ((n >> 2) == 0) a.y_exp[(size_t)(row0 + row) * (d / 32) + cw / 32] = (uint8_t)e;
         }
