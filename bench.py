@@ -205,25 +205,30 @@ def cpu_model() -> str:
 
 def cpu_baseline_cycle(w: gen.Workload, n_layers: int, seconds: float):
     """The oracle on the workload's own calls, layer after layer of its cycle (each layer regenerated
-    on the host between calls, outside the timed region), until the cycle is done or `seconds` of
-    oracle time have passed. Only the oracle calls are timed."""
+    on the host, outside the timed region). The first layer takes one call; every later layer takes as
+    many calls (each on its own seeded tokens) as spread about `seconds` of oracle time over the cycle,
+    and the cycle stops early once twice that has passed. Only the oracle calls are timed."""
     from oracle import oracle
-    spent, tokens, calls = 0.0, 0, 0
+    spent, tokens, calls, reps, layers = 0.0, 0, 0, 1, 0
     for li in range(n_layers):
         L = gen.layer(w, li)
-        x = gen.tokens(w, li, li if w.calls > 1 else 0)
-        t0 = time.perf_counter()
-        oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])
-        spent += time.perf_counter() - t0
-        tokens += x.shape[0]
-        calls += 1
+        for c in range(reps):
+            x = gen.tokens(w, li, (li if w.calls > 1 else 0) + c * n_layers)
+            t0 = time.perf_counter()
+            oracle.forward_layer(x, L["w_router"], L["routed"], L["shared"], w.k, L["logit_bias"])
+            spent += time.perf_counter() - t0
+            tokens += x.shape[0]
+            calls += 1
         del L
-        if spent >= seconds:
+        layers += 1
+        if li == 0:
+            reps = max(1, min(64, int(seconds / (n_layers * max(spent, 1e-6)))))
+        if spent >= 2 * seconds:
             break
     return {"value": tokens / spent, "unit": "MoE-layer tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "cpu": cpu_model(),
-            "sample": f"{calls} layer calls of {w.chunk} tokens (layers 0..{calls - 1} of the {n_layers}-layer cycle), "
-                      f"{spent:.1f} s of oracle time"}
+            "sample": f"{calls} layer calls of {w.chunk} tokens over layers 0..{layers - 1} of the {n_layers}-layer "
+                      f"cycle ({reps} per layer after the first), {spent:.1f} s of oracle time"}
 
 
 # ------------------------------------------------------------------------- exact top-K of logit rows
