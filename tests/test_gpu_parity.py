@@ -351,8 +351,8 @@ def _times_pow2_bf16(bits: np.ndarray, m: int) -> np.ndarray:
                                             (130, 320, 2, 1, 192, 64, 16), (40, 128, 8, 2, 64, 0, 15)])
 def test_grouped_rows_beyond_fp16_range(T, d, E, k, I, Is, m):
     """Down scales and biases times 2^m (exact in bf16) put the grouped down GEMM's rows and the
-    outputs beyond the fp16 range (up to about 1e6); the layer must still match the oracle, so no
-    16-bit intermediate with fp16's range may sit between the down products and the output."""
+    outputs beyond the fp16 range (up to about 1e6); the layer must still match the oracle, so the
+    rows' fp16 storage must carry their range in its per-segment power-of-two exponents."""
     w = _custom(T, d, E, k, I, Is, seed=m + T)
     L = gen.layer(w, 0)
     for f in (L["routed"], L["shared"]):
