@@ -93,7 +93,8 @@ def test_route_small_shapes(T, E, k, Is):
 # Calls of more than 32768 pairs take the sliced metadata (per-slice histograms, one scan block,
 # per-slice ranks); 32768 pairs and fewer take the single launch. Both sides of the switch, one
 # expert, a partial last slice and groups far longer than a slice.
-# (T, d, E, Zipf bias): 4, 8 and 16 tokens per block, one to eight staging passes, ragged expert blocks
+# (T, d, E, Zipf bias): every router block shape (16 tokens x 64 experts, 8 x 64, 8 x 32), one to eight
+# staging passes, ragged expert blocks
 LOGIT_CASES = [(1, 256, 16, False), (7, 512, 64, False), (64, 320, 300, False), (512, 2048, 256, False),
                (1024, 2048, 256, True), (33, 16384, 8, False), (512, 16384, 256, False), (300, 2048, 1024, True)]
 
